@@ -1,0 +1,250 @@
+/*
+ * tmoe.h - C ABI of the ternary Mixture-of-Experts expert layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the layer computes (the pages are the authority):
+ *  - Weights are ternary, {-1, 0, +1} times one fp32 scale per output row
+ *    (ai.thesatyajit.com, "Maple-Preview: a 20B reasoning model where 97% of
+ *    the weights are -1, 0, or +1", section "The claim, verified from the
+ *    bytes"); a ternary weight skips, adds or subtracts its activation
+ *    (codeinsider.com.br, section "Pesos ternarios").
+ *  - Five trits are packed into one byte, 3^5 = 243 <= 256 (ai.thesatyajit.com,
+ *    section "The 5.31 GB claim reconciles").
+ *  - The router stays full precision and picks 8 of 256 experts per token
+ *    (ai.thesatyajit.com, "The claim, verified from the bytes";
+ *    codeinsider.com.br, "256 experts, 8 ativos").
+ *  - One expert is linear(act(clamp(x Wg^T, max=7)) * clamp(x Wu^T, -7, 7), Wd)
+ *    (ai.thesatyajit.com, "The shipped code does no quantization"); act is SiLU.
+ *  - Shapes: hidden 2048, 256 experts, top 8, moe_intermediate_size 512
+ *    (jj-blog Maple-Preview news, architecture list).
+ *
+ * Conventions (all functions):
+ *  - Return an int status: TMOE_OK (0) or a negative TMOE_E_* code. The library
+ *    never aborts, prints or exits. tmoe_last_error() gives a thread-local
+ *    message for the last failure on the calling thread.
+ *  - The caller owns every buffer. Device functions never allocate; scratch
+ *    memory comes from a caller workspace of the size the matching
+ *    *_workspace_bytes query returns.
+ *  - Device functions are asynchronous on the caller's HIP stream, passed as
+ *    `void *stream` (a hipStream_t; NULL means the default stream).
+ *    Arguments are checked synchronously before anything is enqueued; a
+ *    failed check enqueues nothing. A HIP launch error returns TMOE_E_HIP.
+ *  - Sizes are int64_t. Device pointers must be 16-byte aligned unless stated
+ *    otherwise (TMOE_E_ALIGN).
+ *  - Matrices are row-major. A weight matrix is [rows = outputs][cols = inputs]
+ *    (the F.linear orientation of the printed forward).
+ *  - Packed bytes given to device kernels must be valid codes (<= 242); check
+ *    untrusted bytes with tmoe_validate_packed_host first.
+ *  - bf16 values are passed as uint16_t bit patterns.
+ */
+#ifndef TMOE_H
+#define TMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------------- status */
+enum {
+  TMOE_OK = 0,
+  TMOE_E_ARG = -1,         /* null pointer, negative size, bad enum value */
+  TMOE_E_SHAPE = -2,       /* inconsistent or unsupported dimensions */
+  TMOE_E_ALIGN = -3,       /* device pointer not 16-byte aligned */
+  TMOE_E_BADPACK = -4,     /* a packed byte > 242 (not a 5-trit code) */
+  TMOE_E_WORKSPACE = -5,   /* workspace null or smaller than required */
+  TMOE_E_UNSUPPORTED = -6, /* valid request this build does not implement */
+  TMOE_E_HIP = -7          /* the HIP runtime reported an error */
+};
+
+/* Static string naming a status code ("TMOE_OK", "TMOE_E_ARG", ...). */
+const char *tmoe_status_str(int status);
+/* Message describing the last failure on this thread ("" if none). */
+const char *tmoe_last_error(void);
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int tmoe_version(void);
+
+/* -------------------------------------------------- host weight preparation
+ * Offline steps (not on the timed path). Host pointers, synchronous.
+ */
+
+/* Absmean ternarization of fp32 W [R][K] (ai.thesatyajit.com, "The claim,
+ * verified from the bytes": {-s, 0, +s} per row, absmean, per-output-channel
+ * scale).
+ *   s[r] = fp32( (sum_i |W[r][i]|) / K ), the sum taken in fp64 in index order;
+ *   T[r][i] = sign(W[r][i]) if 2|W[r][i]| > s[r], else 0 (ties go to 0; an
+ *   all-zero row gives s = 0 and zero trits).
+ * W must be finite (TMOE_E_ARG otherwise, nothing written).
+ * Out: T int8 [R][K], s fp32 [R]. */
+int tmoe_ternarize_absmean_host(const float *W, int64_t R, int64_t K, int8_t *T, float *s);
+
+/* Canonical packing (ai.thesatyajit.com, "The 5.31 GB claim reconciles"):
+ * byte j of row r is sum_{q<5} (T[r][5j+q] + 1) * 3^q, trits past K count as
+ * 0. P is uint8 [R][ldp], ldp >= ceil(K/5); bytes [ceil(K/5), ldp) of each row
+ * are not written. T values outside {-1,0,1} give TMOE_E_ARG. */
+int tmoe_pack_host(const int8_t *T, int64_t R, int64_t K, uint8_t *P, int64_t ldp);
+
+/* Inverse of tmoe_pack_host: T[r][5j+q] = ((P[r][j] / 3^q) mod 3) - 1 for
+ * 5j+q < K. A byte > 242 gives TMOE_E_BADPACK (T then partly written). */
+int tmoe_unpack_host(const uint8_t *P, int64_t R, int64_t K, int64_t ldp, int8_t *T);
+
+/* Counts bytes > 242 among the ceil(K/5) data bytes of each row into *n_bad;
+ * returns TMOE_E_BADPACK if any, TMOE_OK otherwise. */
+int tmoe_validate_packed_host(const uint8_t *P, int64_t R, int64_t K, int64_t ldp, int64_t *n_bad);
+
+/* ----------------------------------------------------- device weight layout
+ * The GEMM kernels read weights in a "tiled" layout built from the canonical
+ * one: rows are grouped in tiles of 16 (the MFMA row block); within a tile the
+ * bytes are ordered so that each 64-lane wavefront load is one contiguous run.
+ * Row r's canonical bytes are split into four quarters of Q bytes
+ * (Q = ceil(ceil(K/5)/4) rounded up to even); quarter g of row i of a tile is
+ * read by lane i + 16g. Pad bytes (past ceil(K/5), and rows past R) hold 121,
+ * the code of five zero trits. The tiled form is lossless:
+ * tmoe_unpack_tiled returns the same trits as the canonical bytes.
+ * Size in bytes: tmoe_tiled_bytes(R, K) = ceil(R/16) * 16 * 4 * Q.
+ */
+int64_t tmoe_tiled_bytes(int64_t R, int64_t K);
+
+/* Device absmean ternarize + canonical pack of fp32 W [R][K] (row stride K):
+ * same definition as tmoe_ternarize_absmean_host (the fp64 sum is a fixed
+ * tree instead of index order; both are exact for the synthetic weights,
+ * whose values are multiples of 2^-16). Out: P [R][ldp] (bytes past ceil(K/5)
+ * untouched), s [R]. */
+int tmoe_ternarize_pack(void *stream, const float *W, int64_t R, int64_t K, uint8_t *P, int64_t ldp, float *s);
+
+/* Device unpack of canonical bytes (the bit-exact parity hook): T int8 [R][K]. */
+int tmoe_unpack(void *stream, const uint8_t *P, int64_t R, int64_t K, int64_t ldp, int8_t *T);
+
+/* Canonical P [R][ldp] -> tiled Pt [tmoe_tiled_bytes(R, K)]. */
+int tmoe_repack_tiled(void *stream, const uint8_t *P, int64_t R, int64_t K, int64_t ldp, uint8_t *Pt);
+
+/* Tiled Pt -> trits int8 [R][K] (parity hook for the tiled layout). */
+int tmoe_unpack_tiled(void *stream, const uint8_t *Pt, int64_t R, int64_t K, int8_t *T);
+
+/* ------------------------------------------------- synthetic weight source
+ * Counter-based generator (not part of the layer; it draws the synthetic
+ * weights in HBM). out[i] = IH12(Philox4x64-10(counter = (first + i, stream_id,
+ * 0, 0), key = (key0, key1))) where IH12 sums the twelve little-endian 16-bit
+ * halves of output words 0..2, subtracts 393210 and scales by 2^-16; then
+ * out[i] *= mult (one fp32 multiply; mult = 1 leaves it exact).
+ * Philox: Salmon et al., "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
+ */
+int tmoe_synth_ih12(void *stream, uint64_t key0, uint64_t key1, uint64_t stream_id, uint64_t first, int64_t n,
+                    float mult, float *out);
+
+/* ------------------------------------------------------------ ternary linear
+ * Y[n][o] = s[o] * sum_i T[o][i] * X[n][i] for n < T tokens, o < N outputs
+ * (codeinsider.com.br, "Pesos ternarios": add / subtract / skip; the dense
+ * definition with dequantized weights). fp32 accumulation.
+ *   Pt: tiled packed weights of an [N][K] matrix; s: fp32 [N];
+ *   X: bf16 [T][ldx] (ldx >= K, element stride; 2-byte alignment suffices);
+ *   Y: fp32 [T][ldy] (ldy >= N).
+ * ws: workspace of tmoe_linear_workspace_bytes(T, K) bytes. */
+size_t tmoe_linear_workspace_bytes(int64_t T, int64_t K);
+int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,
+                        int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------ router
+ * Full-precision router (ai.thesatyajit.com, "The claim, verified from the
+ * bytes": routers stay sharp; 8 of 256 chosen by logit margins).
+ *   logits[t][e] = sum_i X[t][i] * Wr[e][i] + bias[e]   (bias may be NULL)
+ *   idx[t][0..k)  = the k largest logits, descending, equal logits -> lower e
+ *   w[t][j]       = softmax over the k selected logits
+ * The top-k is certified: fp32 logits carry a rigorous error bound; a token
+ * whose top-(k+1) ranking is not separated by it is recomputed in fp64
+ * (exact products) on the device. Indices therefore equal those of the exact
+ * logits except for logits closer than ~1e-13 relative.
+ *   X bf16 [T][H]; Wr fp32 [E][H]; bias fp32 [E] or NULL;
+ *   idx int32 [T][k]; w fp32 [T][k]; logits fp32 [T][E] or NULL;
+ *   n_fixup: int32 device scalar or NULL, receives the number of tokens that
+ *   took the fp64 path.
+ * Limits: 1 <= k <= min(E, 16), E <= 1024, H % 8 == 0. */
+size_t tmoe_router_workspace_bytes(int64_t T, int64_t E);
+int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
+                     int64_t E, int k, int32_t *idx, float *w, float *logits, int32_t *n_fixup, void *ws,
+                     size_t ws_bytes);
+
+/* ---------------------------------------------------------------- grouping
+ * Stable token -> expert grouping of the T*k (token, slot) pairs: ordered by
+ * expert, then token. counts [E]; offsets [E+1] (exclusive prefix sum,
+ * offsets[E] = T*k); sorted_token, sorted_slot [T*k]; pos [T*k] with
+ * pos[t*k + j] = grouped position of pair (t, j). Deterministic (no atomics
+ * whose order matters). idx values must lie in [0, E) and a token must not
+ * repeat an expert (the router guarantees both). */
+size_t tmoe_group_workspace_bytes(int64_t T, int k, int64_t E);
+int tmoe_group_by_expert(void *stream, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts,
+                         int32_t *offsets, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, void *ws,
+                         size_t ws_bytes);
+
+/* ----------------------------------------------------------- layer weights */
+typedef struct tmoe_moe_weights {
+  int64_t hidden;    /* H, input/output width (2048) */
+  int64_t inter;     /* I, moe_intermediate_size (512) */
+  int64_t n_experts; /* E (256) */
+  int32_t top_k;     /* k (8) */
+  int32_t reserved;  /* must be 0 */
+  const float *router_w;    /* fp32 [E][H] */
+  const float *router_bias; /* fp32 [E] or NULL */
+  /* Tiled packed expert weights; expert e's matrix starts at base + e * stride.
+   * gate, up: [I][H] matrices; down: [H][I] matrices. */
+  const uint8_t *gate_p;
+  const uint8_t *up_p;
+  const uint8_t *down_p;
+  int64_t stride_gu; /* bytes between experts, >= tmoe_tiled_bytes(I, H) */
+  int64_t stride_d;  /* bytes between experts, >= tmoe_tiled_bytes(H, I) */
+  const float *gate_s; /* fp32 [E][I] */
+  const float *up_s;   /* fp32 [E][I] */
+  const float *down_s; /* fp32 [E][H] */
+} tmoe_moe_weights;
+
+/* ---------------------------------------------------------------- expert FFN
+ * For every grouped pair p (expert e, token t = sorted_token[p]):
+ *   g = gate_e x_t, u = up_e x_t            (ternary linear, fp32)
+ *   h = SiLU(min(g, c)) * clamp(u, -c, c)   (c = clamp; INFINITY disables)
+ *   O[p] = down_e h                          (h kept fp32: split in two fp16
+ *                                             parts, both multiplied exactly)
+ * (ai.thesatyajit.com, "The shipped code does no quantization").
+ *   X bf16 [T][H]; offsets [E+1], sorted_token [T*k] from the grouping;
+ *   O fp32 [T*k][H] in grouped order; Hout fp32 [T*k][I] or NULL (h, for
+ *   checking). ws: tmoe_ffn_workspace_bytes(T, W). */
+size_t tmoe_ffn_workspace_bytes(int64_t T, const tmoe_moe_weights *W);
+int tmoe_expert_ffn(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
+                    const int32_t *sorted_token, float clamp, float *O, float *Hout, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------ combine
+ * Y[t] = sum_{j<k} w[t][j] * O[pos[t*k + j]] (fixed slot order, fp32), the
+ * weighted sum of the k expert outputs (codeinsider.com.br, "256 experts, 8
+ * ativos": 8 experts serve each token). If resid_out is not NULL, also
+ * resid_out[t] = bf16_RNE(fp32(resid_in[t]) + Y[t]) (resid_in required then;
+ * resid_out may alias resid_in). Y may be NULL when resid_out is given.
+ *   O fp32 [T*k][H]; w fp32 [T][k]; pos int32 [T*k]; Y fp32 [T][H]. */
+int tmoe_combine(void *stream, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,
+                 float *Y, const uint16_t *resid_in, uint16_t *resid_out);
+
+/* ------------------------------------------------------------- whole layer */
+typedef struct tmoe_moe_options {
+  float clamp;        /* activation clamp c; 7.0 in the model, INFINITY disables */
+  int32_t reserved0;  /* must be 0 */
+  /* Optional outputs (device, may be NULL): router results and grouping. */
+  int32_t *idx;       /* [T][k] */
+  float *w;           /* [T][k] */
+  int32_t *pos;       /* [T*k]  */
+  int32_t *n_fixup;   /* scalar */
+  uint16_t *resid_out;/* [T][H] bf16: X + Y rounded to bf16 (the residual stream) */
+} tmoe_moe_options;
+
+/* Workspace bytes for tmoe_moe_forward with T tokens. */
+int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
+
+/* The layer: router -> top-k -> grouping -> expert FFN -> combine.
+ * X bf16 [T][H]; Y fp32 [T][H] (may be NULL if opt->resid_out is set).
+ * opt may be NULL (clamp 7, no optional outputs). */
+int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
+                     const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TMOE_H */

@@ -1,0 +1,249 @@
+"""Python binding of libtmoe, the ternary Mixture-of-Experts expert layer for
+MI355X (gfx950).
+
+Argument marshalling only: every function here forwards to the C ABI declared
+in ``include/tmoe.h`` (same names without the ``tmoe_`` prefix). Device
+buffers are PyTorch tensors on the GPU (``data_ptr()``), launched on
+``torch.cuda.current_stream()``; host buffers are NumPy arrays. There is no
+CPU fallback: importing this package fails if ``libtmoe.so`` is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import _abi
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtmoe.so")
+
+
+class TmoeError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {_abi.status_name(status)} ({status}): {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} not built; run `python -m ternary_weight_moe_base_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    _abi.declare(lib)
+    return lib
+
+
+lib = _load()
+_abi.bind_status(lib)
+
+LAYOUT_HIDDEN = 2048
+LAYOUT_INTER = 512
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise TmoeError(rc, where, lib.tmoe_last_error().decode())
+
+
+def status_str(code: int) -> str:
+    return lib.tmoe_status_str(code).decode()
+
+
+def version() -> int:
+    return lib.tmoe_version()
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t) -> int | None:
+    """Device pointer of a torch tensor (None for None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    return t.data_ptr()
+
+
+def _np(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream=None) -> int:
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# --------------------------------------------------------- host weight steps
+def ternarize_absmean_host(W: np.ndarray):
+    """fp32 [R][K] -> (int8 trits [R][K], fp32 scales [R])."""
+    W, pw = _np(W, np.float32)
+    R, K = W.shape
+    T = np.empty((R, K), np.int8)
+    s = np.empty(R, np.float32)
+    _check(lib.tmoe_ternarize_absmean_host(pw, R, K, T.ctypes.data_as(ctypes.c_void_p),
+                                           s.ctypes.data_as(ctypes.c_void_p)), "ternarize_absmean_host")
+    return T, s
+
+
+def pack_host(T: np.ndarray, ldp: int | None = None) -> np.ndarray:
+    T, pt = _np(T, np.int8)
+    R, K = T.shape
+    ldp = (K + 4) // 5 if ldp is None else ldp
+    P = np.zeros((R, ldp), np.uint8)
+    _check(lib.tmoe_pack_host(pt, R, K, P.ctypes.data_as(ctypes.c_void_p), ldp), "pack_host")
+    return P
+
+
+def unpack_host(P: np.ndarray, K: int) -> np.ndarray:
+    P, pp = _np(P, np.uint8)
+    R, ldp = P.shape
+    T = np.empty((R, K), np.int8)
+    _check(lib.tmoe_unpack_host(pp, R, K, ldp, T.ctypes.data_as(ctypes.c_void_p)), "unpack_host")
+    return T
+
+
+def validate_packed_host(P: np.ndarray, K: int) -> int:
+    """Number of invalid bytes (> 242); raises TmoeError(TMOE_E_BADPACK) if any."""
+    P, pp = _np(P, np.uint8)
+    R, ldp = P.shape
+    n = ctypes.c_int64(0)
+    rc = lib.tmoe_validate_packed_host(pp, R, K, ldp, ctypes.byref(n))
+    if rc not in (0, _abi.TMOE_E_BADPACK):
+        _check(rc, "validate_packed_host")
+    if rc:
+        raise TmoeError(rc, "validate_packed_host", f"{n.value} invalid bytes")
+    return n.value
+
+
+def tiled_bytes(R: int, K: int) -> int:
+    return lib.tmoe_tiled_bytes(R, K)
+
+
+# ------------------------------------------------------- device weight steps
+def synth_ih12(out, stream_id: int, first: int = 0, key0: int = 0x7E4A, key1: int = 0, mult: float = 1.0,
+               stream=None) -> None:
+    """Fills the fp32 tensor `out` with Irwin-Hall(12) draws of Philox4x64-10 stream `stream_id`."""
+    _check(lib.tmoe_synth_ih12(_stream(stream), key0, key1, stream_id, first, out.numel(), mult, _ptr(out)),
+           "synth_ih12")
+
+
+def ternarize_pack(W, P, s, stream=None) -> None:
+    """W fp32 [R][K] -> canonical P uint8 [R][ldp], scales s fp32 [R] (device)."""
+    R, K = W.shape
+    _check(lib.tmoe_ternarize_pack(_stream(stream), _ptr(W), R, K, _ptr(P), P.shape[1], _ptr(s)), "ternarize_pack")
+
+
+def unpack(P, K: int, T, stream=None) -> None:
+    R, ldp = P.shape
+    _check(lib.tmoe_unpack(_stream(stream), _ptr(P), R, K, ldp, _ptr(T)), "unpack")
+
+
+def repack_tiled(P, K: int, Pt, stream=None) -> None:
+    R, ldp = P.shape
+    _check(lib.tmoe_repack_tiled(_stream(stream), _ptr(P), R, K, ldp, _ptr(Pt)), "repack_tiled")
+
+
+def unpack_tiled(Pt, R: int, K: int, T, stream=None) -> None:
+    _check(lib.tmoe_unpack_tiled(_stream(stream), _ptr(Pt), R, K, _ptr(T)), "unpack_tiled")
+
+
+# ------------------------------------------------------------ ternary linear
+def linear_workspace_bytes(T: int, K: int) -> int:
+    return lib.tmoe_linear_workspace_bytes(T, K)
+
+
+def ternary_linear(Pt, s, N: int, K: int, X, Y, ws, stream=None) -> None:
+    """Y[T][N] fp32 = s * (trits @ X^T); X bf16 bits (int16/uint16 tensor) [T][ldx]."""
+    T, ldx = X.shape
+    _check(lib.tmoe_ternary_linear(_stream(stream), _ptr(Pt), _ptr(s), N, K, _ptr(X), ldx, T, _ptr(Y), Y.shape[1],
+                                   _ptr(ws), ws.numel() * ws.element_size()), "ternary_linear")
+
+
+# -------------------------------------------------------------------- router
+def router_workspace_bytes(T: int, E: int) -> int:
+    return lib.tmoe_router_workspace_bytes(T, E)
+
+
+def router_topk(X, Wr, bias, k: int, idx, w, ws, logits=None, n_fixup=None, stream=None) -> None:
+    T, H = X.shape
+    E = Wr.shape[0]
+    _check(lib.tmoe_router_topk(_stream(stream), _ptr(X), T, H, _ptr(Wr), _ptr(bias), E, k, _ptr(idx), _ptr(w),
+                                _ptr(logits), _ptr(n_fixup), _ptr(ws), ws.numel() * ws.element_size()),
+           "router_topk")
+
+
+# ------------------------------------------------------------------ grouping
+def group_workspace_bytes(T: int, k: int, E: int) -> int:
+    return lib.tmoe_group_workspace_bytes(T, k, E)
+
+
+def group_by_expert(idx, E: int, counts, offsets, sorted_token, sorted_slot, pos, ws=None, stream=None) -> None:
+    T, k = idx.shape
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.tmoe_group_by_expert(_stream(stream), _ptr(idx), T, k, E, _ptr(counts), _ptr(offsets),
+                                    _ptr(sorted_token), _ptr(sorted_slot), _ptr(pos), _ptr(ws), nb),
+           "group_by_expert")
+
+
+# ----------------------------------------------------------- layer weights
+class MoEWeights:
+    """Device weights of one layer plus the C struct that describes them.
+
+    gate_p / up_p: uint8 [E][stride_gu]; down_p: uint8 [E][stride_d] (tiled
+    layout); gate_s, up_s: fp32 [E][I]; down_s: fp32 [E][H]; router_w fp32
+    [E][H]; router_bias fp32 [E] or None. Keeps references to the tensors.
+    """
+
+    def __init__(self, router_w, router_bias, gate_p, up_p, down_p, gate_s, up_s, down_s, top_k: int = 8):
+        self.tensors = (router_w, router_bias, gate_p, up_p, down_p, gate_s, up_s, down_s)
+        E, H = router_w.shape
+        I = gate_s.shape[1]
+        self.hidden, self.inter, self.n_experts, self.top_k = H, I, E, top_k
+        s = _abi.MoEWeightsStruct()
+        s.hidden, s.inter, s.n_experts, s.top_k, s.reserved = H, I, E, top_k, 0
+        s.router_w, s.router_bias = _ptr(router_w), _ptr(router_bias)
+        s.gate_p, s.up_p, s.down_p = _ptr(gate_p), _ptr(up_p), _ptr(down_p)
+        s.stride_gu = gate_p.shape[1] if gate_p.dim() == 2 else tiled_bytes(I, H)
+        s.stride_d = down_p.shape[1] if down_p.dim() == 2 else tiled_bytes(H, I)
+        s.gate_s, s.up_s, s.down_s = _ptr(gate_s), _ptr(up_s), _ptr(down_s)
+        self.struct = s
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def ffn_workspace_bytes(T: int, W: MoEWeights) -> int:
+    return lib.tmoe_ffn_workspace_bytes(T, W.ref)
+
+
+def expert_ffn(W: MoEWeights, X, offsets, sorted_token, O, ws, clamp: float = 7.0, Hout=None, stream=None) -> None:
+    T = X.shape[0]
+    _check(lib.tmoe_expert_ffn(_stream(stream), W.ref, _ptr(X), T, _ptr(offsets), _ptr(sorted_token), clamp, _ptr(O),
+                               _ptr(Hout), _ptr(ws), ws.numel() * ws.element_size()), "expert_ffn")
+
+
+def combine(O, w, pos, Y=None, resid_in=None, resid_out=None, stream=None) -> None:
+    T, k = w.shape
+    H = O.shape[1]
+    _check(lib.tmoe_combine(_stream(stream), _ptr(O), _ptr(w), _ptr(pos), T, k, H, _ptr(Y), _ptr(resid_in),
+                            _ptr(resid_out)), "combine")
+
+
+def moe_workspace_bytes(T: int, W: MoEWeights) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.tmoe_moe_workspace_bytes(T, W.ref, ctypes.byref(out)), "moe_workspace_bytes")
+    return out.value
+
+
+def moe_forward(W: MoEWeights, X, Y, ws, clamp: float = 7.0, idx=None, w=None, pos=None, n_fixup=None,
+                resid_out=None, stream=None) -> None:
+    opt = _abi.MoEOptionsStruct()
+    opt.clamp = clamp
+    opt.reserved0 = 0
+    opt.idx, opt.w, opt.pos, opt.n_fixup, opt.resid_out = _ptr(idx), _ptr(w), _ptr(pos), _ptr(n_fixup), _ptr(resid_out)
+    T = X.shape[0]
+    _check(lib.tmoe_moe_forward(_stream(stream), W.ref, _ptr(X), T, _ptr(Y), ctypes.byref(opt), _ptr(ws),
+                                ws.numel() * ws.element_size()), "moe_forward")

@@ -1,0 +1,51 @@
+// Device helpers shared by the .hip sources of libtmoe.
+#pragma once
+
+#include "common.h"
+
+namespace tmoe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Exclusive prefix sum of cnt[0..n) in place by a workgroup of NT threads
+// (n <= 4 * NT); tmp holds NT ints. Returns the total to every thread.
+template <int NT>
+__device__ inline int block_exclusive_scan(int *cnt, int n, int *tmp) {
+  const int per = (n + NT - 1) / NT;
+  const int b0 = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < n) local += cnt[b0 + i];
+  tmp[threadIdx.x] = local;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    int v = (int)threadIdx.x >= off ? tmp[threadIdx.x - off] : 0;
+    __syncthreads();
+    tmp[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = tmp[threadIdx.x] - local;
+  const int total = tmp[NT - 1];
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < n) {
+      int c = cnt[b0 + i];
+      cnt[b0 + i] = run;
+      run += c;
+    }
+  __syncthreads();
+  return total;
+}
+
+// Round a finite fp32 value to bf16, nearest even; returns the bit pattern.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace tmoe

@@ -1,0 +1,157 @@
+// Deterministic token -> expert grouping.
+//
+// Each token is served by k of E experts (codeinsider.com.br, "256 experts, 8
+// ativos"); the expert kernels need the (token, slot) pairs grouped by expert.
+// Pairs are ordered by expert, then token. A pair's position is
+//   offsets[e] + (pairs of e in earlier token blocks) + (tokens before t in
+//   its block that chose e),
+// the last term read from a per-block bitmask of the tokens choosing each
+// expert (popcount of the bits below t). No atomics influence any output
+// value or order (the bitmask is built with atomicOr, which commutes).
+#include "device_util.h"
+
+namespace tmoe {
+
+static constexpr int kBlockTok = 256;  // tokens per grouping block = threads per workgroup
+
+size_t group_ws_bytes(int64_t T, int k, int64_t E) {
+  (void)k;
+  int64_t nb = cdiv(T, kBlockTok);
+  if (nb <= 1) return 0;
+  return 2 * align_up((size_t)nb * E * 4, 256);
+}
+
+GroupWs group_ws_carve(void *ws, int64_t T, int k, int64_t E) {
+  (void)k;
+  GroupWs g{nullptr, nullptr};
+  int64_t nb = cdiv(T, kBlockTok);
+  if (nb <= 1 || !ws) return g;
+  g.bcount = (int32_t *)ws;
+  g.bbase = (int32_t *)((char *)ws + align_up((size_t)nb * E * 4, 256));
+  return g;
+}
+
+// bits[e * 8 + w]: bit b set <=> token (block_start + 32 w + b) chose expert e.
+__device__ inline void build_bitmask(uint32_t *bits, const int32_t *idx, int64_t T, int k, int E, int64_t t0) {
+  for (int i = threadIdx.x; i < E * 8; i += kBlockTok) bits[i] = 0;
+  __syncthreads();
+  const int64_t t = t0 + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicOr(&bits[e * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+    }
+  }
+  __syncthreads();
+}
+
+__device__ inline int block_count(const uint32_t *bits, int e) {
+  int c = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) c += __popc(bits[e * 8 + w]);
+  return c;
+}
+
+// rank of token slot `tid` among the block's tokens that chose e
+__device__ inline int block_rank(const uint32_t *bits, int e, int tid) {
+  int w = tid >> 5, r = 0;
+  for (int i = 0; i < w; ++i) r += __popc(bits[e * 8 + i]);
+  return r + __popc(bits[e * 8 + w] & ((1u << (tid & 31)) - 1u));
+}
+
+__device__ inline void scatter_block(const uint32_t *bits, const int *base, const int32_t *idx, int64_t T, int k,
+                                     int E, int64_t t0, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos) {
+  const int64_t t = t0 + threadIdx.x;
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    int e = idx[t * k + j];
+    int p = -1;
+    if (e >= 0 && e < E) {
+      p = base[e] + block_rank(bits, e, threadIdx.x);
+      sorted_token[p] = (int32_t)t;
+      sorted_slot[p] = j;
+    }
+    pos[t * k + j] = p;
+  }
+}
+
+// Whole grouping in one workgroup (T <= 256).
+__global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *idx, int64_t T, int k, int E,
+                                                                int32_t *counts, int32_t *offsets,
+                                                                int32_t *sorted_token, int32_t *sorted_slot,
+                                                                int32_t *pos) {
+  __shared__ uint32_t bits[1024 * 8];
+  __shared__ int cnt[1024];
+  __shared__ int tmp[kBlockTok];
+  build_bitmask(bits, idx, T, k, E, 0);
+  for (int e = threadIdx.x; e < E; e += kBlockTok) {
+    int c = block_count(bits, e);
+    cnt[e] = c;
+    counts[e] = c;
+  }
+  __syncthreads();
+  int total = block_exclusive_scan<kBlockTok>(cnt, E, tmp);
+  for (int e = threadIdx.x; e < E; e += kBlockTok) offsets[e] = cnt[e];
+  if (threadIdx.x == 0) offsets[E] = total;
+  scatter_block(bits, cnt, idx, T, k, E, 0, sorted_token, sorted_slot, pos);
+}
+
+__global__ __launch_bounds__(kBlockTok) void group_count_kernel(const int32_t *idx, int64_t T, int k, int E,
+                                                                int32_t *bcount) {
+  __shared__ uint32_t bits[1024 * 8];
+  build_bitmask(bits, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok);
+  for (int e = threadIdx.x; e < E; e += kBlockTok) bcount[(int64_t)blockIdx.x * E + e] = block_count(bits, e);
+}
+
+__global__ __launch_bounds__(kBlockTok) void group_scan_kernel(const int32_t *bcount, int nb, int E, int32_t *bbase,
+                                                               int32_t *counts, int32_t *offsets) {
+  __shared__ int cnt[1024];
+  __shared__ int tmp[kBlockTok];
+  for (int e = threadIdx.x; e < E; e += kBlockTok) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      bbase[(int64_t)b * E + e] = run;
+      run += bcount[(int64_t)b * E + e];
+    }
+    cnt[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  int total = block_exclusive_scan<kBlockTok>(cnt, E, tmp);
+  for (int e = threadIdx.x; e < E; e += kBlockTok) offsets[e] = cnt[e];
+  if (threadIdx.x == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t *idx, int64_t T, int k, int E,
+                                                                  const int32_t *offsets, const int32_t *bbase,
+                                                                  int32_t *sorted_token, int32_t *sorted_slot,
+                                                                  int32_t *pos) {
+  __shared__ uint32_t bits[1024 * 8];
+  __shared__ int base[1024];
+  for (int e = threadIdx.x; e < E; e += kBlockTok) base[e] = offsets[e] + bbase[(int64_t)blockIdx.x * E + e];
+  build_bitmask(bits, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok);
+  scatter_block(bits, base, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok, sorted_token, sorted_slot, pos);
+}
+
+int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
+                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw) {
+  const int64_t nb = cdiv(T, kBlockTok);
+  if (nb <= 1) {
+    hipLaunchKernelGGL(group_fused_kernel, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts, offsets,
+                       sorted_token, sorted_slot, pos);
+    TMOE_LAUNCHED("group_fused");
+    return TMOE_OK;
+  }
+  if (nb > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
+  hipLaunchKernelGGL(group_count_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, gw.bcount);
+  TMOE_LAUNCHED("group_count");
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kBlockTok), 0, st, gw.bcount, (int)nb, (int)E, gw.bbase, counts,
+                     offsets);
+  TMOE_LAUNCHED("group_scan");
+  hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, offsets,
+                     gw.bbase, sorted_token, sorted_slot, pos);
+  TMOE_LAUNCHED("group_scatter");
+  return TMOE_OK;
+}
+
+}  // namespace tmoe

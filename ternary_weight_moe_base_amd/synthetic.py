@@ -1,0 +1,53 @@
+"""Synthetic layer weights built in HBM with the library's own device steps.
+
+Raw fp32 weights come from the counter-based generator (tmoe_synth_ih12,
+Philox4x64-10 + Irwin-Hall(12), the stream numbering of tmoe_inputs); each
+expert matrix is then ternarized and packed on the device (tmoe_ternarize_pack)
+and converted to the tiled layout (tmoe_repack_tiled). No host round trip.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import tmoe_inputs as ti
+
+from . import MoEWeights, repack_tiled, synth_ih12, ternarize_pack, tiled_bytes
+
+
+def _mat(cfg: int, layer: int, e: int, mat: int, rows: int, cols: int, wbuf, pbuf, out_tiled, out_s) -> None:
+    w = wbuf[: rows * cols]
+    synth_ih12(w, ti.stream_id(cfg, layer, e, mat))
+    p = pbuf[: rows * ((cols + 4) // 5)].view(rows, (cols + 4) // 5)
+    ternarize_pack(w.view(rows, cols), p, out_s)
+    repack_tiled(p, cols, out_tiled)
+
+
+def build_layer(cfg: int, layer: int, bias_kind: str | None = None, experts: int = ti.N_EXPERTS,
+                hidden: int = ti.HIDDEN, inter: int = ti.INTER, top_k: int = ti.TOP_K) -> MoEWeights:
+    dev = torch.device("cuda")
+    E, H, I = experts, hidden, inter
+    sgu, sd = tiled_bytes(I, H), tiled_bytes(H, I)
+    gate_p = torch.empty((E, sgu), dtype=torch.uint8, device=dev)
+    up_p = torch.empty((E, sgu), dtype=torch.uint8, device=dev)
+    down_p = torch.empty((E, sd), dtype=torch.uint8, device=dev)
+    gate_s = torch.empty((E, I), dtype=torch.float32, device=dev)
+    up_s = torch.empty((E, I), dtype=torch.float32, device=dev)
+    down_s = torch.empty((E, H), dtype=torch.float32, device=dev)
+    wbuf = torch.empty(H * I, dtype=torch.float32, device=dev)
+    pbuf = torch.empty(max(I * ((H + 4) // 5), H * ((I + 4) // 5)), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        _mat(cfg, layer, e, ti.MAT_GATE, I, H, wbuf, pbuf, gate_p[e], gate_s[e])
+        _mat(cfg, layer, e, ti.MAT_UP, I, H, wbuf, pbuf, up_p[e], up_s[e])
+        _mat(cfg, layer, e, ti.MAT_DOWN, H, I, wbuf, pbuf, down_p[e], down_s[e])
+    router_w = torch.empty((E, H), dtype=torch.float32, device=dev)
+    synth_ih12(router_w.view(-1), ti.stream_id(cfg, layer, 1023, ti.MAT_ROUTER), mult=float(ti.ROUTER_STD))
+    b = ti.router_bias(cfg, bias_kind, E)
+    router_bias = None if b is None else torch.from_numpy(b).to(dev)
+    return MoEWeights(router_w, router_bias, gate_p, up_p, down_p, gate_s, up_s, down_s, top_k=top_k)
+
+
+def activations(cfg: int, tokens: int, hidden: int = ti.HIDDEN, layer: int = 0) -> torch.Tensor:
+    """bf16 activations as an int16 device tensor of bit patterns [T][H]."""
+    x = ti.activations(cfg, tokens, hidden, layer)
+    return torch.from_numpy(x.view(np.int16)).to("cuda")

@@ -1,0 +1,382 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on seeded
+inputs. Integer and index results must match bit for bit; floating-point
+results within a max normalized error (per row) of 2e-5."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tmoe_inputs as ti
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+TOL = 2e-5
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def tm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ternary_weight_moe_base_amd as m
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_dev(bits):
+    return dev(np.ascontiguousarray(bits).view(np.int16))
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ws_bytes(n):
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device="cuda")
+
+
+# --------------------------------------------------------------------- inputs
+def test_synth_matches_host_generator(tm):
+    for stream, n, first in [(ti.stream_id(1, 0, 0, 0), 512 * 2048, 0), (77, 1001, 12345)]:
+        say(f"synth stream={stream} n={n}")
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+        tm.synth_ih12(out, stream, first=first)
+        assert np.array_equal(host(out), ti.ih12_normal(stream, n, first))
+    r = torch.empty(256 * 2048, dtype=torch.float32, device="cuda")
+    tm.synth_ih12(r, ti.stream_id(3, 0, 1023, ti.MAT_ROUTER), mult=float(ti.ROUTER_STD))
+    assert np.array_equal(host(r).reshape(256, 2048), ti.router_matrix(3, 0))
+
+
+# ------------------------------------------------------- ternarize / packing
+@pytest.mark.parametrize("R,K,kind", [(512, 2048, "ih"), (2048, 512, "ih"), (33, 517, "normal"), (9, 23, "normal"),
+                                      (5, 1, "normal")])
+def test_ternarize_pack_device(tm, R, K, kind):
+    say(f"ternarize_pack R={R} K={K} {kind}")
+    g = np.random.default_rng(R + K)
+    W = ti.ih12_normal(99, R * K).reshape(R, K) if kind == "ih" else g.standard_normal((R, K)).astype(np.float32)
+    W[0, :2 if K > 1 else 1] = 0.0
+    Kb = (K + 4) // 5
+    P = torch.full((R, Kb + 3), 7, dtype=torch.uint8, device="cuda")
+    s = torch.empty(R, dtype=torch.float32, device="cuda")
+    tm.ternarize_pack(dev(W), P, s)
+    t_ref, s_ref = O.ternarize_absmean(W)
+    Ph = host(P)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(Ph[:, :Kb], O.pack_trits(t_ref))
+    assert np.all(Ph[:, Kb:] == 7)  # bytes past ceil(K/5) untouched
+    T = torch.empty((R, K), dtype=torch.int8, device="cuda")
+    tm.unpack(P, K, T)
+    assert np.array_equal(host(T), t_ref)
+
+
+def test_unpack_all_codes(tm):
+    codes = np.tile(np.arange(243, dtype=np.uint8), (3, 1))
+    T = torch.empty((3, 243 * 5), dtype=torch.int8, device="cuda")
+    tm.unpack(dev(codes), 243 * 5, T)
+    assert np.array_equal(host(T), O.unpack_trits(codes, 243 * 5))
+
+
+@pytest.mark.parametrize("R,K", [(1, 1), (9, 23), (16, 7), (33, 517), (512, 2048), (2048, 512), (17, 60), (3, 41)])
+def test_tiled_layout_roundtrip(tm, R, K):
+    say(f"tiled R={R} K={K}")
+    g = np.random.default_rng(7 * R + K)
+    t = g.integers(-1, 2, size=(R, K)).astype(np.int8)
+    P = O.pack_trits(t)
+    Pt = torch.empty(tm.tiled_bytes(R, K), dtype=torch.uint8, device="cuda")
+    tm.repack_tiled(dev(P), K, Pt)
+    T = torch.zeros((R, K), dtype=torch.int8, device="cuda")
+    tm.unpack_tiled(Pt, R, K, T)
+    assert np.array_equal(host(T), t)
+    pt = host(Pt)
+    assert pt.max() <= 242
+    # the tiled image holds the canonical bytes once each plus pad codes (121)
+    assert np.bincount(pt, minlength=243)[:243].sum() == pt.size
+    extra = pt.size - P.size
+    assert extra >= 0 and np.sum(pt == 121) >= extra
+
+
+# ------------------------------------------------------------- ternary linear
+def _linear(tm, t, s, x_bits):
+    N, K = t.shape
+    T = x_bits.shape[0]
+    Pt = torch.empty(tm.tiled_bytes(N, K), dtype=torch.uint8, device="cuda")
+    tm.repack_tiled(dev(O.pack_trits(t)), K, Pt)
+    Y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = ws_bytes(tm.linear_workspace_bytes(T, K))
+    tm.ternary_linear(Pt, dev(s), N, K, bf16_dev(x_bits), Y, ws)
+    return host(Y)
+
+
+@pytest.mark.parametrize("N,K,T", [(512, 2048, 4), (512, 2048, 1), (512, 2048, 37), (2048, 512, 5), (9, 23, 3),
+                                   (33, 517, 17), (20, 60, 2), (1, 1, 1)])
+def test_ternary_linear_integer_inputs_exact(tm, N, K, T):
+    # integer activations and power-of-two scales make every partial sum exact
+    say(f"linear exact N={N} K={K} T={T}")
+    g = np.random.default_rng(N + K + T)
+    t = g.integers(-1, 2, size=(N, K)).astype(np.int8)
+    s = (2.0 ** g.integers(-4, 4, size=N)).astype(np.float32)
+    xb = ti.integer_activations(N + T, T, K)
+    Y = _linear(tm, t, s, xb)
+    ref = O.ternary_linear(t, s, O.bf16_to_f64(xb)).astype(np.float32)
+    assert np.array_equal(Y, ref)
+
+
+@pytest.mark.parametrize("T", [4, 1, 37, 256])
+def test_ternary_linear_config1(tm, T):
+    # 2048 -> 512, weights N(0,1) (Irwin-Hall) absmean-ternarized on the device, bf16 N(0,1) input
+    say(f"linear config1 T={T}")
+    N, K = 512, 2048
+    W = torch.empty(N * K, dtype=torch.float32, device="cuda")
+    tm.synth_ih12(W, ti.stream_id(1, 0, 0, ti.MAT_GATE))
+    P = torch.empty((N, 410), dtype=torch.uint8, device="cuda")
+    s = torch.empty(N, dtype=torch.float32, device="cuda")
+    tm.ternarize_pack(W.view(N, K), P, s)
+    Pt = torch.empty(tm.tiled_bytes(N, K), dtype=torch.uint8, device="cuda")
+    tm.repack_tiled(P, K, Pt)
+    xb = ti.activations(1, T)
+    Y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    tm.ternary_linear(Pt, s, N, K, bf16_dev(xb), Y, ws_bytes(tm.linear_workspace_bytes(T, K)))
+    t_ref, s_ref = O.ternarize_absmean(ti.linear_matrix(1))
+    Tt = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    tm.unpack_tiled(Pt, N, K, Tt)
+    assert np.array_equal(host(Tt), t_ref)
+    ref = O.ternary_linear(t_ref, s_ref, O.bf16_to_f64(xb))
+    err = O.max_normalized_error(host(Y), ref)
+    say(f"  max normalized error {err:.2e}")
+    assert err <= TOL
+
+
+# --------------------------------------------------------------------- router
+def _router(tm, xb, Wr, bias, k):
+    T, H = xb.shape
+    E = Wr.shape[0]
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    tm.router_topk(bf16_dev(xb), dev(Wr), None if bias is None else dev(bias), k, idx, w,
+                   ws_bytes(tm.router_workspace_bytes(T, E)), logits=lg, n_fixup=nf)
+    return host(idx), host(w), int(host(nf)[0]), host(lg)
+
+
+@pytest.mark.parametrize("cfg,T,bias_kind", [(2, 1, None), (3, 64, "zipf"), (4, 4096, "uniform"), (5, 256, None)])
+def test_router_parity(tm, cfg, T, bias_kind):
+    say(f"router cfg={cfg} T={T}")
+    xb = ti.activations(cfg, T)
+    Wr = ti.router_matrix(cfg, 0)
+    b = ti.router_bias(cfg, bias_kind)
+    idx, w, nfix, lg = _router(tm, xb, Wr, b, 8)
+    ridx, rw, rL, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
+    say(f"  fp64 fix-ups: {nfix} of {T}")
+    assert np.array_equal(idx, ridx)
+    assert O.max_normalized_error(w, rw) <= TOL
+    assert O.max_normalized_error(lg, rL) <= TOL
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_router_ties_take_fp64_path(tm):
+    T, H, E = 40, 2048, 256
+    xb = ti.activations(9, T)
+    Wr = ti.router_matrix(9, 0).copy()
+    Wr[200] = Wr[17]
+    Wr[201] = Wr[17]
+    b = np.zeros(E, np.float32)
+    b[[17, 200, 201]] = 5.0
+    idx, w, nfix, _ = _router(tm, xb, Wr, b, 8)
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
+    assert nfix == T
+    assert np.array_equal(idx, ridx)
+    assert np.all(idx[:, :3] == [17, 200, 201])
+    assert O.max_normalized_error(w, rw) <= TOL
+
+
+@pytest.mark.parametrize("k,E,H,T", [(1, 256, 2048, 33), (16, 256, 2048, 9), (8, 64, 256, 100), (4, 1000, 512, 7),
+                                     (64 // 8, 8, 256, 5)])
+def test_router_shapes(tm, k, E, H, T):
+    say(f"router k={k} E={E} H={H} T={T}")
+    g = np.random.default_rng(k + E + H + T)
+    xb = ti.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    Wr = (g.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b = g.uniform(-0.05, 0.05, E).astype(np.float32)
+    idx, w, _, _ = _router(tm, xb, Wr, b, k)
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, k)
+    assert np.array_equal(idx, ridx)
+    assert O.max_normalized_error(w, rw) <= TOL
+
+
+# ------------------------------------------------------------------- grouping
+def _group(tm, idx, E):
+    T, k = idx.shape
+    out = [torch.full((n,), -9, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k, T * k)]
+    ws = ws_bytes(tm.group_workspace_bytes(T, k, E))
+    tm.group_by_expert(dev(idx.astype(np.int32)), E, *out, ws=ws)
+    return [host(o) for o in out]
+
+
+@pytest.mark.parametrize("T,k,E,mode", [(1, 8, 256, "rand"), (7, 8, 256, "rand"), (64, 8, 256, "zipf"),
+                                        (256, 8, 256, "rand"), (257, 8, 256, "rand"), (1000, 1, 64, "rand"),
+                                        (4096, 8, 256, "rand"), (300, 16, 1000, "rand"), (600, 8, 256, "one")])
+def test_grouping_parity(tm, T, k, E, mode):
+    say(f"group T={T} k={k} E={E} {mode}")
+    g = np.random.default_rng(T * 31 + k + E)
+    if mode == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        idx = np.stack([g.choice(E, k, replace=False, p=p / p.sum()) for _ in range(T)])
+    else:
+        idx = np.stack([g.choice(E, k, replace=False) for _ in range(T)])
+    if mode == "one":
+        idx[:, 0] = 5  # one expert holds every token
+        for t in range(T):
+            while 5 in idx[t, 1:]:
+                idx[t, 1:][idx[t, 1:] == 5] = g.integers(6, E)
+    got = _group(tm, idx, E)
+    ref = O.group_by_expert(idx, E)
+    for a, b_ in zip(got, ref):
+        assert np.array_equal(a, b_)
+
+
+# ---------------------------------------------------------------- whole layer
+_EXPERT_CACHE = {}
+
+
+def _raw_expert(cfg, layer, e):
+    key = (cfg, layer, e)
+    if key not in _EXPERT_CACHE:
+        _EXPERT_CACHE[key] = tuple(ti.expert_matrix(cfg, layer, e, m) for m in (0, 1, 2))
+    return _EXPERT_CACHE[key]
+
+
+@pytest.fixture(scope="module")
+def layers():
+    from ternary_weight_moe_base_amd import synthetic
+    cache = {}
+
+    def get(cfg, layer, bias):
+        if (cfg, layer) not in cache:
+            say(f"building layer cfg={cfg} layer={layer} on the device")
+            cache[(cfg, layer)] = synthetic.build_layer(cfg, layer, bias)
+            torch.cuda.synchronize()
+        return cache[(cfg, layer)]
+    return get
+
+
+def _run_layer(tm, W, xb, clamp=7.0):
+    T = xb.shape[0]
+    k = W.top_k
+    Y = torch.empty((T, W.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    pos = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = ws_bytes(tm.moe_workspace_bytes(T, W))
+    tm.moe_forward(W, bf16_dev(xb), Y, ws, clamp=clamp, idx=idx, w=w, pos=pos, n_fixup=nf)
+    return dict(Y=host(Y), idx=host(idx), w=host(w), pos=host(pos), nfix=int(host(nf)[0]))
+
+
+@pytest.mark.parametrize("cfg,T,bias_kind,clamp", [(2, 1, None, 7.0), (2, 1, None, math.inf), (3, 64, "zipf", 7.0),
+                                                   (2, 5, None, 7.0)])
+def test_layer_parity(tm, layers, cfg, T, bias_kind, clamp):
+    say(f"layer cfg={cfg} T={T} clamp={clamp}")
+    W = layers(cfg, 0, bias_kind)
+    xb = ti.activations(cfg, T)
+    got = _run_layer(tm, W, xb, clamp)
+    ref = O.moe_layer(xb, ti.router_matrix(cfg, 0), ti.router_bias(cfg, bias_kind),
+                      lambda e: _raw_expert(cfg, 0, e), k=8, clamp=clamp)
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert np.array_equal(got["pos"], ref["pos"])
+    err = O.max_normalized_error(got["Y"], ref["Y"])
+    say(f"  Y max normalized error {err:.2e} (experts hit: {int((ref['counts'] > 0).sum())})")
+    assert err <= TOL
+    # the step-by-step ABI gives the same layer, and its intermediates match too
+    T_, k = xb.shape[0], 8
+    E = 256
+    idx = dev(got["idx"])
+    g = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T_ * k, T_ * k, T_ * k)]
+    tm.group_by_expert(idx, E, *g, ws=ws_bytes(tm.group_workspace_bytes(T_, k, E)))
+    O_ = torch.empty((T_ * k, 2048), dtype=torch.float32, device="cuda")
+    Hh = torch.empty((T_ * k, 512), dtype=torch.float32, device="cuda")
+    tm.expert_ffn(W, bf16_dev(xb), g[1], g[2], O_, ws_bytes(tm.ffn_workspace_bytes(T_, W)), clamp=clamp, Hout=Hh)
+    Y2 = torch.empty((T_, 2048), dtype=torch.float32, device="cuda")
+    tm.combine(O_, dev(got["w"]), g[4], Y=Y2)
+    assert O.max_normalized_error(host(Hh), ref["H"]) <= TOL
+    assert O.max_normalized_error(host(O_), ref["O"]) <= TOL
+    assert np.array_equal(host(Y2), got["Y"])
+
+
+def test_layer_prefill_sampled(tm, layers):
+    # prefill of 4096 tokens: router and grouping checked on every token, the
+    # expert outputs on a sample of tokens (their experts computed by the oracle)
+    cfg, T = 4, 4096
+    W = layers(cfg, 0, "uniform")
+    xb = ti.activations(cfg, T)
+    say("layer prefill T=4096")
+    got = _run_layer(tm, W, xb)
+    Wr, b = ti.router_matrix(cfg, 0), ti.router_bias(cfg, "uniform")
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
+    assert np.array_equal(got["idx"], ridx)
+    counts, offsets, st, ss, pos = O.group_by_expert(ridx, 256)
+    assert np.array_equal(got["pos"], pos)
+    say(f"  expert counts: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}")
+    x = O.bf16_to_f64(xb)
+    for t in (0, 1234, 4095):
+        y = np.zeros(2048)
+        for j in range(8):
+            Wg, Wu, Wd = _raw_expert(cfg, 0, int(ridx[t, j]))
+            deq = [O.dequantize(*O.ternarize_absmean(m)) for m in (Wg, Wu, Wd)]
+            y += rw[t, j] * O.expert_ffn(x[t:t + 1], *deq)[3][0]
+        err = O.max_normalized_error(got["Y"][t:t + 1], y[None])
+        say(f"  token {t}: max normalized error {err:.2e}")
+        assert err <= TOL
+
+
+def test_layer_is_deterministic(tm, layers):
+    W = layers(3, 0, "zipf")
+    xb = ti.activations(3, 64)
+    a = _run_layer(tm, W, xb)
+    b = _run_layer(tm, W, xb)
+    for key in ("Y", "idx", "w", "pos"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_layer_empty_batch(tm, layers):
+    W = layers(2, 0, None)
+    Y = torch.empty((0, 2048), dtype=torch.float32, device="cuda")
+    tm.moe_forward(W, torch.empty((0, 2048), dtype=torch.int16, device="cuda"), Y, ws_bytes(16))
+
+
+def test_stack_teacher_forced(tm, layers):
+    # 24-layer stack workload, first layers: the oracle's layer l consumes the
+    # GPU's residual stream X_l (teacher forcing) on sampled tokens
+    cfg, T = 5, 256
+    xb = ti.activations(cfg, T)
+    for layer in range(2):
+        W = layers(cfg, layer, None)
+        X = bf16_dev(xb)
+        Y = torch.empty((T, 2048), dtype=torch.float32, device="cuda")
+        Xn = torch.empty_like(X)
+        idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+        tm.moe_forward(W, X, Y, ws_bytes(tm.moe_workspace_bytes(T, W)), idx=idx, w=w, resid_out=Xn)
+        Yh, idxh, xn = host(Y), host(idx), host(Xn).view(np.uint16)
+        ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), ti.router_matrix(cfg, layer), None, 8)
+        assert np.array_equal(idxh, ridx)
+        # the residual stream is bf16(x + y) of the GPU's own y
+        assert np.array_equal(xn, O.residual_bf16(xb, Yh))
+        x = O.bf16_to_f64(xb)
+        for t in (3, 200):
+            y = np.zeros(2048)
+            for j in range(8):
+                deq = [O.dequantize(*O.ternarize_absmean(m)) for m in _raw_expert(cfg, layer, int(ridx[t, j]))]
+                y += rw[t, j] * O.expert_ffn(x[t:t + 1], *deq)[3][0]
+            err = O.max_normalized_error(Yh[t:t + 1], y[None])
+            say(f"  stack layer {layer} token {t}: max normalized error {err:.2e}")
+            assert err <= TOL
+        xb = xn
