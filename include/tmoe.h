@@ -95,14 +95,17 @@ int tmoe_unpack_host(const uint8_t *P, int64_t R, int64_t K, int64_t ldp, int8_t
 int tmoe_validate_packed_host(const uint8_t *P, int64_t R, int64_t K, int64_t ldp, int64_t *n_bad);
 
 /* ----------------------------------------------------- device weight layout
- * The GEMM kernels read weights in a "tiled" layout built from the canonical
- * one: rows are grouped in tiles of 16 (the MFMA row block); within a tile the
- * bytes are ordered so that each 64-lane wavefront load is one contiguous run.
- * Row r's canonical bytes are split into four quarters of Q bytes
- * (Q = ceil(ceil(K/5)/4) rounded up to even); quarter g of row i of a tile is
- * read by lane i + 16g. Pad bytes (past ceil(K/5), and rows past R) hold 121,
- * the code of five zero trits. The tiled form is lossless:
- * tmoe_unpack_tiled returns the same trits as the canonical bytes.
+ * The GEMM kernels read weights in a "tiled" layout holding the same trits,
+ * still 5 per byte in base 3 (digit = trit + 1), but re-ordered for the MFMA:
+ * rows are grouped in tiles of 16 (the MFMA row block); a row's input indices
+ * are split into four quarters of 5Q indices (Q = ceil(ceil(K/5)/4) rounded up
+ * to even), quarter g of row i being read by lane i + 16g, so that each 64-lane
+ * wavefront load is one contiguous run. Within a quarter, bytes come in steps
+ * of 8 (and a last, shorter step of Q mod 8 bytes): byte 2p + h of a step
+ * holds, as digit q, the trit of quarter input index 40*step + 10p + 2q + h,
+ * so the 8 trits one MFMA lane needs cover 8 consecutive input indices.
+ * Indices past K, and rows past R, hold zero trits. The tiled form is
+ * lossless: tmoe_unpack_tiled returns the same trits as the canonical bytes.
  * Size in bytes: tmoe_tiled_bytes(R, K) = ceil(R/16) * 16 * 4 * Q.
  */
 int64_t tmoe_tiled_bytes(int64_t R, int64_t K);
@@ -141,7 +144,8 @@ int tmoe_synth_ih12(void *stream, uint64_t key0, uint64_t key1, uint64_t stream_
  *   Pt: tiled packed weights of an [N][K] matrix; s: fp32 [N];
  *   X: bf16 [T][ldx] (ldx >= K, element stride; 2-byte alignment suffices);
  *   Y: fp32 [T][ldy] (ldy >= N).
- * ws: workspace of tmoe_linear_workspace_bytes(T, K) bytes. */
+ * ws: workspace of tmoe_linear_workspace_bytes(T, K) bytes; the current
+ *   kernels need none (0 bytes, ws may be NULL). */
 size_t tmoe_linear_workspace_bytes(int64_t T, int64_t K);
 int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,
                         int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws, size_t ws_bytes);
@@ -152,16 +156,17 @@ int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t
  *   logits[t][e] = sum_i X[t][i] * Wr[e][i] + bias[e]   (bias may be NULL)
  *   idx[t][0..k)  = the k largest logits, descending, equal logits -> lower e
  *   w[t][j]       = softmax over the k selected logits
- * The top-k is certified: fp32 logits carry a rigorous error bound; a token
- * whose top-(k+1) ranking is not separated by it is recomputed in fp64
- * (exact products) on the device. Indices therefore equal those of the exact
- * logits except for logits closer than ~1e-13 relative.
+ * The top-k is certified: logits are accumulated in fp64 from exact
+ * products and carry a rigorous rounding-error bound; a token whose
+ * top-(k+1) ranking is not separated by that bound is recomputed in
+ * double-double arithmetic on the device. Indices therefore equal those of
+ * the exact logits except for logits closer than ~1e-30 relative.
  *   X bf16 [T][H]; Wr fp32 [E][H]; bias fp32 [E] or NULL;
  *   idx int32 [T][k]; w fp32 [T][k]; logits fp32 [T][E] or NULL;
  *   n_fixup: int32 device scalar or NULL, receives the number of tokens that
- *   took the fp64 path.
- * Limits: 1 <= k <= min(E, 16), E <= 1024, H % 8 == 0. */
-size_t tmoe_router_workspace_bytes(int64_t T, int64_t E);
+ *   took the double-double path.
+ * Limits: 1 <= k <= min(E, 16), E <= 1024, H in {256, 512, 1024, 2048, 4096}. */
+size_t tmoe_router_workspace_bytes(int64_t T, int64_t E); /* zero-fill once (see tmoe_moe_workspace_bytes) */
 int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                      int64_t E, int k, int32_t *idx, float *w, float *logits, int32_t *n_fixup, void *ws,
                      size_t ws_bytes);
@@ -235,7 +240,10 @@ typedef struct tmoe_moe_options {
   uint16_t *resid_out;/* [T][H] bf16: X + Y rounded to bf16 (the residual stream) */
 } tmoe_moe_options;
 
-/* Workspace bytes for tmoe_moe_forward with T tokens. */
+/* Workspace bytes for tmoe_moe_forward with T tokens. The workspace must be
+ * zero-filled once after allocation: its first bytes hold a completion
+ * counter that every call leaves at zero again. Calls sharing one workspace
+ * must not run concurrently. */
 int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 
 /* The layer: router -> top-k -> grouping -> expert FFN -> combine.
@@ -243,6 +251,31 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
  * opt may be NULL (clamp 7, no optional outputs). */
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------ kernel timing
+ * Measurement hook. Between tmoe_profile_begin and tmoe_profile_end every
+ * launch of one kernel (TMOE_KERNEL_*) carries a HIP start/stop event pair
+ * that its own dispatch records on its stream (hipExtLaunchKernelGGL), for at
+ * most `capacity` launches (later launches are not recorded). Use it on eager
+ * launches, not inside HIP graph capture. The events
+ * are created by tmoe_profile_begin (not on the hot path) and destroyed by
+ * tmoe_profile_end, which waits for them and writes the per-launch durations
+ * in milliseconds to ms[0..*count). Global state: not thread-safe; one
+ * profiling window at a time (TMOE_E_ARG otherwise). */
+enum {
+  TMOE_KERNEL_ROUTER_LOGITS = 1,
+  TMOE_KERNEL_ROUTER_TOPK = 2,
+  TMOE_KERNEL_ROUTER_FIXUP = 3,
+  TMOE_KERNEL_GROUP = 4, /* the fused grouping kernel (first kernel when T > 256) */
+  TMOE_KERNEL_MAKE_TILES = 5,
+  TMOE_KERNEL_PERMUTE_X = 6,
+  TMOE_KERNEL_GATEUP = 7,
+  TMOE_KERNEL_DOWN = 9,
+  TMOE_KERNEL_COMBINE = 10,
+  TMOE_KERNEL_LINEAR = 11
+};
+int tmoe_profile_begin(int kernel, int capacity);
+int tmoe_profile_end(float *ms, int capacity, int *count);
 
 #ifdef __cplusplus
 }

@@ -25,16 +25,27 @@ class TmoeError(RuntimeError):
         self.status = status
 
 
+_lib = None
+
+
 def _load() -> ctypes.CDLL:
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} not built; run `python -m ternary_weight_moe_base_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
-    _abi.declare(lib)
-    return lib
+    """Loads libtmoe.so on first use; raises ImportError when it is not built
+    (there is no fallback implementation)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} not built; run `python -m ternary_weight_moe_base_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        _abi.declare(lib)
+        _abi.bind_status(lib)
+        _lib = lib
+    return _lib
 
 
-lib = _load()
-_abi.bind_status(lib)
+def __getattr__(name):
+    if name == "lib":
+        return _load()
+    raise AttributeError(name)
 
 LAYOUT_HIDDEN = 2048
 LAYOUT_INTER = 512
@@ -42,15 +53,15 @@ LAYOUT_INTER = 512
 
 def _check(rc: int, where: str) -> None:
     if rc != 0:
-        raise TmoeError(rc, where, lib.tmoe_last_error().decode())
+        raise TmoeError(rc, where, _load().tmoe_last_error().decode())
 
 
 def status_str(code: int) -> str:
-    return lib.tmoe_status_str(code).decode()
+    return _load().tmoe_status_str(code).decode()
 
 
 def version() -> int:
-    return lib.tmoe_version()
+    return _load().tmoe_version()
 
 
 # ------------------------------------------------------------------ helpers
@@ -82,7 +93,7 @@ def ternarize_absmean_host(W: np.ndarray):
     R, K = W.shape
     T = np.empty((R, K), np.int8)
     s = np.empty(R, np.float32)
-    _check(lib.tmoe_ternarize_absmean_host(pw, R, K, T.ctypes.data_as(ctypes.c_void_p),
+    _check(_load().tmoe_ternarize_absmean_host(pw, R, K, T.ctypes.data_as(ctypes.c_void_p),
                                            s.ctypes.data_as(ctypes.c_void_p)), "ternarize_absmean_host")
     return T, s
 
@@ -92,7 +103,7 @@ def pack_host(T: np.ndarray, ldp: int | None = None) -> np.ndarray:
     R, K = T.shape
     ldp = (K + 4) // 5 if ldp is None else ldp
     P = np.zeros((R, ldp), np.uint8)
-    _check(lib.tmoe_pack_host(pt, R, K, P.ctypes.data_as(ctypes.c_void_p), ldp), "pack_host")
+    _check(_load().tmoe_pack_host(pt, R, K, P.ctypes.data_as(ctypes.c_void_p), ldp), "pack_host")
     return P
 
 
@@ -100,7 +111,7 @@ def unpack_host(P: np.ndarray, K: int) -> np.ndarray:
     P, pp = _np(P, np.uint8)
     R, ldp = P.shape
     T = np.empty((R, K), np.int8)
-    _check(lib.tmoe_unpack_host(pp, R, K, ldp, T.ctypes.data_as(ctypes.c_void_p)), "unpack_host")
+    _check(_load().tmoe_unpack_host(pp, R, K, ldp, T.ctypes.data_as(ctypes.c_void_p)), "unpack_host")
     return T
 
 
@@ -109,7 +120,7 @@ def validate_packed_host(P: np.ndarray, K: int) -> int:
     P, pp = _np(P, np.uint8)
     R, ldp = P.shape
     n = ctypes.c_int64(0)
-    rc = lib.tmoe_validate_packed_host(pp, R, K, ldp, ctypes.byref(n))
+    rc = _load().tmoe_validate_packed_host(pp, R, K, ldp, ctypes.byref(n))
     if rc not in (0, _abi.TMOE_E_BADPACK):
         _check(rc, "validate_packed_host")
     if rc:
@@ -118,71 +129,71 @@ def validate_packed_host(P: np.ndarray, K: int) -> int:
 
 
 def tiled_bytes(R: int, K: int) -> int:
-    return lib.tmoe_tiled_bytes(R, K)
+    return _load().tmoe_tiled_bytes(R, K)
 
 
 # ------------------------------------------------------- device weight steps
 def synth_ih12(out, stream_id: int, first: int = 0, key0: int = 0x7E4A, key1: int = 0, mult: float = 1.0,
                stream=None) -> None:
     """Fills the fp32 tensor `out` with Irwin-Hall(12) draws of Philox4x64-10 stream `stream_id`."""
-    _check(lib.tmoe_synth_ih12(_stream(stream), key0, key1, stream_id, first, out.numel(), mult, _ptr(out)),
+    _check(_load().tmoe_synth_ih12(_stream(stream), key0, key1, stream_id, first, out.numel(), mult, _ptr(out)),
            "synth_ih12")
 
 
 def ternarize_pack(W, P, s, stream=None) -> None:
     """W fp32 [R][K] -> canonical P uint8 [R][ldp], scales s fp32 [R] (device)."""
     R, K = W.shape
-    _check(lib.tmoe_ternarize_pack(_stream(stream), _ptr(W), R, K, _ptr(P), P.shape[1], _ptr(s)), "ternarize_pack")
+    _check(_load().tmoe_ternarize_pack(_stream(stream), _ptr(W), R, K, _ptr(P), P.shape[1], _ptr(s)), "ternarize_pack")
 
 
 def unpack(P, K: int, T, stream=None) -> None:
     R, ldp = P.shape
-    _check(lib.tmoe_unpack(_stream(stream), _ptr(P), R, K, ldp, _ptr(T)), "unpack")
+    _check(_load().tmoe_unpack(_stream(stream), _ptr(P), R, K, ldp, _ptr(T)), "unpack")
 
 
 def repack_tiled(P, K: int, Pt, stream=None) -> None:
     R, ldp = P.shape
-    _check(lib.tmoe_repack_tiled(_stream(stream), _ptr(P), R, K, ldp, _ptr(Pt)), "repack_tiled")
+    _check(_load().tmoe_repack_tiled(_stream(stream), _ptr(P), R, K, ldp, _ptr(Pt)), "repack_tiled")
 
 
 def unpack_tiled(Pt, R: int, K: int, T, stream=None) -> None:
-    _check(lib.tmoe_unpack_tiled(_stream(stream), _ptr(Pt), R, K, _ptr(T)), "unpack_tiled")
+    _check(_load().tmoe_unpack_tiled(_stream(stream), _ptr(Pt), R, K, _ptr(T)), "unpack_tiled")
 
 
 # ------------------------------------------------------------ ternary linear
 def linear_workspace_bytes(T: int, K: int) -> int:
-    return lib.tmoe_linear_workspace_bytes(T, K)
+    return _load().tmoe_linear_workspace_bytes(T, K)
 
 
 def ternary_linear(Pt, s, N: int, K: int, X, Y, ws, stream=None) -> None:
     """Y[T][N] fp32 = s * (trits @ X^T); X bf16 bits (int16/uint16 tensor) [T][ldx]."""
     T, ldx = X.shape
-    _check(lib.tmoe_ternary_linear(_stream(stream), _ptr(Pt), _ptr(s), N, K, _ptr(X), ldx, T, _ptr(Y), Y.shape[1],
+    _check(_load().tmoe_ternary_linear(_stream(stream), _ptr(Pt), _ptr(s), N, K, _ptr(X), ldx, T, _ptr(Y), Y.shape[1],
                                    _ptr(ws), ws.numel() * ws.element_size()), "ternary_linear")
 
 
 # -------------------------------------------------------------------- router
 def router_workspace_bytes(T: int, E: int) -> int:
-    return lib.tmoe_router_workspace_bytes(T, E)
+    return _load().tmoe_router_workspace_bytes(T, E)
 
 
 def router_topk(X, Wr, bias, k: int, idx, w, ws, logits=None, n_fixup=None, stream=None) -> None:
     T, H = X.shape
     E = Wr.shape[0]
-    _check(lib.tmoe_router_topk(_stream(stream), _ptr(X), T, H, _ptr(Wr), _ptr(bias), E, k, _ptr(idx), _ptr(w),
+    _check(_load().tmoe_router_topk(_stream(stream), _ptr(X), T, H, _ptr(Wr), _ptr(bias), E, k, _ptr(idx), _ptr(w),
                                 _ptr(logits), _ptr(n_fixup), _ptr(ws), ws.numel() * ws.element_size()),
            "router_topk")
 
 
 # ------------------------------------------------------------------ grouping
 def group_workspace_bytes(T: int, k: int, E: int) -> int:
-    return lib.tmoe_group_workspace_bytes(T, k, E)
+    return _load().tmoe_group_workspace_bytes(T, k, E)
 
 
 def group_by_expert(idx, E: int, counts, offsets, sorted_token, sorted_slot, pos, ws=None, stream=None) -> None:
     T, k = idx.shape
     nb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.tmoe_group_by_expert(_stream(stream), _ptr(idx), T, k, E, _ptr(counts), _ptr(offsets),
+    _check(_load().tmoe_group_by_expert(_stream(stream), _ptr(idx), T, k, E, _ptr(counts), _ptr(offsets),
                                     _ptr(sorted_token), _ptr(sorted_slot), _ptr(pos), _ptr(ws), nb),
            "group_by_expert")
 
@@ -216,25 +227,25 @@ class MoEWeights:
 
 
 def ffn_workspace_bytes(T: int, W: MoEWeights) -> int:
-    return lib.tmoe_ffn_workspace_bytes(T, W.ref)
+    return _load().tmoe_ffn_workspace_bytes(T, W.ref)
 
 
 def expert_ffn(W: MoEWeights, X, offsets, sorted_token, O, ws, clamp: float = 7.0, Hout=None, stream=None) -> None:
     T = X.shape[0]
-    _check(lib.tmoe_expert_ffn(_stream(stream), W.ref, _ptr(X), T, _ptr(offsets), _ptr(sorted_token), clamp, _ptr(O),
+    _check(_load().tmoe_expert_ffn(_stream(stream), W.ref, _ptr(X), T, _ptr(offsets), _ptr(sorted_token), clamp, _ptr(O),
                                _ptr(Hout), _ptr(ws), ws.numel() * ws.element_size()), "expert_ffn")
 
 
 def combine(O, w, pos, Y=None, resid_in=None, resid_out=None, stream=None) -> None:
     T, k = w.shape
     H = O.shape[1]
-    _check(lib.tmoe_combine(_stream(stream), _ptr(O), _ptr(w), _ptr(pos), T, k, H, _ptr(Y), _ptr(resid_in),
+    _check(_load().tmoe_combine(_stream(stream), _ptr(O), _ptr(w), _ptr(pos), T, k, H, _ptr(Y), _ptr(resid_in),
                             _ptr(resid_out)), "combine")
 
 
 def moe_workspace_bytes(T: int, W: MoEWeights) -> int:
     out = ctypes.c_size_t(0)
-    _check(lib.tmoe_moe_workspace_bytes(T, W.ref, ctypes.byref(out)), "moe_workspace_bytes")
+    _check(_load().tmoe_moe_workspace_bytes(T, W.ref, ctypes.byref(out)), "moe_workspace_bytes")
     return out.value
 
 
@@ -245,5 +256,19 @@ def moe_forward(W: MoEWeights, X, Y, ws, clamp: float = 7.0, idx=None, w=None, p
     opt.reserved0 = 0
     opt.idx, opt.w, opt.pos, opt.n_fixup, opt.resid_out = _ptr(idx), _ptr(w), _ptr(pos), _ptr(n_fixup), _ptr(resid_out)
     T = X.shape[0]
-    _check(lib.tmoe_moe_forward(_stream(stream), W.ref, _ptr(X), T, _ptr(Y), ctypes.byref(opt), _ptr(ws),
+    _check(_load().tmoe_moe_forward(_stream(stream), W.ref, _ptr(X), T, _ptr(Y), ctypes.byref(opt), _ptr(ws),
                                 ws.numel() * ws.element_size()), "moe_forward")
+
+
+# ------------------------------------------------------------- kernel timing
+def profile_begin(kernel: str, capacity: int) -> None:
+    """Start recording HIP events around each launch of `kernel` (see _abi.KERNELS)."""
+    _check(_load().tmoe_profile_begin(_abi.KERNELS[kernel], capacity), "profile_begin")
+
+
+def profile_end(capacity: int) -> np.ndarray:
+    """Wait for the recorded launches and return their durations in milliseconds."""
+    ms = np.zeros(max(capacity, 1), np.float32)
+    n = ctypes.c_int(0)
+    _check(_load().tmoe_profile_end(ms.ctypes.data_as(ctypes.c_void_p), capacity, ctypes.byref(n)), "profile_end")
+    return ms[: n.value].copy()

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host and device sources of libtmoe.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -34,16 +35,25 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ------------------------------------------------------- tiled weight layout
-// A weight matrix [R][K] is stored as ceil(R/16) tiles of 16 rows. Each row's
-// ceil(K/5) canonical bytes are split in four quarters of Q bytes (Q even);
-// quarter g of tile row i belongs to lane i + 16g of the wavefront that
-// multiplies the tile. A lane's quarter is consumed in "steps" of 8 bytes
-// (4 byte pairs -> 20 bf16 pair-words -> 5 MFMA 16x16x32 operands) and a tail
-// of r = Q mod 8 bytes (0, 2, 4 or 6). Inside a tile:
+// A weight matrix [R][K] is stored as ceil(R/16) tiles of 16 rows. Each row is
+// split in four quarters; quarter g holds the 5Q input indices
+// [5Qg, 5Qg + 5Q) in Q bytes (Q even, 4Q >= ceil(K/5)); indices >= K are
+// zero trits. Quarter g of tile row i belongs to lane i + 16g of the
+// wavefront that multiplies the tile. A lane consumes its Q bytes in F "steps"
+// of 8 bytes and a tail of r = Q mod 8 bytes (0, 2, 4 or 6). Inside a step
+// (or the tail), byte 2p + h (pair p, half h) holds, as base-3 digit q (digit
+// = trit + 1, weight 3^q), the trit of input index
+//     5Qg + 40s + 10p + 2q + h        (s = step; the tail counts as step F).
+// The packed-fp16 decoder turns byte pair p into five "pair-words" u = 5p + q
+// holding the two trits of indices 40s + 2u + {0, 1}: MFMA m of the step takes
+// pair-words 4m..4m+3, i.e. the 8 consecutive input indices 5Qg + 8(5s+m) + e,
+// e = 0..7. The activation operand is therefore the input row itself, laid out
+// per quarter: operand position g*QS + j (QS = 8M, M = MFMAs per quarter) holds
+// input 5Qg + j for j < 5Q (zero beyond 5Q or K).
+// Tile byte order (each wavefront load is one contiguous run):
 //   full step s < F : offset s*512 + lane*8 + b      (b < 8)
 //   tail dword part : offset F*512 + lane*4 + b      (r >= 4, b < 4)
-//   tail short part : offset F*512 + (r>=4 ? 256 : 0) + lane*2 + b (r odd pair)
-// Every offset is a contiguous 512/256/128-byte run per wavefront load.
+//   tail short part : offset F*512 + (r>=4 ? 256 : 0) + lane*2 + b
 struct Geom {
   int64_t K;      // real input width
   int64_t Kb;     // canonical bytes per row = ceil(K/5)
@@ -51,8 +61,9 @@ struct Geom {
   int32_t F;      // full 8-byte steps per quarter
   int32_t r;      // tail bytes per quarter (0, 2, 4, 6)
   int32_t tailM;  // MFMAs for the tail (0, 2, 3, 4)
-  int32_t M;      // MFMAs per 16-row tile over the whole K = 5F + tailM
-  int32_t slots;  // operand slots per token = 4 quarters * M * 8
+  int32_t M;      // MFMAs per quarter = 5F + tailM
+  int32_t QS;     // operand positions per quarter = 8M (>= 5Q)
+  int32_t slots;  // operand positions per row = 4 QS
   int64_t tile_bytes;  // 64 * Q
 };
 
@@ -68,7 +79,8 @@ __host__ __device__ inline Geom make_geom(int64_t K) {
   g.r = g.Q % 8;
   g.tailM = g.r == 0 ? 0 : (5 * (g.r / 2) + 3) / 4;
   g.M = 5 * g.F + g.tailM;
-  g.slots = 32 * g.M;
+  g.QS = 8 * g.M;
+  g.slots = 4 * g.QS;
   g.tile_bytes = 64 * (int64_t)g.Q;
   return g;
 }
@@ -86,31 +98,47 @@ __host__ __device__ inline int64_t tile_offset(const Geom &g, int lane, int b) {
   return base + lane * 2 + tb;
 }
 
-// Input index K of operand slot `slot` (0 <= slot < g.slots), or -1 for a pad
-// slot. Slot = (quarter * M + mfma) * 8 + e: element e of the 8-wide operand
-// of MFMA `mfma` for the lanes of quarter `quarter`. Element e is half (e & 1)
-// of pair-word i = e >> 1; pair-word u = 4 * mfma' + i counts the 5 base-3
-// digits q of byte pairs p = u / 5 (q = u % 5) of the step; half 0 is the
-// pair's first byte.
-__host__ __device__ inline int64_t slot_to_k(const Geom &g, int slot) {
-  int e = slot & 7;
-  int mi = (slot >> 3) % g.M;
-  int quarter = (slot >> 3) / g.M;
-  int i = e >> 1, h = e & 1;
-  int b, q;
-  if (mi < 5 * g.F) {
-    int s = mi / 5, m = mi % 5;
-    int u = 4 * m + i;
-    b = 8 * s + 2 * (u / 5) + h;
-    q = u % 5;
-  } else {
-    int u = 4 * (mi - 5 * g.F) + i;
-    if (u >= 5 * (g.r / 2)) return -1;
-    b = 8 * g.F + 2 * (u / 5) + h;
-    q = u % 5;
-  }
-  int64_t k = 5 * ((int64_t)quarter * g.Q + b) + q;
+// Input index held by digit q of byte b of quarter `quarter` (>= K: a zero trit).
+__host__ __device__ inline int64_t tiled_k(const Geom &g, int quarter, int b, int q) {
+  const int full = 8 * g.F;
+  const int s = b < full ? b / 8 : g.F;
+  const int bb = b < full ? b % 8 : b - full;
+  return 5LL * g.Q * quarter + 40 * s + 10 * (bb >> 1) + 2 * q + (bb & 1);
+}
+
+// Input index of operand position j (0 <= j < QS) of quarter `quarter`, or -1.
+__host__ __device__ inline int64_t operand_k(const Geom &g, int quarter, int j) {
+  if (j >= 5 * g.Q) return -1;
+  const int64_t k = 5LL * g.Q * quarter + j;
   return k < g.K ? k : -1;
+}
+
+// ------------------------------------------------------------ kernel timing
+// When a tmoe_profile_begin window selects kernel `kid`, hands out the next
+// event pair (and returns true); the launch then records them itself.
+bool prof_events(int kid, hipEvent_t *start, hipEvent_t *stop);
+
+// Launch that, under a profiling window for `kid`, carries start/stop events
+// recorded by the dispatch itself (hipExtLaunchKernelGGL).
+#define TMOE_LAUNCH(kid, kernel, grid, block, lds, st, ...)                              \
+  do {                                                                                 \
+    hipEvent_t ev0_, ev1_;                                                             \
+    if (::tmoe::prof_events(kid, &ev0_, &ev1_))                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev0_, ev1_, 0, __VA_ARGS__); \
+    else                                                                               \
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);                   \
+  } while (0)
+
+// Kernels using more than 64 KiB of LDS opt in once per kernel (gfx950 has 160 KiB).
+template <auto Kern>
+inline int allow_lds(size_t bytes) {
+  static bool done = false;  // one flag per kernel instantiation
+  if (done || bytes <= 65536) return TMOE_OK;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)bytes);
+  if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
+  done = true;
+  return TMOE_OK;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -123,15 +151,24 @@ int launch_repack_tiled(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, 
 int launch_unpack_tiled(hipStream_t st, const uint8_t *Pt, int64_t R, int64_t K, int8_t *T);
 
 struct RouterWs {
-  float *wl1;         // [E]    L1 norms of router rows
-  float *logits;      // [T][E] fp32 logits
-  int32_t *fix_count; // [1]
-  int32_t *fix_list;  // [T]
+  uint32_t *ctr;       // completion counter of the fused decode kernel; zero between calls
+  uint64_t *bnd;       // [T] bits of max_e (sum_i |x_i w_ei| + |b_e|) (fp64, >= 0); zero between calls
+  double *lg;          // [T][E] fp64 logits
+  int32_t *fix_count;  // [1]
+  int32_t *fix_list;   // [T]
+  int32_t *scratch;    // grouping outputs of the router-only decode path
 };
 size_t router_ws_bytes(int64_t T, int64_t E);
 RouterWs router_ws_carve(void *ws, int64_t T, int64_t E);
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                   int64_t E, int k, int32_t *idx, float *w, float *logits_out, int32_t *n_fixup, const RouterWs &rw);
+// Fused decode front end (T <= kDecodeMaxT): router, top-k, grouping, work
+// tiles and permuted activations in one kernel.
+constexpr int kDecodeMaxT = 16;
+int launch_router_decode(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
+                         int64_t E, int k, const RouterWs &rw, int32_t *idx, float *w, int32_t *n_fixup,
+                         int32_t *counts, int32_t *offsets, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos,
+                         int32_t *tiles, int32_t *ntiles);
 
 struct GroupWs {
   int32_t *bcount;  // [nb][E]
@@ -145,16 +182,15 @@ int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E
 struct FfnWs {
   int32_t *tiles;    // [max_tiles][4]: expert, start, count, 0
   int32_t *ntiles;   // [1]
-  uint16_t *xp;      // [T][slots_H] bf16, permuted activations
-  float *h;          // [T*k][I] fp32 (natural order), when the caller gives none
-  uint16_t *hp;      // [2][T*k][slots_I] fp16 hi / lo parts, permuted
-  int32_t *hexp;     // [T*k] power-of-two scale of each h row before the fp16 split
+  uint16_t *hp;      // [3][T*k][slots_I] bf16 parts hi + mid + lo = h of each grouped pair,
+                     // in the down projection's operand layout
 };
 int64_t ffn_max_tiles(int64_t pairs, int64_t E);
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I);
 FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I);
+// prepared: tiles and ntiles were already written (fused decode front end)
 int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
-               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw);
+               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool prepared);
 
 size_t linear_ws_bytes(int64_t T, int64_t K);
 int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,

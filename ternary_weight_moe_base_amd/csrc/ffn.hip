@@ -8,14 +8,18 @@
 //    ((d - 1) mod 4) << 14 (d = t + 1 the base-3 digit) is the same in bf16
 //    and fp16: 0xC000 = -2, 0 = 0, 0x4000 = +2. Products with bf16 or fp16
 //    operands are exact; MFMA accumulates in fp32; the result is halved.
+//  - The tiled layout puts the 8 trits of each MFMA operand slice on 8
+//    consecutive input indices, so activations enter the MFMA in their natural
+//    order (per row quarter, see Geom).
 //  - Digits are decoded two bytes at a time in packed fp16: a byte pair b0, b1
 //    becomes the fp16 pair (1024 + b0, 1024 + b1); one packed FMA computes
 //    1024 + floor(R / 3) (rounding to the integer grid of [1024, 2048) is the
 //    floor), another 1027 + R + floor(R / 3), whose two low bits are
 //    (d - 1) mod 4 because d = R - 3 floor(R / 3) == R + floor(R / 3) (mod 4).
 //  - gate/up take the bf16 activations directly. The down projection's input h
-//    is fp32: it is scaled by a power of two and split into two fp16 parts
-//    hi + lo (22 significant bits), each multiplied exactly.
+//    is fp32: it is split exactly into three bf16 parts h = hi + mid + lo (each
+//    rounding keeps the next 8 of the 24 significant bits), each multiplied
+//    exactly.
 #include "device_util.h"
 
 namespace tmoe {
@@ -104,49 +108,32 @@ __device__ __forceinline__ f32x4 mfma_f16(const uint32_t *a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ u32x4 lds16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // LDS row stride (bytes) of a staged operand row with `slots` 16-bit values:
-// slots/2 dwords is a multiple of 16; +4 dwords makes the 16 token rows start
-// in 16 different 4-bank groups of the 64 LDS banks.
+// slots/2 = 16M dwords; +4 dwords makes the 16 token rows start in 16
+// different 4-bank groups of the 64 LDS banks.
 __host__ __device__ inline int lds_row_bytes(int slots) { return slots * 2 + 16; }
 
-// ----------------------------------------------------- operand permutation
-// xp[t][slot] = X[t][slot_to_k(slot)] (0 for pad slots): the activations in
-// the order the MFMA B operand reads them.
-__global__ void permute_x_kernel(const uint16_t *X, int64_t ldx, int64_t T, Geom g, uint16_t *xp) {
-  const int64_t t = blockIdx.x;
-  const int slot = blockIdx.y * 256 + threadIdx.x;
-  if (t >= T || slot >= g.slots) return;
-  int64_t k = slot_to_k(g, slot);
-  xp[t * g.slots + slot] = k >= 0 ? X[t * ldx + k] : (uint16_t)0;
+// ------------------------------------------------------------- staging
+// Operand row n of LDS <- input row `src` (16-bit values): position g*QS + j
+// holds src[5Qg + j] for j < 5Q and 5Qg + j < K, zero otherwise. `contig`:
+// QS == 5Q and K % 8 == 0 (then positions are the input indices and 16-byte
+// copies suffice).
+__device__ inline void stage_row(char *dst, const uint16_t *src, const Geom &g, bool contig, int tid, int nthreads) {
+  if (contig) {
+    const int vec = g.slots / 8, kv = (int)(g.K / 8);
+    for (int c = tid; c < vec; c += nthreads)
+      *reinterpret_cast<uint4 *>(dst + c * 16) =
+          c < kv ? reinterpret_cast<const uint4 *>(src)[c] : make_uint4(0, 0, 0, 0);
+    return;
+  }
+  for (int i = tid; i < g.slots; i += nthreads) {
+    const int quarter = i / g.QS, j = i - quarter * g.QS;
+    const int64_t k = operand_k(g, quarter, j);
+    reinterpret_cast<uint16_t *>(dst)[i] = k >= 0 ? src[k] : (uint16_t)0;
+  }
 }
 
-// One workgroup per grouped pair p: h row -> power-of-two scale 2^e with
-// max|h| 2^-e in [2^14, 2^15), then fp16 hi = rn(h'), lo = rn(h' - hi) in
-// down-operand order.
-__global__ __launch_bounds__(256) void permute_h_kernel(const float *Hn, int I, const int32_t *offsets, int E,
-                                                         Geom g, uint16_t *hp_hi, uint16_t *hp_lo, int32_t *hexp,
-                                                         int64_t pairs) {
-  __shared__ float red[4];
-  const int64_t p = blockIdx.x;
-  if (p >= pairs || p >= offsets[E]) return;
-  const float *h = Hn + p * I;
-  float m = 0.f;
-  for (int i = threadIdx.x; i < I; i += 256) m = fmaxf(m, fabsf(h[i]));
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int e = 0;
-  if (m > 0.f && m < INFINITY) e = ilogbf(m) - 14;
-  if (threadIdx.x == 0) hexp[p] = e;
-  for (int slot = threadIdx.x; slot < g.slots; slot += 256) {
-    int64_t k = slot_to_k(g, slot);
-    float v = k >= 0 ? ldexpf(h[k], -e) : 0.f;
-    _Float16 hi = (_Float16)v;
-    _Float16 lo = (_Float16)(v - (float)hi);
-    hp_hi[p * g.slots + slot] = __builtin_bit_cast(uint16_t, hi);
-    hp_lo[p * g.slots + slot] = __builtin_bit_cast(uint16_t, lo);
-  }
+__device__ inline void zero_row(char *dst, int slots, int tid, int nthreads) {
+  for (int c = tid; c < slots / 8; c += nthreads) *reinterpret_cast<uint4 *>(dst + c * 16) = make_uint4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- tiles
@@ -173,10 +160,13 @@ struct GateUpArgs {
   const uint8_t *gate_p, *up_p;
   int64_t stride_gu;
   const float *gate_s, *up_s;
-  const uint16_t *xp;  // [T][slots]
+  const uint16_t *X;  // [T][H] bf16, natural order
   const int32_t *tiles, *ntiles, *sorted_token;
-  float *h;  // [pairs][I]
-  int I, slots;
+  float *h;            // [pairs][I] fp32 (grouped order) or null
+  uint16_t *hp;        // [3][pairs][gd.slots] bf16 parts of h in the down operand layout
+  int64_t hp_plane;    // pairs * gd.slots
+  Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
+  int I;
   float clamp;
 };
 
@@ -198,7 +188,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
   constexpr int SMAX = (F + KS - 1) / KS;
   const int rt = blockIdx.y * RTB + wave / KS;
   const int kp = wave % KS;
-  const int rs = lds_row_bytes(a.slots);
+  const int rs = lds_row_bytes(a.gx.slots);
   char *xs = smem;  // [17][rs]; row 16 = zeros
 
   // weights first: all loads of this wavefront are in flight while x is staged
@@ -221,13 +211,28 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     load_tail<RT>(ut, F, lane, udw, ush);
   }
 
-  const int vpr = a.slots / 8;
-  for (int i = threadIdx.x; i < cnt * vpr; i += 256) {
-    int n = i / vpr, c = i - n * vpr;
-    int64_t tok = a.sorted_token[start + n];
-    *reinterpret_cast<uint4 *>(xs + n * rs + c * 16) = reinterpret_cast<const uint4 *>(a.xp + tok * a.slots)[c];
+  // activations of the tile's pairs (natural order = operand order for H = 2048)
+  const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
+  for (int i = threadIdx.x; i < cnt * vec; i += 256) {
+    const int n = i / vec, c = i - n * vec;
+    const int64_t tok = a.sorted_token[start + n];
+    *reinterpret_cast<uint4 *>(xs + n * rs + c * 16) =
+        c < kv ? reinterpret_cast<const uint4 *>(a.X + tok * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
   }
-  for (int c = threadIdx.x; c < vpr; c += 256) *reinterpret_cast<uint4 *>(xs + 16 * rs + c * 16) = make_uint4(0, 0, 0, 0);
+  zero_row(xs + 16 * rs, a.gx.slots, threadIdx.x, 256);
+  // zero pad positions of this tile's rows of the down operand (written once per pair)
+  if (blockIdx.y == 0 && wave == 0) {
+    for (int n = 0; n < cnt; ++n)
+      for (int i = lane; i < a.gd.slots; i += 64) {
+        const int quarter = i / a.gd.QS, j = i - quarter * a.gd.QS;
+        if (operand_k(a.gd, quarter, j) < 0) {
+          const int64_t o = (int64_t)(start + n) * a.gd.slots + i;
+          a.hp[o] = 0;
+          a.hp[a.hp_plane + o] = 0;
+          a.hp[2 * a.hp_plane + o] = 0;
+        }
+      }
+  }
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
@@ -292,13 +297,26 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
   const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
   float hv[4];
   const float c = a.clamp;
+  const int64_t p = start + n;
+  const int q5 = 5 * a.gd.Q;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    float gg = (accg[v] * 0.5f) * sgv[v];
-    float uu = (accu[v] * 0.5f) * suv[v];
+    const float gg = (accg[v] * 0.5f) * sgv[v];
+    const float uu = (accu[v] * 0.5f) * suv[v];
     hv[v] = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
+    // h = hi + mid + lo exactly (each bf16 rounding keeps the next 8 bits)
+    const uint16_t b0 = f32_to_bf16_rne(hv[v]);
+    const float r1 = hv[v] - __uint_as_float((uint32_t)b0 << 16);
+    const uint16_t b1 = f32_to_bf16_rne(r1);
+    const float r2 = r1 - __uint_as_float((uint32_t)b1 << 16);
+    const uint16_t b2 = f32_to_bf16_rne(r2);
+    const int nn = row0 + v;  // intermediate index = down input index
+    const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
+    a.hp[o] = b0;
+    a.hp[a.hp_plane + o] = b1;
+    a.hp[2 * a.hp_plane + o] = b2;
   }
-  *reinterpret_cast<float4 *>(a.h + (int64_t)(start + n) * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+  if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
 }
 
 // ----------------------------------------------------------------- down
@@ -306,14 +324,15 @@ struct DownArgs {
   const uint8_t *down_p;
   int64_t stride_d;
   const float *down_s;
-  const uint16_t *hp_hi, *hp_lo;  // [pairs][slots]
-  const int32_t *hexp;
+  const uint16_t *hp;  // [3][pairs][slots] bf16 parts of h (operand layout)
+  int64_t hp_plane;
   const int32_t *tiles, *ntiles;
   float *O;  // [pairs][H]
   int H, slots;
 };
 
-// Workgroup = 4 wavefronts x one 16-row tile each (64 output rows).
+// Workgroup = 4 wavefronts x one 16-row tile each (64 output rows); three
+// bf16 passes (hi, mid, lo parts of h) per operand slice.
 template <int F, int RT>
 __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -325,8 +344,7 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   constexpr int M = 5 * F + tail_mfmas(RT);
   const int rt = blockIdx.y * 4 + wave;
   const int rs = lds_row_bytes(a.slots);
-  char *xh = smem;            // [17][rs]
-  char *xl = smem + 17 * rs;  // [17][rs]
+  char *xb[3] = {smem, smem + 17 * rs, smem + 34 * rs};  // [3][17][rs]
 
   const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
   const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)rt * tbytes;
@@ -338,15 +356,15 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
 
   const int vpr = a.slots / 8;
   for (int i = threadIdx.x; i < cnt * vpr; i += 256) {
-    int n = i / vpr, c = i - n * vpr;
-    int64_t p = start + n;
-    *reinterpret_cast<uint4 *>(xh + n * rs + c * 16) = reinterpret_cast<const uint4 *>(a.hp_hi + p * a.slots)[c];
-    *reinterpret_cast<uint4 *>(xl + n * rs + c * 16) = reinterpret_cast<const uint4 *>(a.hp_lo + p * a.slots)[c];
+    const int n = i / vpr, c = i - n * vpr;
+    const int64_t p = start + n;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      *reinterpret_cast<uint4 *>(xb[q] + n * rs + c * 16) =
+          reinterpret_cast<const uint4 *>(a.hp + q * a.hp_plane + p * a.slots)[c];
   }
-  for (int c = threadIdx.x; c < vpr; c += 256) {
-    *reinterpret_cast<uint4 *>(xh + 16 * rs + c * 16) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4 *>(xl + 16 * rs + c * 16) = make_uint4(0, 0, 0, 0);
-  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) zero_row(xb[q] + 16 * rs, a.slots, threadIdx.x, 256);
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
@@ -357,30 +375,27 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
     uint32_t pw[20];
     unpack8(dd[s], pw);
 #pragma unroll
-    for (int m = 0; m < 5; ++m) {
-      acc = mfma_f16(pw + 4 * m, lds16(xh + boff + (5 * s + m) * 16), acc);
-      acc = mfma_f16(pw + 4 * m, lds16(xl + boff + (5 * s + m) * 16), acc);
-    }
+    for (int m = 0; m < 5; ++m)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(xb[q] + boff + (5 * s + m) * 16), acc);
   }
   if constexpr (RT > 0) {
     uint32_t pw[16];
     unpack_tail<RT>(ddw, dsh, pw);
 #pragma unroll
-    for (int m = 0; m < tail_mfmas(RT); ++m) {
-      acc = mfma_f16(pw + 4 * m, lds16(xh + boff + (5 * F + m) * 16), acc);
-      acc = mfma_f16(pw + 4 * m, lds16(xl + boff + (5 * F + m) * 16), acc);
-    }
+    for (int m = 0; m < tail_mfmas(RT); ++m)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(xb[q] + boff + (5 * F + m) * 16), acc);
   }
   if (n >= cnt) return;
   const int64_t p = start + n;
-  const int ex = a.hexp[p] - 1;  // the trits entered as 2t
   const int row0 = rt * 16 + 4 * g;
   const float4 sd = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + row0);
-  float4 o;
-  o.x = ldexpf(acc[0], ex) * sd.x;
-  o.y = ldexpf(acc[1], ex) * sd.y;
-  o.z = ldexpf(acc[2], ex) * sd.z;
-  o.w = ldexpf(acc[3], ex) * sd.w;
+  float4 o;  // the trits entered as 2t
+  o.x = (acc[0] * 0.5f) * sd.x;
+  o.y = (acc[1] * 0.5f) * sd.y;
+  o.z = (acc[2] * 0.5f) * sd.z;
+  o.w = (acc[3] * 0.5f) * sd.w;
   *reinterpret_cast<float4 *>(a.O + p * a.H + row0) = o;
 }
 
@@ -388,11 +403,11 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
 struct LinearArgs {
   const uint8_t *pt;
   const float *s;
-  const uint16_t *xp;  // [T][slots]
+  const uint16_t *X;  // [T][ldx] bf16, natural order
   float *Y;
-  int64_t T, N, ldy;
-  int slots;
-  Geom g;  // used by the generic (F < 0) instance
+  int64_t T, N, ldx, ldy;
+  Geom g;
+  bool contig;
 };
 
 // blockIdx.x = 16-token tile, blockIdx.y = group of 4/KS row tiles. F < 0:
@@ -408,7 +423,7 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   const int rt = blockIdx.y * RTB + wave / KS;
   const int kp = wave % KS;
   const bool active = rt < nrt;
-  const int rs = lds_row_bytes(a.slots);
+  const int rs = lds_row_bytes(a.g.slots);
   const int Fr = F >= 0 ? F : a.g.F;
   const int Rr = F >= 0 ? RT : a.g.r;
   const int M = 5 * Fr + (Rr == 0 ? 0 : (5 * (Rr / 2) + 3) / 4);
@@ -416,12 +431,8 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   const uint8_t *wt = a.pt + (int64_t)(active ? rt : 0) * tbytes;
   char *xs = smem;
 
-  const int vpr = a.slots / 8;
-  for (int i = threadIdx.x; i < cnt * vpr; i += 256) {
-    int n = i / vpr, c = i - n * vpr;
-    *reinterpret_cast<uint4 *>(xs + n * rs + c * 16) = reinterpret_cast<const uint4 *>(a.xp + (t0 + n) * a.slots)[c];
-  }
-  for (int c = threadIdx.x; c < vpr; c += 256) *reinterpret_cast<uint4 *>(xs + 16 * rs + c * 16) = make_uint4(0, 0, 0, 0);
+  for (int n = 0; n < cnt; ++n) stage_row(xs + n * rs, a.X + (t0 + n) * a.ldx, a.g, a.contig, threadIdx.x, 256);
+  zero_row(xs + 16 * rs, a.g.slots, threadIdx.x, 256);
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
@@ -506,67 +517,55 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
-// One workgroup per token; fixed slot order j = 0..k-1.
-__global__ __launch_bounds__(256) void combine_kernel(const float *O, const float *w, const int32_t *pos, int k,
+// grid (T, H / 512), 128 threads x one float4 each; fixed slot order j = 0..k-1.
+__global__ __launch_bounds__(128) void combine_kernel(const float *O, const float *w, const int32_t *pos, int k,
                                                        int H, float *Y, const uint16_t *resid_in,
                                                        uint16_t *resid_out) {
   const int64_t t = blockIdx.x;
-  for (int c = threadIdx.x; c < H / 4; c += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[t * k + j];
-      if (p < 0) continue;
-      const float wj = w[t * k + j];
-      const float4 o = reinterpret_cast<const float4 *>(O + (int64_t)p * H)[c];
-      acc.x = fmaf(wj, o.x, acc.x);
-      acc.y = fmaf(wj, o.y, acc.y);
-      acc.z = fmaf(wj, o.z, acc.z);
-      acc.w = fmaf(wj, o.w, acc.w);
-    }
-    if (Y) reinterpret_cast<float4 *>(Y + t * H)[c] = acc;
-    if (resid_out) {
-      const uint2 xi = reinterpret_cast<const uint2 *>(resid_in + t * H)[c];
-      const float x0 = __uint_as_float(xi.x << 16), x1 = __uint_as_float(xi.x & 0xFFFF0000u);
-      const float x2 = __uint_as_float(xi.y << 16), x3 = __uint_as_float(xi.y & 0xFFFF0000u);
-      uint2 r;
-      r.x = (uint32_t)f32_to_bf16_rne(x0 + acc.x) | ((uint32_t)f32_to_bf16_rne(x1 + acc.y) << 16);
-      r.y = (uint32_t)f32_to_bf16_rne(x2 + acc.z) | ((uint32_t)f32_to_bf16_rne(x3 + acc.w) << 16);
-      reinterpret_cast<uint2 *>(resid_out + t * H)[c] = r;
-    }
+  const int c = blockIdx.y * 128 + threadIdx.x;  // float4 column
+  if (c * 4 >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int j = 0; j < k; ++j) {
+    const int p = pos[t * k + j];
+    if (p < 0) continue;
+    const float wj = w[t * k + j];
+    const float4 o = reinterpret_cast<const float4 *>(O + (int64_t)p * H)[c];
+    acc.x = fmaf(wj, o.x, acc.x);
+    acc.y = fmaf(wj, o.y, acc.y);
+    acc.z = fmaf(wj, o.z, acc.z);
+    acc.w = fmaf(wj, o.w, acc.w);
+  }
+  if (Y) reinterpret_cast<float4 *>(Y + t * H)[c] = acc;
+  if (resid_out) {
+    const uint2 xi = reinterpret_cast<const uint2 *>(resid_in + t * H)[c];
+    const float x0 = __uint_as_float(xi.x << 16), x1 = __uint_as_float(xi.x & 0xFFFF0000u);
+    const float x2 = __uint_as_float(xi.y << 16), x3 = __uint_as_float(xi.y & 0xFFFF0000u);
+    uint2 r;
+    r.x = (uint32_t)f32_to_bf16_rne(x0 + acc.x) | ((uint32_t)f32_to_bf16_rne(x1 + acc.y) << 16);
+    r.y = (uint32_t)f32_to_bf16_rne(x2 + acc.z) | ((uint32_t)f32_to_bf16_rne(x3 + acc.w) << 16);
+    reinterpret_cast<uint2 *>(resid_out + t * H)[c] = r;
   }
 }
 
 // ----------------------------------------------------------------- host side
-// Kernels staging more than 64 KiB of LDS must opt in once (gfx950 has 160 KiB).
-template <auto Kern>
-static int allow_lds(size_t bytes) {
-  static bool done = false;  // one flag per kernel instantiation
-  if (done || bytes <= 65536) return TMOE_OK;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)bytes);
-  if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
-  done = true;
-  return TMOE_OK;
-}
-
 int64_t ffn_max_tiles(int64_t pairs, int64_t E) { return cdiv(pairs, 16) + (pairs < E ? pairs : E); }
 
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
+  (void)H;
   const int64_t P = T * k;
-  const Geom gh = make_geom(H), gi = make_geom(I);
+  const Geom gi = make_geom(I);
   size_t o = 0;
   o = align_up(o + ffn_max_tiles(P, E) * 16, 256);
   o = align_up(o + 16, 256);
-  o = align_up(o + (size_t)T * gh.slots * 2, 256);
-  o = align_up(o + (size_t)P * I * 4, 256);
-  o = align_up(o + (size_t)2 * P * gi.slots * 2, 256);
-  o = align_up(o + (size_t)P * 4, 256);
+  o = align_up(o + (size_t)3 * P * gi.slots * 2, 256);
   return o;
 }
 
 FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) {
+  (void)H;
+  (void)I;
   const int64_t P = T * k;
-  const Geom gh = make_geom(H), gi = make_geom(I);
   char *b = (char *)ws;
   FfnWs f;
   size_t o = 0;
@@ -574,43 +573,36 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   o = align_up(o + ffn_max_tiles(P, E) * 16, 256);
   f.ntiles = (int32_t *)(b + o);
   o = align_up(o + 16, 256);
-  f.xp = (uint16_t *)(b + o);
-  o = align_up(o + (size_t)T * gh.slots * 2, 256);
-  f.h = (float *)(b + o);
-  o = align_up(o + (size_t)P * I * 4, 256);
   f.hp = (uint16_t *)(b + o);
-  o = align_up(o + (size_t)2 * P * gi.slots * 2, 256);
-  f.hexp = (int32_t *)(b + o);
   return f;
 }
 
 template <int F, int RT, int KS>
 static int run_gateup(hipStream_t st, const GateUpArgs &a, int64_t max_tiles, int I) {
-  const int rs = lds_row_bytes(a.slots);
+  const int rs = lds_row_bytes(a.gx.slots);
   size_t lds = (size_t)17 * rs + (KS > 1 ? 4 * 64 * 8 * 4 : 0);
   dim3 grid((unsigned)max_tiles, (unsigned)(I / 16 / (4 / KS)));
   int rc = allow_lds<gateup_kernel<F, RT, KS>>(lds);
   if (rc) return rc;
-  hipLaunchKernelGGL((gateup_kernel<F, RT, KS>), grid, dim3(256), lds, st, a);
+  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS>), grid, dim3(256), lds, st, a);
   TMOE_LAUNCHED("gateup");
   return TMOE_OK;
 }
 
 int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
-               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw) {
+               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool prepared) {
   const int64_t E = W->n_experts, H = W->hidden, I = W->inter, P = T * W->top_k;
   const Geom gh = make_geom(H), gi = make_geom(I);
-  if (!(gh.F == 13 && gh.r == 0 && gi.F == 3 && gi.r == 2))
+  if (!(gh.F == 13 && gh.r == 0 && gi.F == 3 && gi.r == 2 && H % 64 == 0 && I % 64 == 0))
     return fail(TMOE_E_UNSUPPORTED, "expert kernels are built for hidden 2048 and moe_intermediate 512");
   const int64_t max_tiles = ffn_max_tiles(P, E);
   if (max_tiles > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too many tokens");
-  float *Hn = Hout ? Hout : fw.h;
 
-  hipLaunchKernelGGL(make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles, fw.ntiles);
-  TMOE_LAUNCHED("make_tiles");
-  hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)T, (unsigned)cdiv(gh.slots, 256)), dim3(256), 0, st, X, H, T,
-                     gh, fw.xp);
-  TMOE_LAUNCHED("permute_x");
+  if (!prepared) {
+    TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
+                fw.ntiles);
+    TMOE_LAUNCHED("make_tiles");
+  }
 
   GateUpArgs ga;
   ga.gate_p = W->gate_p;
@@ -618,74 +610,76 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   ga.stride_gu = W->stride_gu;
   ga.gate_s = W->gate_s;
   ga.up_s = W->up_s;
-  ga.xp = fw.xp;
+  ga.X = X;
   ga.tiles = fw.tiles;
   ga.ntiles = fw.ntiles;
   ga.sorted_token = sorted_token;
-  ga.h = Hn;
+  ga.h = Hout;
+  ga.hp = fw.hp;
+  ga.hp_plane = P * gi.slots;
+  ga.gx = gh;
+  ga.gd = gi;
   ga.I = (int)I;
-  ga.slots = gh.slots;
   ga.clamp = clamp;
   int rc = P <= 64 ? run_gateup<13, 0, 4>(st, ga, max_tiles, (int)I) : run_gateup<13, 0, 1>(st, ga, max_tiles, (int)I);
   if (rc) return rc;
-
-  uint16_t *hp_hi = fw.hp, *hp_lo = fw.hp + (size_t)P * gi.slots;
-  hipLaunchKernelGGL(permute_h_kernel, dim3((unsigned)P), dim3(256), 0, st, Hn, (int)I, offsets, (int)E, gi, hp_hi,
-                     hp_lo, fw.hexp, P);
-  TMOE_LAUNCHED("permute_h");
 
   DownArgs da;
   da.down_p = W->down_p;
   da.stride_d = W->stride_d;
   da.down_s = W->down_s;
-  da.hp_hi = hp_hi;
-  da.hp_lo = hp_lo;
-  da.hexp = fw.hexp;
+  da.hp = fw.hp;
+  da.hp_plane = P * gi.slots;
   da.tiles = fw.tiles;
   da.ntiles = fw.ntiles;
   da.O = O;
   da.H = (int)H;
   da.slots = gi.slots;
-  const size_t lds = (size_t)2 * 17 * lds_row_bytes(gi.slots);
-  hipLaunchKernelGGL((down_kernel<3, 2>), dim3((unsigned)max_tiles, (unsigned)(H / 64)), dim3(256), lds, st, da);
+  const size_t lds = (size_t)3 * 17 * lds_row_bytes(gi.slots);
+  rc = allow_lds<down_kernel<3, 2>>(lds);
+  if (rc) return rc;
+  TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_kernel<3, 2>), dim3((unsigned)max_tiles, (unsigned)(H / 64)), dim3(256), lds, st,
+              da);
   TMOE_LAUNCHED("down");
   return TMOE_OK;
 }
 
-size_t linear_ws_bytes(int64_t T, int64_t K) { return align_up((size_t)T * make_geom(K).slots * 2, 256); }
+size_t linear_ws_bytes(int64_t T, int64_t K) {
+  (void)T;
+  (void)K;
+  return 0;
+}
 
 template <int F, int RT, int KS>
 static int run_linear(hipStream_t st, const LinearArgs &a, int64_t ntok_tiles, int64_t nrt) {
-  const int rs = lds_row_bytes(a.slots);
+  const int rs = lds_row_bytes(a.g.slots);
   size_t lds = (size_t)17 * rs + (KS > 1 ? 4 * 64 * 4 * 4 : 0);
   dim3 grid((unsigned)ntok_tiles, (unsigned)cdiv(nrt, 4 / KS));
   int rc = allow_lds<linear_kernel<F, RT, KS>>(lds);
   if (rc) return rc;
-  hipLaunchKernelGGL((linear_kernel<F, RT, KS>), grid, dim3(256), lds, st, a);
+  TMOE_LAUNCH(TMOE_KERNEL_LINEAR, (linear_kernel<F, RT, KS>), grid, dim3(256), lds, st, a);
   TMOE_LAUNCHED("ternary_linear");
   return TMOE_OK;
 }
 
 int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,
                   int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws) {
+  (void)ws;
   const Geom g = make_geom(K);
   if ((size_t)17 * lds_row_bytes(g.slots) + 4096 > 160 * 1024) return fail(TMOE_E_UNSUPPORTED, "K too large");
   const int64_t nrt = cdiv(N, 16), ntt = cdiv(T, 16);
   if (ntt > 0x7FFFFFFF || nrt > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too large");
-  uint16_t *xp = (uint16_t *)ws;
-  hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)T, (unsigned)cdiv(g.slots, 256)), dim3(256), 0, st, X, ldx, T, g,
-                     xp);
-  TMOE_LAUNCHED("permute_x");
   LinearArgs a;
   a.pt = Pt;
   a.s = s;
-  a.xp = xp;
+  a.X = X;
   a.Y = Y;
   a.T = T;
   a.N = N;
+  a.ldx = ldx;
   a.ldy = ldy;
-  a.slots = g.slots;
   a.g = g;
+  a.contig = g.QS == 5 * g.Q && K % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X & 15) == 0;
   const bool small = T <= 16;
   if (g.F == 13 && g.r == 0) return small ? run_linear<13, 0, 4>(st, a, ntt, nrt) : run_linear<13, 0, 1>(st, a, ntt, nrt);
   if (g.F == 3 && g.r == 2) return run_linear<3, 2, 1>(st, a, ntt, nrt);
@@ -695,7 +689,8 @@ int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, 
 int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,
                    float *Y, const uint16_t *resid_in, uint16_t *resid_out) {
   if (T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, st, O, w, pos, k, (int)H, Y, resid_in, resid_out);
+  TMOE_LAUNCH(TMOE_KERNEL_COMBINE, combine_kernel, dim3((unsigned)T, (unsigned)cdiv(H, 512)), dim3(128), 0, st, O, w,
+              pos, k, (int)H, Y, resid_in, resid_out);
   TMOE_LAUNCHED("combine");
   return TMOE_OK;
 }

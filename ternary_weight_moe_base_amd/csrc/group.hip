@@ -137,13 +137,13 @@ int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E
                  int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw) {
   const int64_t nb = cdiv(T, kBlockTok);
   if (nb <= 1) {
-    hipLaunchKernelGGL(group_fused_kernel, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts, offsets,
+    TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_fused_kernel, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts, offsets,
                        sorted_token, sorted_slot, pos);
     TMOE_LAUNCHED("group_fused");
     return TMOE_OK;
   }
   if (nb > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
-  hipLaunchKernelGGL(group_count_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, gw.bcount);
+  TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_count_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, gw.bcount);
   TMOE_LAUNCHED("group_count");
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kBlockTok), 0, st, gw.bcount, (int)nb, (int)E, gw.bbase, counts,
                      offsets);

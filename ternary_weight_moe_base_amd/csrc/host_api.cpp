@@ -26,6 +26,30 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(TMOE_E_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
 
+// ------------------------------------------------------------ kernel timing
+static struct {
+  int kernel = 0, cap = 0, n = 0;
+  hipEvent_t *start = nullptr, *stop = nullptr;
+} g_prof;
+
+bool prof_events(int kid, hipEvent_t *start, hipEvent_t *stop) {
+  if (g_prof.kernel != kid || g_prof.n >= g_prof.cap) return false;
+  *start = g_prof.start[g_prof.n];
+  *stop = g_prof.stop[g_prof.n];
+  ++g_prof.n;
+  return true;
+}
+
+static void prof_free() {
+  for (int i = 0; i < g_prof.cap; ++i) {
+    if (g_prof.start && g_prof.start[i]) hipEventDestroy(g_prof.start[i]);
+    if (g_prof.stop && g_prof.stop[i]) hipEventDestroy(g_prof.stop[i]);
+  }
+  delete[] g_prof.start;
+  delete[] g_prof.stop;
+  g_prof = {};
+}
+
 }  // namespace tmoe
 
 using namespace tmoe;
@@ -206,7 +230,8 @@ int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t
   REQUIRE(aligned16(Pt), TMOE_E_ALIGN, "Pt not 16-byte aligned");
   REQUIRE(aligned4(s) && aligned4(Y) && ((uintptr_t)X & 1) == 0, TMOE_E_ALIGN, "misaligned s, X or Y");
   size_t need = linear_ws_bytes(T, K);
-  REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes (16-aligned)", need);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), TMOE_E_WORKSPACE,
+          "workspace needs %zu bytes (16-aligned)", need);
   return launch_linear((hipStream_t)stream, Pt, s, N, K, X, ldx, T, Y, ldy, ws);
 }
 
@@ -302,7 +327,7 @@ int tmoe_expert_ffn(void *stream, const tmoe_moe_weights *W, const uint16_t *X, 
   size_t need = ffn_ws_bytes(T, W->top_k, W->n_experts, W->hidden, W->inter);
   REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes", need);
   return launch_ffn((hipStream_t)stream, W, X, T, offsets, sorted_token, clamp, O, Hout,
-                    ffn_ws_carve(ws, T, W->top_k, W->n_experts, W->hidden, W->inter));
+                    ffn_ws_carve(ws, T, W->top_k, W->n_experts, W->hidden, W->inter), false);
 }
 
 // ------------------------------------------------------------------ combine
@@ -394,16 +419,62 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   int32_t *st_tok = (int32_t *)(base + L.off_st);
   int32_t *st_slot = (int32_t *)(base + L.off_ss);
   float *O = (float *)(base + L.off_O);
-  rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup,
-                     router_ws_carve(base + L.off_router, T, E));
-  if (rc) return rc;
-  rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos,
-                    group_ws_carve(base + L.off_group, T, k, E));
-  if (rc) return rc;
-  rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr,
-                  ffn_ws_carve(base + L.off_ffn, T, k, E, H, W->inter));
+  const RouterWs rw = router_ws_carve(base + L.off_router, T, E);
+  const FfnWs fw = ffn_ws_carve(base + L.off_ffn, T, k, E, H, W->inter);
+  if (T <= kDecodeMaxT) {
+    // one kernel: logits, certified top-k, grouping, work tiles, permuted activations
+    rc = launch_router_decode(st, X, T, H, W->router_w, W->router_bias, E, k, rw, idx, wt, o.n_fixup, counts,
+                              offsets, st_tok, st_slot, pos, fw.tiles, fw.ntiles);
+    if (rc) return rc;
+    rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw, true);
+  } else {
+    rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup, rw);
+    if (rc) return rc;
+    rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos,
+                      group_ws_carve(base + L.off_group, T, k, E));
+    if (rc) return rc;
+    rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw, false);
+  }
   if (rc) return rc;
   return launch_combine(st, O, wt, pos, T, k, H, Y, o.resid_out ? X : nullptr, o.resid_out);
+}
+
+int tmoe_profile_begin(int kernel, int capacity) {
+  clear_error();
+  REQUIRE(kernel >= TMOE_KERNEL_ROUTER_LOGITS && kernel <= TMOE_KERNEL_LINEAR, TMOE_E_ARG, "unknown kernel id %d",
+          kernel);
+  REQUIRE(capacity > 0 && capacity <= (1 << 20), TMOE_E_ARG, "capacity out of range");
+  REQUIRE(g_prof.kernel == 0, TMOE_E_ARG, "a profiling window is already open");
+  g_prof.start = new hipEvent_t[capacity]();
+  g_prof.stop = new hipEvent_t[capacity]();
+  g_prof.cap = capacity;
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&g_prof.start[i]);
+    if (e == hipSuccess) e = hipEventCreate(&g_prof.stop[i]);
+    if (e != hipSuccess) {
+      prof_free();
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  g_prof.kernel = kernel;
+  g_prof.n = 0;
+  return TMOE_OK;
+}
+
+int tmoe_profile_end(float *ms, int capacity, int *count) {
+  clear_error();
+  REQUIRE(count && (ms || capacity == 0), TMOE_E_ARG, "null output");
+  REQUIRE(g_prof.kernel != 0, TMOE_E_ARG, "no profiling window open");
+  int n = g_prof.n < capacity ? g_prof.n : capacity;
+  int rc = TMOE_OK;
+  for (int i = 0; i < n && rc == TMOE_OK; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.stop[i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_prof.start[i], g_prof.stop[i]);
+    if (e != hipSuccess) rc = hip_fail(e, "profile events");
+  }
+  *count = n;
+  prof_free();
+  return rc;
 }
 
 }  // extern "C"

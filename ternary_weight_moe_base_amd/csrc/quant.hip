@@ -128,7 +128,8 @@ int launch_unpack(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, int64_
 
 // ------------------------------------------------------- tiled conversions
 // One thread per byte of the tiled image: tile, lane (row i = lane & 15,
-// quarter g = lane >> 4) and quarter byte b are recovered from the offset.
+// quarter g = lane >> 4) and quarter byte b are recovered from the offset; the
+// byte's five trits are the input indices tiled_k(g, quarter, b, 0..4).
 __device__ inline void tiled_coords(const Geom &g, int64_t off, int64_t &tile, int &lane, int &b) {
   tile = off / g.tile_bytes;
   int64_t o = off % g.tile_bytes;
@@ -156,17 +157,35 @@ __device__ inline void tiled_coords(const Geom &g, int64_t off, int64_t &tile, i
   b = 8 * g.F + (w % 2);
 }
 
+// canonical trit of input index k of a row (0 past K)
+__device__ inline int canon_trit(const uint8_t *row, int64_t K, int64_t k) {
+  if (k >= K) return 0;
+  int b = row[k / 5];
+  switch (k % 5) {
+    case 4: b /= 81; break;
+    case 3: b /= 27; break;
+    case 2: b /= 9; break;
+    case 1: b /= 3; break;
+    default: break;
+  }
+  return b % 3 - 1;
+}
+
 __global__ void repack_tiled_kernel(const uint8_t *P, int64_t R, int64_t ldp, Geom g, int64_t total, uint8_t *Pt) {
   int64_t off = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (off >= total) return;
   int64_t tile;
   int lane, b;
   tiled_coords(g, off, tile, lane, b);
-  int64_t row = tile * 16 + (lane & 15);
-  int64_t j = (int64_t)(lane >> 4) * g.Q + b;
-  uint8_t v = 121;  // five zero trits
-  if (row < R && j < g.Kb) v = P[row * ldp + j];
-  Pt[off] = v;
+  const int64_t row = tile * 16 + (lane & 15);
+  const int quarter = lane >> 4;
+  int code = 0, p3 = 1;
+#pragma unroll
+  for (int q = 0; q < 5; ++q, p3 *= 3) {
+    const int t = row < R ? canon_trit(P + row * ldp, g.K, tiled_k(g, quarter, b, q)) : 0;
+    code += (t + 1) * p3;
+  }
+  Pt[off] = (uint8_t)code;
 }
 
 __global__ void unpack_tiled_kernel(const uint8_t *Pt, int64_t R, Geom g, int64_t total, int8_t *T) {
@@ -175,15 +194,17 @@ __global__ void unpack_tiled_kernel(const uint8_t *Pt, int64_t R, Geom g, int64_
   int64_t tile;
   int lane, b;
   tiled_coords(g, off, tile, lane, b);
-  int64_t row = tile * 16 + (lane & 15);
-  int64_t j = (int64_t)(lane >> 4) * g.Q + b;
-  if (row >= R || j >= g.Kb) return;
+  const int64_t row = tile * 16 + (lane & 15);
+  if (row >= R) return;
+  const int quarter = lane >> 4;
   int8_t t[5];
-  int v = Pt[off];
+  const int v = Pt[off];
   decode5(v > 242 ? 121 : v, t);
 #pragma unroll
-  for (int q = 0; q < 5; ++q)
-    if (5 * j + q < g.K) T[row * g.K + 5 * j + q] = t[q];
+  for (int q = 0; q < 5; ++q) {
+    const int64_t k = tiled_k(g, quarter, b, q);
+    if (k < g.K) T[row * g.K + k] = t[q];
+  }
 }
 
 int launch_repack_tiled(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, int64_t ldp, uint8_t *Pt) {

@@ -40,7 +40,8 @@ def host(t):
 
 
 def ws_bytes(n):
-    return torch.empty(max(int(n), 16), dtype=torch.uint8, device="cuda")
+    # workspaces are zero-filled once after allocation (the layer keeps a counter there)
+    return torch.zeros(max(int(n), 16), dtype=torch.uint8, device="cuda")
 
 
 # --------------------------------------------------------------------- inputs
@@ -95,12 +96,40 @@ def test_tiled_layout_roundtrip(tm, R, K):
     T = torch.zeros((R, K), dtype=torch.int8, device="cuda")
     tm.unpack_tiled(Pt, R, K, T)
     assert np.array_equal(host(T), t)
-    pt = host(Pt)
-    assert pt.max() <= 242
-    # the tiled image holds the canonical bytes once each plus pad codes (121)
-    assert np.bincount(pt, minlength=243)[:243].sum() == pt.size
-    extra = pt.size - P.size
-    assert extra >= 0 and np.sum(pt == 121) >= extra
+    assert np.array_equal(host(Pt), _tiled_image(t))
+
+
+def _tiled_image(t):
+    """The tiled byte image of trits t [R][K], built from the layout's
+    description (16-row tiles, four quarters of 5Q inputs, steps of 8 bytes
+    whose byte 2p+h holds inputs 40*step + 10p + 2q + h of the quarter)."""
+    R, K = t.shape
+    Q = -(-(-(-K // 5)) // 4)
+    Q += Q % 2
+    Q = max(Q, 2)
+    F, r = Q // 8, Q % 8
+    tile_bytes = 64 * Q
+    nt = -(-R // 16)
+    out = np.zeros(nt * tile_bytes, dtype=np.uint8)
+    tp = np.zeros((nt * 16, 20 * Q), dtype=np.int64)
+    tp[:R, :K] = t
+    for lane in range(64):
+        i, g = lane & 15, lane >> 4
+        for b in range(Q):
+            if b < 8 * F:
+                s, bb = b // 8, b % 8
+                off = s * 512 + lane * 8 + bb
+            else:
+                s, bb = F, b - 8 * F
+                if r >= 4:
+                    off = 512 * F + (lane * 4 + bb if bb < 4 else 256 + lane * 2 + bb - 4)
+                else:
+                    off = 512 * F + lane * 2 + bb
+            ks = [5 * Q * g + 40 * s + 10 * (bb >> 1) + 2 * q + (bb & 1) for q in range(5)]
+            rows = np.arange(nt) * 16 + i
+            code = sum((tp[rows, k] + 1) * 3 ** q for q, k in enumerate(ks))
+            out[np.arange(nt) * tile_bytes + off] = code
+    return out
 
 
 # ------------------------------------------------------------- ternary linear
@@ -175,15 +204,19 @@ def test_router_parity(tm, cfg, T, bias_kind):
     b = ti.router_bias(cfg, bias_kind)
     idx, w, nfix, lg = _router(tm, xb, Wr, b, 8)
     ridx, rw, rL, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
-    say(f"  fp64 fix-ups: {nfix} of {T}")
+    say(f"  exact-path tokens: {nfix} of {T}")
+    assert nfix == 0  # fp64 logits separate every ranking of these inputs
     assert np.array_equal(idx, ridx)
     assert O.max_normalized_error(w, rw) <= TOL
     assert O.max_normalized_error(lg, rL) <= TOL
     assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
 
 
-def test_router_ties_take_fp64_path(tm):
-    T, H, E = 40, 2048, 256
+@pytest.mark.parametrize("T", [40, 8])
+def test_router_ties_take_exact_path(tm, T):
+    # exactly equal logits cannot be certified by the error bound: those tokens
+    # are recomputed in double-double and the tie goes to the lower index
+    H, E = 2048, 256
     xb = ti.activations(9, T)
     Wr = ti.router_matrix(9, 0).copy()
     Wr[200] = Wr[17]
@@ -344,6 +377,44 @@ def test_layer_is_deterministic(tm, layers):
     b = _run_layer(tm, W, xb)
     for key in ("Y", "idx", "w", "pos"):
         assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_layer_workspace_reuse(tm, layers):
+    # one workspace, alternating decode sizes: the in-workspace counter is left at zero by every call
+    W = layers(2, 0, None)
+    ws = ws_bytes(tm.moe_workspace_bytes(16, W))
+    outs = {}
+    for rep in range(3):
+        for T in (1, 16, 5):
+            xb = ti.activations(7, T)
+            Y = torch.empty((T, 2048), dtype=torch.float32, device="cuda")
+            idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+            tm.moe_forward(W, bf16_dev(xb), Y, ws, idx=idx)
+            got = (host(Y), host(idx))
+            if rep == 0:
+                outs[T] = got
+                ridx, _, _, _ = O.router_topk(O.bf16_to_f64(xb), ti.router_matrix(2, 0), None, 8)
+                assert np.array_equal(got[1], ridx)
+            else:
+                assert np.array_equal(got[0], outs[T][0]) and np.array_equal(got[1], outs[T][1])
+
+
+def test_layer_decode_ties(tm, layers):
+    # the fused decode front end with exactly tied router rows (exact path inside the kernel)
+    from ternary_weight_moe_base_amd import synthetic
+    W = layers(2, 0, None)
+    Wr = W.tensors[0].clone()
+    Wr[99] = Wr[3]
+    Wr[250] = Wr[3]
+    b = torch.zeros(256, dtype=torch.float32, device="cuda")
+    b[[3, 99, 250]] = 5.0
+    W2 = type(W)(Wr, b, *W.tensors[2:], top_k=8)
+    xb = ti.activations(11, 6)
+    got = _run_layer(tm, W2, xb)
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), host(Wr), host(b), 8)
+    assert got["nfix"] == 6
+    assert np.array_equal(got["idx"], ridx)
+    assert np.all(got["idx"][:, :3] == [3, 99, 250])
 
 
 def test_layer_empty_batch(tm, layers):

@@ -72,8 +72,7 @@ def philox_words(stream: int, first: int, n: int) -> np.ndarray:
 def ih12_normal(stream: int, n: int, first: int = 0) -> np.ndarray:
     """n float32 Irwin-Hall(12) draws of one stream (see module docstring)."""
     words = philox_words(stream, first, n)[:, :3].copy()
-    u16 = words.view(np.uint16).reshape(n, 12).astype(np.int64)
-    s = u16.sum(axis=1) - IH12_OFFSET
+    s = words.view(np.uint16).reshape(n, 12).sum(axis=1, dtype=np.int32) - IH12_OFFSET
     return (s.astype(np.float32) * np.float32(2.0 ** -16)).astype(np.float32)
 
 
