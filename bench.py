@@ -23,6 +23,7 @@ import time
 METRIC = "ternary MoE layer tokens/s (decode & prefill); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
+FP64_PEAK_TFLOPS = 78.6  # fp64 vector / matrix
 H, I, E, K_TOP = 2048, 512, 256, 8
 PACKED_GU = I * ((H + 4) // 5)  # bytes of one gate or up matrix
 PACKED_D = H * ((I + 4) // 5)
@@ -37,6 +38,50 @@ WORKLOADS = {
 }
 
 
+# kernels each path launches (names of the C ABI's timing hook)
+DECODE_KERNELS = ("router_logits", "gateup", "down", "combine")
+BATCH_KERNELS = ("router_logits", "router_topk", "router_fixup", "group", "make_tiles", "gateup", "down", "combine")
+
+
+def roofline(name, ms, n_hit, T, cfg, bias):
+    """Achieved rate of one kernel: algorithmic bytes (or flops) per launch over
+    its mean launch duration. Algorithmic bytes count what the step must move:
+    packed weights + scales of the experts with a routed token, the fp32 router,
+    the layer input X and output Y; intermediates (logits, h, expert outputs)
+    are not counted."""
+    import numpy as np
+
+    P = T * K_TOP
+    mean_s = float(np.mean(ms)) * 1e-3
+    x_b, y_b = T * H * 2, T * H * (2 if cfg == 5 else 4)
+    flops = None
+    if name == "router_logits":
+        b = np.full(len(n_hit), ROUTER_BYTES + x_b + (E * 4 if bias else 0) + (T * K_TOP * 8 if T <= 16 else 0))
+        flops, fpeak = 2.0 * T * E * H, FP64_PEAK_TFLOPS
+    elif name == "gateup":
+        b = n_hit * 2 * (PACKED_GU + 4 * I) + x_b
+        flops, fpeak = 4.0 * P * I * H, BF16_PEAK_TFLOPS
+    elif name == "down":
+        b = n_hit * (PACKED_D + 4 * H)
+        flops, fpeak = 2.0 * P * I * H, BF16_PEAK_TFLOPS
+    elif name == "combine":
+        b = np.full(len(n_hit), y_b + (x_b if cfg == 5 else 0) + T * K_TOP * 8)
+    else:  # top-k, grouping, tiles: index arrays only
+        b = np.full(len(n_hit), T * K_TOP * 4 * 4)
+    mean_b = float(np.mean(b))
+    if cfg == 4 and flops is not None:
+        achieved = flops / mean_s / 1e12
+        r = {"bound": "alu" if name == "router_logits" else "mfma", "achieved": achieved, "peak": fpeak, "unit": "TFLOP/s", "frac": achieved / fpeak,
+             "traffic": None, "algorithmic_flops_per_launch": flops}
+    else:
+        achieved = mean_b / mean_s / 1e9
+        r = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    r.update({"kernel": name, "mean_launch_us": mean_s * 1e6, "launches": int(len(ms)),
+              "algorithmic_bytes_per_launch": mean_b})
+    return r
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,7 +89,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="distinct layers to rotate over")
-    ap.add_argument("--kernel", default="gateup", help="kernel whose roofline is reported")
+    ap.add_argument("--kernel", default=None, help="kernel whose roofline is reported (default: the dominant one)")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
@@ -63,8 +108,12 @@ def ensure_built():
 
 
 # -------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg: int, wl: dict, n_tok: int):
-    """The CPU oracle, untuned, timed on this host on a bounded token sample."""
+def cpu_baseline(cfg: int, wl: dict, n_tok: int | None, budget_s: float = 12.0):
+    """The CPU oracle, untuned, timed on this host on a bounded sample of the
+    workload: successive token batches of the workload (for one-token decode,
+    token i through layer i mod 24) until `budget_s` seconds of oracle time or
+    n_tok tokens. The inputs a batch reads (router, raw fp32 experts it routes
+    to) are drawn before its timed call; only the oracle's moe_layer is timed."""
     import numpy as np
 
     import oracle as O
@@ -76,41 +125,28 @@ def cpu_baseline(cfg: int, wl: dict, n_tok: int):
         blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas = 1
-    layer_of = (lambda i: i % wl["layers"]) if cfg in (2, 3, 4) else (lambda i: 0)
     if cfg == 2:
-        batches = [(i, ti.activations(cfg, i + 1)[i:i + 1]) for i in range(n_tok)]
+        batches = ((i % wl["layers"], ti.activations(cfg, i + 1)[i:i + 1]) for i in range(n_tok or 1000))
     else:
         x = ti.activations(cfg, wl["tokens"])
-        batches = [(0, x[:n_tok])]
-    cache = {}
-
-    def raw(layer, e):
-        if (layer, e) not in cache:
-            cache[(layer, e)] = tuple(ti.expert_matrix(cfg, layer, e, m) for m in range(3))
-        return cache[(layer, e)]
-
-    # draw the inputs the oracle will read (untimed): router, then the routed experts
-    prep = []
-    for i, xb in batches:
-        layer = layer_of(i)
-        Wr, b = ti.router_matrix(cfg, layer), ti.router_bias(cfg, wl["bias"])
-        idx, _, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, K_TOP)
-        prep.append((layer, xb, Wr, b, sorted(set(idx.ravel().tolist()))))
+        batches = ((0, x[j:j + 8]) for j in range(0, min(n_tok or len(x), len(x)), 8))
+    tokens, timed = 0, 0.0
     with concurrent.futures.ThreadPoolExecutor(min(16, threads)) as ex:
-        keys = [(layer, e) for layer, _, _, _, es in prep for e in es]
-        for k_, v in zip(keys, ex.map(lambda le: tuple(ti.expert_matrix(cfg, le[0], le[1], m) for m in range(3)),
-                                      keys)):
-            cache[k_] = v
-    tokens = 0
-    t0 = time.perf_counter()
-    for layer, xb, Wr, b, _ in prep:
-        O.moe_layer(xb, Wr, b, lambda e, layer=layer: raw(layer, e), k=K_TOP)
-        tokens += xb.shape[0]
-    dt = time.perf_counter() - t0
-    per_layer_tokens = tokens
-    sample = (f"{per_layer_tokens} token(s) of the {wl['name']} workload through the oracle's moe_layer "
-              f"(raw fp32 experts drawn beforehand, untimed), {dt:.1f} s")
-    return {"value": per_layer_tokens / dt, "unit": "tokens/s", "cores": blas if blas > 1 else 1,
+        for layer, xb in batches:
+            Wr, b = ti.router_matrix(cfg, layer), ti.router_bias(cfg, wl["bias"])
+            idx, _, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, K_TOP)
+            es = sorted(set(idx.ravel().tolist()))
+            mats = dict(zip(es, ex.map(lambda e: tuple(ti.expert_matrix(cfg, layer, e, m) for m in range(3)), es)))
+            t0 = time.perf_counter()
+            O.moe_layer(xb, Wr, b, lambda e: mats[e], k=K_TOP)
+            timed += time.perf_counter() - t0
+            tokens += xb.shape[0]
+            if timed >= budget_s:
+                break
+    what = "token i through layer i mod 24" if cfg == 2 else "batches of 8 tokens through layer 0"
+    sample = (f"{tokens} token(s) of the {wl['name']} workload ({what}) through the oracle's moe_layer; "
+              f"{timed:.1f} s of oracle time; router and raw fp32 experts drawn beforehand, untimed")
+    return {"value": tokens / timed, "unit": "tokens/s", "cores": blas if blas > 1 else 1,
             "host_cpus": threads, "kind": "oracle", "sample": sample}
 
 
@@ -119,8 +155,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures a single GPU only: the layer is data-parallel and this build runs "
-              "and reports one MI355X (--gpus 1). Multi-GPU runs are not supported.", file=sys.stderr)
+        print("bench.py measures a single GPU only: the layer is data-parallel, and this benchmark "
+              "runs and reports one MI355X (--gpus 1). Multi-GPU runs are not supported.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -181,8 +217,6 @@ def main():
         torch.cuda.synchronize()
         graph.replay()  # first replay of a fresh graph: untimed
         torch.cuda.synchronize()
-    else:
-        tm.profile_begin(args.kernel, prof_cap)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -193,13 +227,19 @@ def main():
             step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    if use_graph:
-        # Kernel durations: the same K steps launched eagerly, the selected
-        # kernel carrying start/stop events recorded by its own dispatch.
-        tm.profile_begin(args.kernel, prof_cap)
+
+    # Per-kernel durations: the same K steps launched again (eagerly), one
+    # kernel at a time carrying start/stop events recorded by its own dispatch
+    # on the stream it runs on.
+    kern = {}
+    for name in (DECODE_KERNELS if T <= 16 else BATCH_KERNELS):
+        tm.profile_begin(name, prof_cap)
         for i in range(W_, W_ + K):
             step(i)
-    kern_ms = tm.profile_end(prof_cap)
+        ms = tm.profile_end(prof_cap)
+        if len(ms):
+            kern[name] = ms
+    torch.cuda.synchronize()
 
     ms_per_step = 1e3 * elapsed / K
     layer_passes = K * (L if cfg == 5 else 1)
@@ -215,32 +255,11 @@ def main():
     step_bytes = ROUTER_BYTES + n_hit * EXPERT_BYTES + T * H * 2 + T * H * (2 if cfg == 5 else 4)
     hbm_gbs = float(step_bytes.sum()) / elapsed / 1e9
 
-    # roofline of the selected kernel: algorithmic bytes (or flops) per launch / mean launch time
-    P = T * K_TOP
-    mean_ms = float(np.mean(kern_ms)) if len(kern_ms) else float("nan")
-    if args.kernel == "gateup":
-        kb = n_hit * 2 * (PACKED_GU + 4 * I) + T * H * 2 + P * I * 4
-        kflops = 4.0 * P * I * H
-    elif args.kernel == "down":
-        kb = n_hit * (PACKED_D + 4 * H) + P * I * 4 + P * H * 4
-        kflops = 2.0 * P * I * H
-    elif args.kernel == "router_logits":
-        kb = np.full(len(n_hit), ROUTER_BYTES + T * H * 2 + T * E * 4)
-        kflops = 2.0 * T * E * H
-    else:
-        kb = np.full(len(n_hit), np.nan)
-        kflops = float("nan")
-    mean_kb = float(np.mean(kb))
-    if cfg == 4:
-        achieved = kflops / (mean_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
-    else:
-        achieved = mean_kb / (mean_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    roof.update({"kernel": args.kernel, "mean_launch_us": mean_ms * 1e3, "launches": int(len(kern_ms)),
-                 "algorithmic_bytes_per_launch": mean_kb})
+    # roofline of the dominant kernel (largest total time per step)
+    per_step_us = {n: float(np.sum(v)) * 1e3 / layer_passes for n, v in kern.items()}
+    dom = args.kernel if args.kernel else max(per_step_us, key=per_step_us.get)
+    roof = roofline(dom, kern[dom], n_hit, T, cfg, bias=wl["bias"] is not None)
+    roof["kernels_us_per_layer"] = {n: round(v, 3) for n, v in per_step_us.items()}
 
     out = {
         "metric": METRIC,
@@ -264,9 +283,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        n_tok = args.cpu_tokens if args.cpu_tokens is not None else (6 if cfg == 2 else 8)
-        log(f"timing the CPU oracle on {n_tok} token(s)")
-        out["cpu_baseline"] = cpu_baseline(cfg, wl, n_tok)
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

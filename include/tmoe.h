@@ -55,7 +55,7 @@ enum {
   TMOE_E_ALIGN = -3,       /* device pointer not 16-byte aligned */
   TMOE_E_BADPACK = -4,     /* a packed byte > 242 (not a 5-trit code) */
   TMOE_E_WORKSPACE = -5,   /* workspace null or smaller than required */
-  TMOE_E_UNSUPPORTED = -6, /* valid request this build does not implement */
+  TMOE_E_UNSUPPORTED = -6, /* valid request this library does not implement */
   TMOE_E_HIP = -7          /* the HIP runtime reported an error */
 };
 
@@ -260,15 +260,16 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
  * launches, not inside HIP graph capture. The events
  * are created by tmoe_profile_begin (not on the hot path) and destroyed by
  * tmoe_profile_end, which waits for them and writes the per-launch durations
- * in milliseconds to ms[0..*count). Global state: not thread-safe; one
+ * in milliseconds to ms[0..*count). The events carry no system-scope fence
+ * (hipEventDisableSystemFence), so they add no cache write-back to the timed
+ * dispatch. Global state: not thread-safe; one
  * profiling window at a time (TMOE_E_ARG otherwise). */
 enum {
-  TMOE_KERNEL_ROUTER_LOGITS = 1,
+  TMOE_KERNEL_ROUTER_LOGITS = 1, /* for T <= 16: the fused decode router (logits, top-k, grouping) */
   TMOE_KERNEL_ROUTER_TOPK = 2,
   TMOE_KERNEL_ROUTER_FIXUP = 3,
   TMOE_KERNEL_GROUP = 4, /* the fused grouping kernel (first kernel when T > 256) */
   TMOE_KERNEL_MAKE_TILES = 5,
-  TMOE_KERNEL_PERMUTE_X = 6,
   TMOE_KERNEL_GATEUP = 7,
   TMOE_KERNEL_DOWN = 9,
   TMOE_KERNEL_COMBINE = 10,

@@ -24,7 +24,7 @@ what the layer is defined to compute. Sources (the pages are the authority):
 * jj-blog (Maple-Preview news), architecture list: hidden 2048, 256 experts,
   8 per token, no shared expert, moe_intermediate_size 512, 24 layers.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 scale = fp32 of the fp64 mean of |W_row| summed in index order; trit =
 sign(W) where 2|W| > s, else 0 (RoundClip(W/s) with ties to zero, no
 epsilon); digit d = t + 1, little-endian base 3 along the input dimension,

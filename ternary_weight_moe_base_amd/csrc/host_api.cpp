@@ -449,8 +449,9 @@ int tmoe_profile_begin(int kernel, int capacity) {
   g_prof.stop = new hipEvent_t[capacity]();
   g_prof.cap = capacity;
   for (int i = 0; i < capacity; ++i) {
-    hipError_t e = hipEventCreate(&g_prof.start[i]);
-    if (e == hipSuccess) e = hipEventCreate(&g_prof.stop[i]);
+    // timing-only events: no system-scope fence (no cache write-back around the kernel)
+    hipError_t e = hipEventCreateWithFlags(&g_prof.start[i], hipEventDisableSystemFence);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_prof.stop[i], hipEventDisableSystemFence);
     if (e != hipSuccess) {
       prof_free();
       return hip_fail(e, "hipEventCreate");

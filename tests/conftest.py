@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is visible, so a plain
-    # `pytest tests/` on a CPU host stays green; `-m gpu` on the GPU machine runs them.
+    # `pytest tests/` on a CPU host stays green; `-m gpu` on a GPU host runs them.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
