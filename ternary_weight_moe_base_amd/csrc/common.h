@@ -151,24 +151,22 @@ int launch_repack_tiled(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, 
 int launch_unpack_tiled(hipStream_t st, const uint8_t *Pt, int64_t R, int64_t K, int8_t *T);
 
 struct RouterWs {
-  uint32_t *ctr;       // completion counter of the fused decode kernel; zero between calls
   uint64_t *bnd;       // [T] bits of max_e (sum_i |x_i w_ei| + |b_e|) (fp64, >= 0); zero between calls
   double *lg;          // [T][E] fp64 logits
   int32_t *fix_count;  // [1]
   int32_t *fix_list;   // [T]
-  int32_t *scratch;    // grouping outputs of the router-only decode path
 };
 size_t router_ws_bytes(int64_t T, int64_t E);
 RouterWs router_ws_carve(void *ws, int64_t T, int64_t E);
+// Logits, certified top-k and double-double fix-up (three kernels).
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                   int64_t E, int k, int32_t *idx, float *w, float *logits_out, int32_t *n_fixup, const RouterWs &rw);
-// Fused decode front end (T <= kDecodeMaxT): router, top-k, grouping, work
-// tiles and permuted activations in one kernel.
+// Logits and per-token bounds only (the decode layer path certifies the top-k
+// in the gate/up kernel's prologue). Returns the accumulation depth in *depth.
+int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
+                         int64_t E, const RouterWs &rw, int *depth);
+// Decode path (T <= kDecodeMaxT): every (token, slot) pair of an expert fits one work tile.
 constexpr int kDecodeMaxT = 16;
-int launch_router_decode(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
-                         int64_t E, int k, const RouterWs &rw, int32_t *idx, float *w, int32_t *n_fixup,
-                         int32_t *counts, int32_t *offsets, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos,
-                         int32_t *tiles, int32_t *ntiles);
 
 struct GroupWs {
   int32_t *bcount;  // [nb][E]
@@ -184,13 +182,36 @@ struct FfnWs {
   int32_t *ntiles;   // [1]
   uint16_t *hp;      // [3][T*k][slots_I] bf16 parts hi + mid + lo = h of each grouped pair,
                      // in the down projection's operand layout
+  float *pw;         // [T*k] routing weight of each grouped pair (decode path)
 };
 int64_t ffn_max_tiles(int64_t pairs, int64_t E);
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I);
 FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I);
-// prepared: tiles and ntiles were already written (fused decode front end)
+// Grouped expert FFN (gate/up + SiLU/clamp, down) from grouping offsets.
 int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
-               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool prepared);
+               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw);
+
+// Decode layer tail (T <= kDecodeMaxT): gate/up whose prologue certifies the
+// top-k of every token from the fp64 logits and groups the pairs (workgroup
+// (0, 0) publishes idx, w, grouping arrays and work tiles), then, for at most
+// kDcMaxPairs pairs, down with the weighted combine (+ residual) fused, else
+// down into O and the combine. The per-token bound slots are cleared for the
+// next call.
+struct DecodeRoute {
+  const double *lg;
+  uint64_t *bnd;
+  int depth;
+  const float *Wr, *bias;
+  int32_t *idx, *n_fixup, *sorted_token, *sorted_slot, *pos;
+  float *w;
+  int32_t *tiles, *ntiles;  // set by launch_decode_tail (FFN workspace)
+  float *pair_w;            // [T*k] routing weight of each grouped pair (FFN workspace)
+};
+// O [T*k][H] is used (and must exist) only when T*k > kDcMaxPairs.
+constexpr int kDcMaxPairs = 32;
+int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float clamp,
+                       const DecodeRoute &r, const FfnWs &fw, float *O, float *Y, const uint16_t *resid_in,
+                       uint16_t *resid_out);
 
 size_t linear_ws_bytes(int64_t T, int64_t K);
 int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,

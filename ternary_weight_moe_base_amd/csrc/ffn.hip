@@ -20,7 +20,7 @@
 //    is fp32: it is split exactly into three bf16 parts h = hi + mid + lo (each
 //    rounding keeps the next 8 of the 24 significant bits), each multiplied
 //    exactly.
-#include "device_util.h"
+#include "route_util.h"
 
 namespace tmoe {
 
@@ -168,20 +168,146 @@ struct GateUpArgs {
   Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
   int I;
   float clamp;
+  // routing prologue (decode path only)
+  DecodeRoute r;
+  int T, E, k;
 };
+
+// ------------------------------------------------------ routing prologue
+// Decode path (T <= 16 tokens, so one work tile per hit expert): every
+// workgroup certifies the top-k of all tokens from the fp64 logits (one
+// wavefront per token; the double-double recompute when the bound cannot
+// separate the top k+1), then each (token, slot) pair finds, from the others,
+// its grouped position (pairs of lower experts, then of the same expert and a
+// lower token) and its tile (hit experts below its expert). The workgroup takes
+// the blockIdx.x-th hit expert (in expert order) as its tile. Workgroup (0, 0)
+// publishes idx, w, pos, the grouped tokens, slots and weights, and the tiles.
+struct RouteLds {
+  int32_t sidx[kDecodeMaxT * 16];
+  float sw[kDecodeMaxT * 16];
+  uint32_t hit[32];  // bit e: some token chose expert e (E <= 1024)
+  int32_t tok[kDecodeMaxT];
+  int32_t info[3];  // expert (-1: none), start, count of this workgroup's tile
+  int32_t nfix;
+};
+
+template <int NPL>
+__device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *smem, int rs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const DecodeRoute &r = a.r;
+  const int T = a.T, E = a.E, k = a.k, P = T * k;
+  const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
+  // order keys of this wavefront's tokens (t = wave + 4q), in flight with the staging below
+  uint64_t key[kDecodeMaxT / 4][NPL];
+  double bnd[kDecodeMaxT / 4];
+#pragma unroll
+  for (int q = 0; q < kDecodeMaxT / 4; ++q) {
+    const int t = wave + 4 * q;
+    if (t < T) {
+      topk_keys<NPL>(r.lg + (int64_t)t * E, E, key[q]);
+      bnd[q] = bitsd(r.bnd[t]);
+    }
+  }
+  // every token's activations into LDS row t, zero row 16
+  const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
+  for (int i = threadIdx.x; i < T * vec; i += 256) {
+    const int t = i / vec, c = i - t * vec;
+    *reinterpret_cast<uint4 *>(smem + t * rs + c * 16) =
+        c < kv ? reinterpret_cast<const uint4 *>(a.X + (int64_t)t * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
+  }
+  zero_row(smem + 16 * rs, a.gx.slots, threadIdx.x, 256);
+  if (threadIdx.x < 32) s.hit[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    s.info[0] = -1;
+    s.nfix = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kDecodeMaxT / 4; ++q) {
+    const int t = wave + 4 * q;
+    if (t < T) {
+      const double B = 1.01 * gamma_d(r.depth) * bnd[q];
+      if (!topk_select<NPL>(key[q], E, k, B, s.sidx + t * k, s.sw + t * k)) {
+        if (lane == 0) atomicAdd(&s.nfix, 1);
+        topk_dd<NPL>(a.X + (int64_t)t * a.gx.K, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx + t * k, s.sw + t * k,
+                     nullptr);
+      }
+    }
+  }
+  __syncthreads();
+  const int i = threadIdx.x;
+  if (i < P) atomicOr(&s.hit[s.sidx[i] >> 5], 1u << (s.sidx[i] & 31));
+  __syncthreads();
+  if (i < P) {
+    const int t = i / k, j = i - t * k, e = s.sidx[i];
+    int before = 0, same = 0, cnt = 0;
+    for (int i2 = 0; i2 < P; ++i2) {
+      const int e2 = s.sidx[i2];
+      before += e2 < e;
+      if (e2 == e) {
+        ++cnt;
+        same += i2 < i;  // same expert, lower token
+      }
+    }
+    const int pos = before + same;
+    int tl = __popc(s.hit[e >> 5] & ((1u << (e & 31)) - 1u));
+    for (int q = 0; q < (e >> 5); ++q) tl += __popc(s.hit[q]);
+    if (tl == (int)blockIdx.x) {
+      s.tok[same] = t;
+      if (same == 0) {
+        s.info[1] = before;
+        s.info[2] = cnt;
+        s.info[0] = e;
+      }
+    }
+    if (publish) {
+      r.idx[i] = e;
+      r.w[i] = s.sw[i];
+      r.pos[i] = pos;
+      r.sorted_token[pos] = t;
+      r.sorted_slot[pos] = j;
+      r.pair_w[pos] = s.sw[i];
+      if (same == 0) reinterpret_cast<int4 *>(r.tiles)[tl] = make_int4(e, before, cnt, 0);
+    }
+  }
+  if (publish && threadIdx.x == 0) {
+    int nh = 0;
+    for (int q = 0; q < (E + 31) / 32; ++q) nh += __popc(s.hit[q]);
+    *r.ntiles = nh;
+    if (r.n_fixup) *r.n_fixup = s.nfix;
+  }
+  __syncthreads();
+}
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
 // Workgroup = 4 wavefronts. KS wavefronts split the K steps of one 16-row tile
 // (partial sums reduced in LDS in fixed order); 4/KS row tiles per workgroup.
 // blockIdx.x = work tile (expert, <= 16 pairs), blockIdx.y = row-tile group.
-template <int F, int RT, int KS>
+// RNPL > 0: decode path with the routing prologue (experts per lane of its top-k).
+template <int F, int RT, int KS, int RNPL>
 __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int tile = blockIdx.x;
-  if (tile >= *a.ntiles) return;
-  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[tile];
-  const int e = td.x, start = td.y, cnt = td.z;
+  int e, start, cnt;
+  const int32_t *toks;
+  const int rs0 = lds_row_bytes(a.gx.slots);
+  if constexpr (RNPL > 0) {
+    __shared__ RouteLds rl;
+    route_prologue<RNPL>(a, rl, smem, rs0);
+    e = rl.info[0];
+    if (e < 0) return;
+    start = rl.info[1];
+    cnt = rl.info[2];
+    toks = rl.tok;
+  } else {
+    const int tile = blockIdx.x;
+    if (tile >= *a.ntiles) return;
+    const int4 td = reinterpret_cast<const int4 *>(a.tiles)[tile];
+    e = td.x;
+    start = td.y;
+    cnt = td.z;
+    toks = a.sorted_token + start;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int RTB = 4 / KS;
   constexpr int M = 5 * F + tail_mfmas(RT);
@@ -204,6 +330,10 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
       ud[i] = *reinterpret_cast<const uint2 *>(ut + (int64_t)(s0 + i) * 512 + lane * 8);
     }
   }
+  // row scales of this lane's four output rows (epilogue), fetched with the weights
+  const int row0 = rt * 16 + 4 * (lane >> 4);
+  const float4 sg = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
+  const float4 su = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
   uint32_t gdw = 0, gsh = 0, udw = 0, ush = 0;
   const bool tail_here = RT > 0 && kp == KS - 1;
   if (tail_here) {
@@ -211,22 +341,27 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     load_tail<RT>(ut, F, lane, udw, ush);
   }
 
-  // activations of the tile's pairs (natural order = operand order for H = 2048)
-  const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
-  for (int i = threadIdx.x; i < cnt * vec; i += 256) {
-    const int n = i / vec, c = i - n * vec;
-    const int64_t tok = a.sorted_token[start + n];
-    *reinterpret_cast<uint4 *>(xs + n * rs + c * 16) =
-        c < kv ? reinterpret_cast<const uint4 *>(a.X + tok * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
+  if constexpr (RNPL == 0) {
+    // activations of the tile's pairs (natural order = operand order for H = 2048)
+    const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
+    for (int i = threadIdx.x; i < cnt * vec; i += 256) {
+      const int n = i / vec, c = i - n * vec;
+      const int64_t tok = toks[n];
+      *reinterpret_cast<uint4 *>(xs + n * rs + c * 16) =
+          c < kv ? reinterpret_cast<const uint4 *>(a.X + tok * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
+    }
+    zero_row(xs + 16 * rs, a.gx.slots, threadIdx.x, 256);
   }
-  zero_row(xs + 16 * rs, a.gx.slots, threadIdx.x, 256);
   // zero pad positions of this tile's rows of the down operand (written once per pair)
   if (blockIdx.y == 0 && wave == 0) {
+    const int q5 = 5 * a.gd.Q;
     for (int n = 0; n < cnt; ++n)
-      for (int i = lane; i < a.gd.slots; i += 64) {
-        const int quarter = i / a.gd.QS, j = i - quarter * a.gd.QS;
-        if (operand_k(a.gd, quarter, j) < 0) {
-          const int64_t o = (int64_t)(start + n) * a.gd.slots + i;
+      for (int g = 0; g < 4; ++g) {
+        // quarter g holds inputs 5Qg .. 5Qg + 5Q - 1 (those < K) at positions 0 ..
+        const int64_t live = a.gd.K - (int64_t)q5 * g;
+        const int lo = live < 0 ? 0 : (live < q5 ? (int)live : q5);
+        for (int j = lo + lane; j < a.gd.QS; j += 64) {
+          const int64_t o = (int64_t)(start + n) * a.gd.slots + g * a.gd.QS + j;
           a.hp[o] = 0;
           a.hp[a.hp_plane + o] = 0;
           a.hp[2 * a.hp_plane + o] = 0;
@@ -236,7 +371,8 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
-  const char *bp = xs + (n < cnt ? n : 16) * rs + g * M * 16;
+  const int brow = n < cnt ? (RNPL > 0 ? toks[n] : n) : 16;
+  const char *bp = xs + brow * rs + g * M * 16;
   f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < SMAX; ++i) {
@@ -291,9 +427,6 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     }
   }
   if (n >= cnt) return;
-  const int row0 = rt * 16 + 4 * g;
-  const float4 sg = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
-  const float4 su = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
   const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
   float hv[4];
   const float c = a.clamp;
@@ -397,6 +530,114 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   o.z = (acc[2] * 0.5f) * sd.z;
   o.w = (acc[3] * 0.5f) * sd.w;
   *reinterpret_cast<float4 *>(a.O + p * a.H + row0) = o;
+}
+
+// ------------------------------------------------- down + combine (decode)
+struct DownCombineArgs {
+  const uint8_t *down_p;
+  int64_t stride_d;
+  const float *down_s;
+  const uint16_t *hp;  // [3][pairs][slots] bf16 parts of h (operand layout), contiguous
+  int slots;
+  const int32_t *tiles, *ntiles, *sorted_token;
+  const float *pair_w;  // [pairs] routing weight of each grouped pair
+  int P, T, H, max_tiles;
+  float *Y;                   // [T][H] or null
+  const uint16_t *resid_in;   // [T][H] bf16 or null
+  uint16_t *resid_out;        // [T][H] bf16 or null (may alias resid_in)
+  uint64_t *bnd;              // per-token bound slots, cleared here for the next call
+};
+
+constexpr int kDcWaves = 8;
+
+// Decode path with few pairs (T*k <= 32): workgroup = one 16-row block of the
+// H outputs for all work tiles. The three bf16 parts of h of every pair are
+// staged in LDS together with the first tile descriptors; wavefront w then takes
+// tiles w, w + 8, ... in order and adds pair_w * o (o = sd * (Td h)) into its
+// own LDS accumulator of the pair's token; the accumulators are summed in fixed
+// order, then Y and/or the residual bf16(x + y) are written. MFMA columns past
+// the tile's pairs repeat its last pair and are discarded.
+template <int F, int RT>
+__global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombineArgs a) {
+  extern __shared__ __align__(16) char hps[];  // [3][P][slots] bf16
+  __shared__ float yacc[kDcWaves][kDecodeMaxT][16];
+  __shared__ int32_t s_tok[kDcMaxPairs];
+  __shared__ float s_pw[kDcMaxPairs];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rt = blockIdx.x;
+  constexpr int M = 5 * F + tail_mfmas(RT);
+  const int nt = *a.ntiles;
+  int4 td0 = make_int4(0, 0, 1, 0);
+  if (wave < a.max_tiles) td0 = reinterpret_cast<const int4 *>(a.tiles)[wave];  // first tile, before nt is known
+  const int nchunk = 3 * a.P * a.slots / 8;
+  for (int c = threadIdx.x; c < nchunk; c += 64 * kDcWaves)
+    reinterpret_cast<uint4 *>(hps)[c] = reinterpret_cast<const uint4 *>(a.hp)[c];
+  if ((int)threadIdx.x < a.P) {
+    s_tok[threadIdx.x] = a.sorted_token[threadIdx.x];
+    s_pw[threadIdx.x] = a.pair_w[threadIdx.x];
+  }
+  for (int i = lane; i < kDecodeMaxT * 16; i += 64) (&yacc[wave][0][0])[i] = 0.f;
+  if (blockIdx.x == 0 && (int)threadIdx.x < a.T) a.bnd[threadIdx.x] = 0;
+  __syncthreads();
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
+  const int plane = a.P * a.slots * 2;
+  for (int tile = wave; tile < nt; tile += kDcWaves) {
+    const int4 td = tile == wave ? td0 : reinterpret_cast<const int4 *>(a.tiles)[tile];
+    const int e = td.x, start = td.y, cnt = td.z;
+    const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)rt * tbytes;
+    uint2 dd[F];
+#pragma unroll
+    for (int s = 0; s < F; ++s) dd[s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
+    uint32_t ddw = 0, dsh = 0;
+    if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw, dsh);
+    const float4 sd = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + rt * 16 + 4 * g);
+    const bool live = n < cnt;
+    const int p = start + (live ? n : cnt - 1);
+    const char *hb = hps + p * a.slots * 2 + g * 16 * M;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < F; ++s) {
+      uint32_t pw[20];
+      unpack8(dd[s], pw);
+#pragma unroll
+      for (int m = 0; m < 5; ++m)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(hb + q * plane + 16 * (5 * s + m)), acc);
+    }
+    if constexpr (RT > 0) {
+      uint32_t pw[16];
+      unpack_tail<RT>(ddw, dsh, pw);
+#pragma unroll
+      for (int m = 0; m < tail_mfmas(RT); ++m)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(hb + q * plane + 16 * (5 * F + m)), acc);
+    }
+    if (live) {
+      const int tok = s_tok[p];
+      const float wt = s_pw[p];
+      const float sdv[4] = {sd.x, sd.y, sd.z, sd.w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        yacc[wave][tok][4 * g + v] = fmaf(wt, (acc[v] * 0.5f) * sdv[v], yacc[wave][tok][4 * g + v]);
+    }
+  }
+  __syncthreads();
+  const int i = threadIdx.x;
+  if (i < a.T * 16) {
+    const int t = i >> 4, r = i & 15;
+    float y = yacc[0][t][r];
+#pragma unroll
+    for (int w = 1; w < kDcWaves; ++w) y += yacc[w][t][r];
+    const int64_t o = (int64_t)t * a.H + rt * 16 + r;
+    if (a.Y) a.Y[o] = y;
+    if (a.resid_out) a.resid_out[o] = f32_to_bf16_rne(__uint_as_float((uint32_t)a.resid_in[o] << 16) + y);
+  }
+}
+
+// Clears the per-token bound slots (decode path with the separate combine).
+__global__ void clear_bounds_kernel(uint64_t *bnd, int T) {
+  if ((int)threadIdx.x < T) bnd[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------- ternary linear
@@ -559,12 +800,12 @@ size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   o = align_up(o + ffn_max_tiles(P, E) * 16, 256);
   o = align_up(o + 16, 256);
   o = align_up(o + (size_t)3 * P * gi.slots * 2, 256);
+  o = align_up(o + (size_t)P * 4, 256);
   return o;
 }
 
 FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   (void)H;
-  (void)I;
   const int64_t P = T * k;
   char *b = (char *)ws;
   FfnWs f;
@@ -574,37 +815,27 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   f.ntiles = (int32_t *)(b + o);
   o = align_up(o + 16, 256);
   f.hp = (uint16_t *)(b + o);
+  o = align_up(o + (size_t)3 * P * make_geom(I).slots * 2, 256);
+  f.pw = (float *)(b + o);
   return f;
 }
 
-template <int F, int RT, int KS>
+template <int F, int RT, int KS, int RNPL>
 static int run_gateup(hipStream_t st, const GateUpArgs &a, int64_t max_tiles, int I) {
   const int rs = lds_row_bytes(a.gx.slots);
   size_t lds = (size_t)17 * rs + (KS > 1 ? 4 * 64 * 8 * 4 : 0);
   dim3 grid((unsigned)max_tiles, (unsigned)(I / 16 / (4 / KS)));
-  int rc = allow_lds<gateup_kernel<F, RT, KS>>(lds);
+  int rc = allow_lds<gateup_kernel<F, RT, KS, RNPL>>(lds);
   if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS>), grid, dim3(256), lds, st, a);
+  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS, RNPL>), grid, dim3(256), lds, st, a);
   TMOE_LAUNCHED("gateup");
   return TMOE_OK;
 }
 
-int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
-               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool prepared) {
-  const int64_t E = W->n_experts, H = W->hidden, I = W->inter, P = T * W->top_k;
-  const Geom gh = make_geom(H), gi = make_geom(I);
-  if (!(gh.F == 13 && gh.r == 0 && gi.F == 3 && gi.r == 2 && H % 64 == 0 && I % 64 == 0))
-    return fail(TMOE_E_UNSUPPORTED, "expert kernels are built for hidden 2048 and moe_intermediate 512");
-  const int64_t max_tiles = ffn_max_tiles(P, E);
-  if (max_tiles > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too many tokens");
-
-  if (!prepared) {
-    TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
-                fw.ntiles);
-    TMOE_LAUNCHED("make_tiles");
-  }
-
-  GateUpArgs ga;
+static GateUpArgs gateup_args(const tmoe_moe_weights *W, const uint16_t *X, int64_t P, float clamp, float *Hout,
+                              const FfnWs &fw, const int32_t *sorted_token) {
+  const Geom gh = make_geom(W->hidden), gi = make_geom(W->inter);
+  GateUpArgs ga{};
   ga.gate_p = W->gate_p;
   ga.up_p = W->up_p;
   ga.stride_gu = W->stride_gu;
@@ -619,11 +850,22 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   ga.hp_plane = P * gi.slots;
   ga.gx = gh;
   ga.gd = gi;
-  ga.I = (int)I;
+  ga.I = (int)W->inter;
   ga.clamp = clamp;
-  int rc = P <= 64 ? run_gateup<13, 0, 4>(st, ga, max_tiles, (int)I) : run_gateup<13, 0, 1>(st, ga, max_tiles, (int)I);
-  if (rc) return rc;
+  return ga;
+}
 
+static int check_ffn_shapes(const tmoe_moe_weights *W) {
+  const int64_t H = W->hidden, I = W->inter;
+  const Geom gh = make_geom(H), gi = make_geom(I);
+  if (!(gh.F == 13 && gh.r == 0 && gi.F == 3 && gi.r == 2 && H % 64 == 0 && I % 64 == 0))
+    return fail(TMOE_E_UNSUPPORTED, "expert kernels are built for hidden 2048 and moe_intermediate 512");
+  return TMOE_OK;
+}
+
+static int run_down(hipStream_t st, const tmoe_moe_weights *W, const FfnWs &fw, int64_t P, int64_t max_tiles,
+                    float *O) {
+  const Geom gi = make_geom(W->inter);
   DownArgs da;
   da.down_p = W->down_p;
   da.stride_d = W->stride_d;
@@ -633,15 +875,95 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   da.tiles = fw.tiles;
   da.ntiles = fw.ntiles;
   da.O = O;
-  da.H = (int)H;
+  da.H = (int)W->hidden;
   da.slots = gi.slots;
   const size_t lds = (size_t)3 * 17 * lds_row_bytes(gi.slots);
-  rc = allow_lds<down_kernel<3, 2>>(lds);
+  int rc = allow_lds<down_kernel<3, 2>>(lds);
   if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_kernel<3, 2>), dim3((unsigned)max_tiles, (unsigned)(H / 64)), dim3(256), lds, st,
-              da);
+  TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_kernel<3, 2>), dim3((unsigned)max_tiles, (unsigned)(W->hidden / 64)), dim3(256),
+              lds, st, da);
   TMOE_LAUNCHED("down");
   return TMOE_OK;
+}
+
+int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float clamp,
+                       const DecodeRoute &r, const FfnWs &fw, float *O, float *Y, const uint16_t *resid_in,
+                       uint16_t *resid_out) {
+  int rc = check_ffn_shapes(W);
+  if (rc) return rc;
+  const int64_t E = W->n_experts, H = W->hidden, I = W->inter;
+  const int k = W->top_k;
+  const int64_t P = T * k;
+  if (T < 1 || T > kDecodeMaxT || k > 16 || E > 1024) return fail(TMOE_E_UNSUPPORTED, "decode path limits");
+  const Geom gi = make_geom(I);
+  GateUpArgs ga = gateup_args(W, X, P, clamp, nullptr, fw, r.sorted_token);
+  ga.r = r;
+  ga.r.tiles = fw.tiles;
+  ga.r.ntiles = fw.ntiles;
+  ga.r.pair_w = fw.pw;
+  ga.T = (int)T;
+  ga.E = (int)E;
+  ga.k = k;
+  const int64_t nx = P < E ? P : E;  // hit experts <= min(T k, E), one tile each
+  if (E <= 256)
+    rc = P <= 64 ? run_gateup<13, 0, 4, 4>(st, ga, nx, (int)I) : run_gateup<13, 0, 1, 4>(st, ga, nx, (int)I);
+  else
+    rc = P <= 64 ? run_gateup<13, 0, 4, 16>(st, ga, nx, (int)I) : run_gateup<13, 0, 1, 16>(st, ga, nx, (int)I);
+  if (rc) return rc;
+
+  if (P <= kDcMaxPairs) {
+    DownCombineArgs da;
+    da.down_p = W->down_p;
+    da.stride_d = W->stride_d;
+    da.down_s = W->down_s;
+    da.hp = fw.hp;
+    da.slots = gi.slots;
+    da.tiles = fw.tiles;
+    da.ntiles = fw.ntiles;
+    da.sorted_token = r.sorted_token;
+    da.pair_w = fw.pw;
+    da.P = (int)P;
+    da.max_tiles = (int)nx;
+    da.T = (int)T;
+    da.H = (int)H;
+    da.Y = Y;
+    da.resid_in = resid_in;
+    da.resid_out = resid_out;
+    da.bnd = r.bnd;
+    const size_t lds = (size_t)3 * P * gi.slots * 2;
+    rc = allow_lds<down_combine_kernel<3, 2>>(lds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_combine_kernel<3, 2>), dim3((unsigned)(H / 16)), dim3(64 * kDcWaves), lds,
+                st, da);
+    TMOE_LAUNCHED("down_combine");
+    return TMOE_OK;
+  }
+  // more pairs: down over (tile, 64-row block) into O, then the combine
+  rc = run_down(st, W, fw, P, nx, O);
+  if (rc) return rc;
+  hipLaunchKernelGGL(clear_bounds_kernel, dim3(1), dim3(64), 0, st, r.bnd, (int)T);
+  TMOE_LAUNCHED("clear_bounds");
+  return launch_combine(st, O, r.w, r.pos, T, k, H, Y, resid_in, resid_out);
+}
+
+int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
+               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw) {
+  int rc = check_ffn_shapes(W);
+  if (rc) return rc;
+  const int64_t E = W->n_experts, H = W->hidden, I = W->inter, P = T * W->top_k;
+  const Geom gi = make_geom(I);
+  const int64_t max_tiles = ffn_max_tiles(P, E);
+  if (max_tiles > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too many tokens");
+
+  TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
+              fw.ntiles);
+  TMOE_LAUNCHED("make_tiles");
+
+  GateUpArgs ga = gateup_args(W, X, P, clamp, Hout, fw, sorted_token);
+  rc = P <= 64 ? run_gateup<13, 0, 4, 0>(st, ga, max_tiles, (int)I) : run_gateup<13, 0, 1, 0>(st, ga, max_tiles, (int)I);
+  if (rc) return rc;
+
+  return run_down(st, W, fw, P, max_tiles, O);
 }
 
 size_t linear_ws_bytes(int64_t T, int64_t K) {

@@ -327,7 +327,7 @@ int tmoe_expert_ffn(void *stream, const tmoe_moe_weights *W, const uint16_t *X, 
   size_t need = ffn_ws_bytes(T, W->top_k, W->n_experts, W->hidden, W->inter);
   REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes", need);
   return launch_ffn((hipStream_t)stream, W, X, T, offsets, sorted_token, clamp, O, Hout,
-                    ffn_ws_carve(ws, T, W->top_k, W->n_experts, W->hidden, W->inter), false);
+                    ffn_ws_carve(ws, T, W->top_k, W->n_experts, W->hidden, W->inter));
 }
 
 // ------------------------------------------------------------------ combine
@@ -373,7 +373,8 @@ static LayerWs layer_ws(int64_t T, const tmoe_moe_weights *W) {
   L.off_offsets = take((E + 1) * 4);
   L.off_st = take(P * 4);
   L.off_ss = take(P * 4);
-  L.off_O = take((size_t)P * H * 4);
+  // expert outputs; the decode path with few pairs fuses the combine and needs none
+  L.off_O = take(T <= kDecodeMaxT && P <= kDcMaxPairs ? 0 : (size_t)P * H * 4);
   L.total = o;
   return L;
 }
@@ -422,19 +423,19 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   const RouterWs rw = router_ws_carve(base + L.off_router, T, E);
   const FfnWs fw = ffn_ws_carve(base + L.off_ffn, T, k, E, H, W->inter);
   if (T <= kDecodeMaxT) {
-    // one kernel: logits, certified top-k, grouping, work tiles, permuted activations
-    rc = launch_router_decode(st, X, T, H, W->router_w, W->router_bias, E, k, rw, idx, wt, o.n_fixup, counts,
-                              offsets, st_tok, st_slot, pos, fw.tiles, fw.ntiles);
+    // logits; gate/up with the certified top-k and grouping in its prologue; down + combine
+    int depth = 0;
+    rc = launch_router_logits(st, X, T, H, W->router_w, W->router_bias, E, rw, &depth);
     if (rc) return rc;
-    rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw, true);
-  } else {
-    rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup, rw);
-    if (rc) return rc;
-    rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos,
-                      group_ws_carve(base + L.off_group, T, k, E));
-    if (rc) return rc;
-    rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw, false);
+    const DecodeRoute r{rw.lg, rw.bnd, depth, W->router_w, W->router_bias, idx, o.n_fixup, st_tok, st_slot, pos,
+                        wt, nullptr, nullptr, nullptr};
+    return launch_decode_tail(st, W, X, T, o.clamp, r, fw, O, Y, o.resid_out ? X : nullptr, o.resid_out);
   }
+  rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup, rw);
+  if (rc) return rc;
+  rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos, group_ws_carve(base + L.off_group, T, k, E));
+  if (rc) return rc;
+  rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw);
   if (rc) return rc;
   return launch_combine(st, O, wt, pos, T, k, H, Y, o.resid_out ? X : nullptr, o.resid_out);
 }

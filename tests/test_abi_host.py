@@ -134,7 +134,9 @@ def test_layer_struct_validation_without_gpu():
         setattr(s, name, 256)
     s.stride_gu, s.stride_d = tm.tiled_bytes(512, 2048), tm.tiled_bytes(2048, 512)
     assert lib.tmoe_moe_workspace_bytes(4, ctypes.byref(s), ctypes.byref(out)) == 0
-    assert out.value > 4 * 8 * 2048 * 4
+    assert out.value > 3 * 4 * 8 * 544 * 2  # the three bf16 parts of h per (token, slot) pair
+    assert lib.tmoe_moe_workspace_bytes(64, ctypes.byref(s), ctypes.byref(out)) == 0
+    assert out.value > 64 * 8 * 2048 * 4  # batched path: expert outputs before the combine
     s.stride_gu -= 16
     assert lib.tmoe_moe_workspace_bytes(4, ctypes.byref(s), ctypes.byref(out)) == Ew.TMOE_E_SHAPE
     s.stride_gu += 16
