@@ -40,7 +40,7 @@ WORKLOADS = {
 
 # kernels each path launches (names of the C ABI's timing hook)
 DECODE_KERNELS = ("router_logits", "gateup", "down", "combine")
-BATCH_KERNELS = ("router_logits", "router_topk", "router_fixup", "group", "make_tiles", "gateup", "down", "combine")
+BATCH_KERNELS = ("router_logits", "router_topk", "group", "gateup", "down", "combine")
 
 
 def roofline(name, ms, n_hit, T, cfg, bias):

@@ -270,13 +270,12 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
  * dispatch. Global state: not thread-safe; one
  * profiling window at a time (TMOE_E_ARG otherwise). */
 enum {
-  TMOE_KERNEL_ROUTER_LOGITS = 1, /* for T <= 16: the fused decode router (logits, top-k, grouping) */
-  TMOE_KERNEL_ROUTER_TOPK = 2,
-  TMOE_KERNEL_ROUTER_FIXUP = 3,
-  TMOE_KERNEL_GROUP = 4, /* the fused grouping kernel (first kernel when T > 256) */
-  TMOE_KERNEL_MAKE_TILES = 5,
-  TMOE_KERNEL_GATEUP = 7,
-  TMOE_KERNEL_DOWN = 9,
+  TMOE_KERNEL_ROUTER_LOGITS = 1, /* fp64 logits (VALU for T <= 16, matrix cores above) */
+  TMOE_KERNEL_ROUTER_TOPK = 2,   /* certified top-k (with its rare double-double recompute) */
+  TMOE_KERNEL_GROUP = 4,         /* the fused grouping kernel (first kernel when T > 256) */
+  TMOE_KERNEL_MAKE_TILES = 5,    /* tmoe_expert_ffn only (the layer's grouping writes the tiles) */
+  TMOE_KERNEL_GATEUP = 7,        /* for T <= 16 with the top-k and grouping in its prologue */
+  TMOE_KERNEL_DOWN = 9,          /* for T*k <= 32 with the combine fused */
   TMOE_KERNEL_COMBINE = 10,
   TMOE_KERNEL_LINEAR = 11
 };

@@ -80,8 +80,8 @@ SIGNATURES = {
     "tmoe_profile_end": (c_int, [c_void_p, c_int, POINTER(c_int)]),
 }
 
-KERNELS = {"router_logits": 1, "router_topk": 2, "router_fixup": 3, "group": 4, "make_tiles": 5, "gateup": 7,
-           "down": 9, "combine": 10, "linear": 11}
+KERNELS = {"router_logits": 1, "router_topk": 2, "group": 4, "make_tiles": 5, "gateup": 7, "down": 9, "combine": 10,
+           "linear": 11}
 
 
 def declare(lib) -> None:

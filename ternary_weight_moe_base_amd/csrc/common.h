@@ -151,18 +151,17 @@ int launch_repack_tiled(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, 
 int launch_unpack_tiled(hipStream_t st, const uint8_t *Pt, int64_t R, int64_t K, int8_t *T);
 
 struct RouterWs {
-  uint64_t *bnd;       // [T] bits of max_e (sum_i |x_i w_ei| + |b_e|) (fp64, >= 0); zero between calls
-  double *lg;          // [T][E] fp64 logits
-  int32_t *fix_count;  // [1]
-  int32_t *fix_list;   // [T]
+  uint64_t *bnd;  // [T] bits of an upper bound of max_e (sum_i |x_i w_ei| + |b_e|) (fp64 >= 0); zero between calls
+  double *lg;     // [T][E] fp64 logits
 };
 size_t router_ws_bytes(int64_t T, int64_t E);
 RouterWs router_ws_carve(void *ws, int64_t T, int64_t E);
-// Logits, certified top-k and double-double fix-up (three kernels).
+// Logits (fp64 VALU for T <= 16, fp64 matrix cores above) and the certified
+// top-k with its double-double fall-back (two kernels).
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                   int64_t E, int k, int32_t *idx, float *w, float *logits_out, int32_t *n_fixup, const RouterWs &rw);
-// Logits and per-token bounds only (the decode layer path certifies the top-k
-// in the gate/up kernel's prologue). Returns the accumulation depth in *depth.
+// Logits and per-token bounds only, T <= 16 (the decode layer path certifies
+// the top-k in the gate/up kernel's prologue). Returns the error-bound depth in *depth.
 int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                          int64_t E, const RouterWs &rw, int *depth);
 // Decode path (T <= kDecodeMaxT): every (token, slot) pair of an expert fits one work tile.
@@ -174,8 +173,10 @@ struct GroupWs {
 };
 size_t group_ws_bytes(int64_t T, int k, int64_t E);
 GroupWs group_ws_carve(void *ws, int64_t T, int k, int64_t E);
+// tiles / ntiles (may be null): also write the work tiles (<= 16 pairs of one expert each)
 int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
-                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw);
+                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw, int32_t *tiles,
+                 int32_t *ntiles);
 
 struct FfnWs {
   int32_t *tiles;    // [max_tiles][4]: expert, start, count, 0
@@ -187,9 +188,10 @@ struct FfnWs {
 int64_t ffn_max_tiles(int64_t pairs, int64_t E);
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I);
 FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I);
-// Grouped expert FFN (gate/up + SiLU/clamp, down) from grouping offsets.
+// Grouped expert FFN (gate/up + SiLU/clamp, down) from grouping offsets;
+// tiles_ready: fw.tiles / fw.ntiles were already written by the grouping.
 int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
-               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw);
+               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool tiles_ready);
 
 // Decode layer tail (T <= kDecodeMaxT): gate/up whose prologue certifies the
 // top-k of every token from the fp64 logits and groups the pairs (workgroup

@@ -6,11 +6,37 @@
 namespace tmoe {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+struct KeepChunk {
+  __device__ uint4 operator()(int, uint4 v) const { return v; }
+};
+
+// Copies n 16-byte chunks, chunk i from *src(i) to *dst(i) (through
+// fix(i, value)), by a workgroup of NT threads with up to 8 loads in flight per
+// thread: all loads of a batch are issued before its stores.
+template <int NT, typename Src, typename Dst, typename Fix = KeepChunk>
+__device__ inline void copy16(int n, Src src, Dst dst, Fix fix = Fix()) {
+  constexpr int B = 8;
+  for (int base = threadIdx.x; base < n; base += NT * B) {
+    uint4 v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * NT;
+      if (i < n) v[j] = src(i);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + j * NT;
+      if (i < n) *dst(i) = fix(i, v[j]);
+    }
+  }
+}
 
 // Exclusive prefix sum of cnt[0..n) in place by a workgroup of NT threads
 // (n <= 4 * NT); tmp holds NT ints. Returns the total to every thread.

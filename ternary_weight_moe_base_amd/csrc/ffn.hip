@@ -114,17 +114,8 @@ __host__ __device__ inline int lds_row_bytes(int slots) { return slots * 2 + 16;
 
 // ------------------------------------------------------------- staging
 // Operand row n of LDS <- input row `src` (16-bit values): position g*QS + j
-// holds src[5Qg + j] for j < 5Q and 5Qg + j < K, zero otherwise. `contig`:
-// QS == 5Q and K % 8 == 0 (then positions are the input indices and 16-byte
-// copies suffice).
-__device__ inline void stage_row(char *dst, const uint16_t *src, const Geom &g, bool contig, int tid, int nthreads) {
-  if (contig) {
-    const int vec = g.slots / 8, kv = (int)(g.K / 8);
-    for (int c = tid; c < vec; c += nthreads)
-      *reinterpret_cast<uint4 *>(dst + c * 16) =
-          c < kv ? reinterpret_cast<const uint4 *>(src)[c] : make_uint4(0, 0, 0, 0);
-    return;
-  }
+// holds src[5Qg + j] for j < 5Q and 5Qg + j < K, zero otherwise.
+__device__ inline void stage_row(char *dst, const uint16_t *src, const Geom &g, int tid, int nthreads) {
   for (int i = tid; i < g.slots; i += nthreads) {
     const int quarter = i / g.QS, j = i - quarter * g.QS;
     const int64_t k = operand_k(g, quarter, j);
@@ -134,6 +125,27 @@ __device__ inline void stage_row(char *dst, const uint16_t *src, const Geom &g, 
 
 __device__ inline void zero_row(char *dst, int slots, int tid, int nthreads) {
   for (int c = tid; c < slots / 8; c += nthreads) *reinterpret_cast<uint4 *>(dst + c * 16) = make_uint4(0, 0, 0, 0);
+}
+
+// Positions of an operand row that hold no input (j >= 5Q in a quarter, or
+// input index >= K) must be zero where they meet activations: number of live
+// 16-bit values in 16-byte chunk c of a staged row, and the chunk with the
+// others cleared.
+template <int F, int RT>
+__device__ inline int live_in_chunk(int K, int c) {
+  constexpr int QS = 8 * (5 * F + (RT == 0 ? 0 : (5 * (RT / 2) + 3) / 4)), Q5 = 5 * (8 * F + RT);
+  const int pos = c * 8, quarter = pos / QS, j0 = pos - quarter * QS;
+  const int live = K - Q5 * quarter;
+  const int lq = live < 0 ? 0 : (live < Q5 ? live : Q5);
+  const int n = lq - j0;
+  return n < 0 ? 0 : (n > 8 ? 8 : n);
+}
+__device__ inline uint4 keep_live(uint4 v, int nlive) {
+  if (nlive >= 8) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] &= (2 * i + 1 < nlive) ? 0xFFFFFFFFu : (2 * i < nlive ? 0x0000FFFFu : 0u);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ---------------------------------------------------------------- tiles
@@ -163,7 +175,7 @@ struct GateUpArgs {
   const uint16_t *X;  // [T][H] bf16, natural order
   const int32_t *tiles, *ntiles, *sorted_token;
   float *h;            // [pairs][I] fp32 (grouped order) or null
-  uint16_t *hp;        // [3][pairs][gd.slots] bf16 parts of h in the down operand layout
+  uint16_t *hp;        // [3][pairs][gd.slots] bf16 parts of h in the down operand layout (pads not written)
   int64_t hp_plane;    // pairs * gd.slots
   Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
   int I;
@@ -210,11 +222,16 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   }
   // every token's activations into LDS row t, zero row 16
   const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
-  for (int i = threadIdx.x; i < T * vec; i += 256) {
-    const int t = i / vec, c = i - t * vec;
-    *reinterpret_cast<uint4 *>(smem + t * rs + c * 16) =
-        c < kv ? reinterpret_cast<const uint4 *>(a.X + (int64_t)t * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
-  }
+  copy16<256>(
+      T * vec,
+      [&](int i) {
+        const int t = i / vec, c = i - t * vec;
+        return c < kv ? reinterpret_cast<const uint4 *>(a.X + (int64_t)t * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
+      },
+      [&](int i) {
+        const int t = i / vec, c = i - t * vec;
+        return reinterpret_cast<uint4 *>(smem + t * rs + c * 16);
+      });
   zero_row(smem + 16 * rs, a.gx.slots, threadIdx.x, 256);
   if (threadIdx.x < 32) s.hit[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
@@ -282,11 +299,14 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
 // Workgroup = 4 wavefronts. KS wavefronts split the K steps of one 16-row tile
-// (partial sums reduced in LDS in fixed order); 4/KS row tiles per workgroup.
-// blockIdx.x = work tile (expert, <= 16 pairs), blockIdx.y = row-tile group.
+// (partial sums reduced in LDS in fixed order); with KS = 1 each wavefront
+// takes R row tiles and reads every activation slice from LDS once for all of
+// them (and for both matrices). blockIdx.x = work tile (expert, <= 16 pairs),
+// blockIdx.y = group of (4 / KS) * R row tiles.
 // RNPL > 0: decode path with the routing prologue (experts per lane of its top-k).
-template <int F, int RT, int KS, int RNPL>
+template <int F, int RT, int KS, int RNPL, int R>
 __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
+  static_assert(KS == 1 || R == 1, "row tiles per wavefront need the full K range");
   extern __shared__ __align__(16) char smem[];
   int e, start, cnt;
   const int32_t *toks;
@@ -312,93 +332,104 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
   constexpr int RTB = 4 / KS;
   constexpr int M = 5 * F + tail_mfmas(RT);
   constexpr int SMAX = (F + KS - 1) / KS;
-  const int rt = blockIdx.y * RTB + wave / KS;
+  const int rtb = blockIdx.y * RTB * R + wave / KS;  // row tiles rtb + RTB r
   const int kp = wave % KS;
   const int rs = lds_row_bytes(a.gx.slots);
   char *xs = smem;  // [17][rs]; row 16 = zeros
 
   // weights first: all loads of this wavefront are in flight while x is staged
   const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
-  const uint8_t *gt = a.gate_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
-  const uint8_t *ut = a.up_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
   const int s0 = kp * F / KS, s1 = (kp + 1) * F / KS;
-  uint2 gd[SMAX], ud[SMAX];
-#pragma unroll
-  for (int i = 0; i < SMAX; ++i) {
-    if (s0 + i < s1) {
-      gd[i] = *reinterpret_cast<const uint2 *>(gt + (int64_t)(s0 + i) * 512 + lane * 8);
-      ud[i] = *reinterpret_cast<const uint2 *>(ut + (int64_t)(s0 + i) * 512 + lane * 8);
-    }
-  }
-  // row scales of this lane's four output rows (epilogue), fetched with the weights
-  const int row0 = rt * 16 + 4 * (lane >> 4);
-  const float4 sg = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
-  const float4 su = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
-  uint32_t gdw = 0, gsh = 0, udw = 0, ush = 0;
   const bool tail_here = RT > 0 && kp == KS - 1;
-  if (tail_here) {
-    load_tail<RT>(gt, F, lane, gdw, gsh);
-    load_tail<RT>(ut, F, lane, udw, ush);
+  uint2 gd[R][SMAX], ud[R][SMAX];
+  uint32_t gdw[R], gsh[R], udw[R], ush[R];
+  float4 sg[R], su[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rt = rtb + RTB * r;
+    const uint8_t *gt = a.gate_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
+    const uint8_t *ut = a.up_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
+#pragma unroll
+    for (int i = 0; i < SMAX; ++i) {
+      if (s0 + i < s1) {
+        gd[r][i] = *reinterpret_cast<const uint2 *>(gt + (int64_t)(s0 + i) * 512 + lane * 8);
+        ud[r][i] = *reinterpret_cast<const uint2 *>(ut + (int64_t)(s0 + i) * 512 + lane * 8);
+      }
+    }
+    gdw[r] = gsh[r] = udw[r] = ush[r] = 0;
+    if (tail_here) {
+      load_tail<RT>(gt, F, lane, gdw[r], gsh[r]);
+      load_tail<RT>(ut, F, lane, udw[r], ush[r]);
+    }
+    // row scales of this lane's four output rows (epilogue), fetched with the weights
+    const int row0 = rt * 16 + 4 * (lane >> 4);
+    sg[r] = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
+    su[r] = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
   }
 
   if constexpr (RNPL == 0) {
     // activations of the tile's pairs (natural order = operand order for H = 2048)
-    const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
-    for (int i = threadIdx.x; i < cnt * vec; i += 256) {
-      const int n = i / vec, c = i - n * vec;
-      const int64_t tok = toks[n];
-      *reinterpret_cast<uint4 *>(xs + n * rs + c * 16) =
-          c < kv ? reinterpret_cast<const uint4 *>(a.X + tok * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
-    }
+    constexpr int vec = 4 * M;
+    const int kv = (int)(a.gx.K / 8);
+    copy16<256>(
+        cnt * vec,
+        [&](int i) {
+          const int n = i / vec, c = i - n * vec;
+          return c < kv ? reinterpret_cast<const uint4 *>(a.X + (int64_t)toks[n] * a.gx.K)[c]
+                        : make_uint4(0, 0, 0, 0);
+        },
+        [&](int i) {
+          const int n = i / vec, c = i - n * vec;
+          return reinterpret_cast<uint4 *>(xs + n * rs + c * 16);
+        });
     zero_row(xs + 16 * rs, a.gx.slots, threadIdx.x, 256);
-  }
-  // zero pad positions of this tile's rows of the down operand (written once per pair)
-  if (blockIdx.y == 0 && wave == 0) {
-    const int q5 = 5 * a.gd.Q;
-    for (int n = 0; n < cnt; ++n)
-      for (int g = 0; g < 4; ++g) {
-        // quarter g holds inputs 5Qg .. 5Qg + 5Q - 1 (those < K) at positions 0 ..
-        const int64_t live = a.gd.K - (int64_t)q5 * g;
-        const int lo = live < 0 ? 0 : (live < q5 ? (int)live : q5);
-        for (int j = lo + lane; j < a.gd.QS; j += 64) {
-          const int64_t o = (int64_t)(start + n) * a.gd.slots + g * a.gd.QS + j;
-          a.hp[o] = 0;
-          a.hp[a.hp_plane + o] = 0;
-          a.hp[2 * a.hp_plane + o] = 0;
-        }
-      }
   }
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
   const int brow = n < cnt ? (RNPL > 0 ? toks[n] : n) : 16;
   const char *bp = xs + brow * rs + g * M * 16;
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accg[R], accu[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    accg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int i = 0; i < SMAX; ++i) {
     const int s = s0 + i;
     if (s < s1) {
-      uint32_t pg[20], pu[20];
-      unpack8(gd[i], pg);
-      unpack8(ud[i], pu);
+      u32x4 bx[5];
 #pragma unroll
-      for (int m = 0; m < 5; ++m) {
-        u32x4 bx = lds16(bp + (5 * s + m) * 16);
-        accg = mfma_bf16(pg + 4 * m, bx, accg);
-        accu = mfma_bf16(pu + 4 * m, bx, accu);
+      for (int m = 0; m < 5; ++m) bx[m] = lds16(bp + (5 * s + m) * 16);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint32_t pg[20], pu[20];
+        unpack8(gd[r][i], pg);
+        unpack8(ud[r][i], pu);
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          accg[r] = mfma_bf16(pg + 4 * m, bx[m], accg[r]);
+          accu[r] = mfma_bf16(pu + 4 * m, bx[m], accu[r]);
+        }
       }
     }
   }
   if constexpr (RT > 0) {
     if (tail_here) {
-      uint32_t pg[16], pu[16];
-      unpack_tail<RT>(gdw, gsh, pg);
-      unpack_tail<RT>(udw, ush, pu);
+      u32x4 bx[tail_mfmas(RT)];
 #pragma unroll
-      for (int m = 0; m < tail_mfmas(RT); ++m) {
-        u32x4 bx = lds16(bp + (5 * F + m) * 16);
-        accg = mfma_bf16(pg + 4 * m, bx, accg);
-        accu = mfma_bf16(pu + 4 * m, bx, accu);
+      for (int m = 0; m < tail_mfmas(RT); ++m) bx[m] = lds16(bp + (5 * F + m) * 16);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint32_t pg[16], pu[16];
+        unpack_tail<RT>(gdw[r], gsh[r], pg);
+        unpack_tail<RT>(udw[r], ush[r], pu);
+#pragma unroll
+        for (int m = 0; m < tail_mfmas(RT); ++m) {
+          accg[r] = mfma_bf16(pg + 4 * m, bx[m], accg[r]);
+          accu[r] = mfma_bf16(pu + 4 * m, bx[m], accu[r]);
+        }
       }
     }
   }
@@ -407,49 +438,53 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     float *mine = red + (wave * 64 + lane) * 8;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      mine[v] = accg[v];
-      mine[4 + v] = accu[v];
+      mine[v] = accg[0][v];
+      mine[4 + v] = accu[0][v];
     }
     __syncthreads();
     if (kp != 0) return;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      accg[v] = 0.f;
-      accu[v] = 0.f;
+      accg[0][v] = 0.f;
+      accu[0][v] = 0.f;
     }
     for (int q = 0; q < KS; ++q) {
       const float *o = red + ((wave + q) * 64 + lane) * 8;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        accg[v] += o[v];
-        accu[v] += o[4 + v];
+        accg[0][v] += o[v];
+        accu[0][v] += o[4 + v];
       }
     }
   }
   if (n >= cnt) return;
-  const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
-  float hv[4];
   const float c = a.clamp;
   const int64_t p = start + n;
   const int q5 = 5 * a.gd.Q;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float gg = (accg[v] * 0.5f) * sgv[v];
-    const float uu = (accu[v] * 0.5f) * suv[v];
-    hv[v] = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
-    // h = hi + mid + lo exactly (each bf16 rounding keeps the next 8 bits)
-    const uint16_t b0 = f32_to_bf16_rne(hv[v]);
-    const float r1 = hv[v] - __uint_as_float((uint32_t)b0 << 16);
-    const uint16_t b1 = f32_to_bf16_rne(r1);
-    const float r2 = r1 - __uint_as_float((uint32_t)b1 << 16);
-    const uint16_t b2 = f32_to_bf16_rne(r2);
-    const int nn = row0 + v;  // intermediate index = down input index
-    const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
-    a.hp[o] = b0;
-    a.hp[a.hp_plane + o] = b1;
-    a.hp[2 * a.hp_plane + o] = b2;
+  for (int r = 0; r < R; ++r) {
+    const int row0 = (rtb + RTB * r) * 16 + 4 * g;
+    const float sgv[4] = {sg[r].x, sg[r].y, sg[r].z, sg[r].w}, suv[4] = {su[r].x, su[r].y, su[r].z, su[r].w};
+    float hv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float gg = (accg[r][v] * 0.5f) * sgv[v];
+      const float uu = (accu[r][v] * 0.5f) * suv[v];
+      hv[v] = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
+      // h = hi + mid + lo exactly (each bf16 rounding keeps the next 8 bits)
+      const uint16_t b0 = f32_to_bf16_rne(hv[v]);
+      const float r1 = hv[v] - __uint_as_float((uint32_t)b0 << 16);
+      const uint16_t b1 = f32_to_bf16_rne(r1);
+      const float r2 = r1 - __uint_as_float((uint32_t)b1 << 16);
+      const uint16_t b2 = f32_to_bf16_rne(r2);
+      const int nn = row0 + v;  // intermediate index = down input index
+      const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
+      a.hp[o] = b0;
+      a.hp[a.hp_plane + o] = b1;
+      a.hp[2 * a.hp_plane + o] = b2;
+    }
+    if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
   }
-  if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
 }
 
 // ----------------------------------------------------------------- down
@@ -462,11 +497,13 @@ struct DownArgs {
   const int32_t *tiles, *ntiles;
   float *O;  // [pairs][H]
   int H, slots;
+  Geom gd;  // operand geometry of the down projection (K = I)
 };
 
-// Workgroup = 4 wavefronts x one 16-row tile each (64 output rows); three
-// bf16 passes (hi, mid, lo parts of h) per operand slice.
-template <int F, int RT>
+// Workgroup = 4 wavefronts x R 16-row tiles each (64 R output rows); three
+// bf16 passes (hi, mid, lo parts of h) per operand slice, each slice read from
+// LDS once per wavefront for its R row tiles.
+template <int F, int RT, int R>
 __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tile = blockIdx.x;
@@ -475,61 +512,93 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
   const int e = td.x, start = td.y, cnt = td.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int M = 5 * F + tail_mfmas(RT);
-  const int rt = blockIdx.y * 4 + wave;
+  const int rtb = blockIdx.y * 4 * R + wave;  // row tiles rtb + 4 r
   const int rs = lds_row_bytes(a.slots);
   char *xb[3] = {smem, smem + 17 * rs, smem + 34 * rs};  // [3][17][rs]
+  const int g = lane >> 4;
 
   const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
-  const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)rt * tbytes;
-  uint2 dd[F];
+  uint2 dd[R][F];
+  uint32_t ddw[R], dsh[R];
+  float4 sd[R];
 #pragma unroll
-  for (int s = 0; s < F; ++s) dd[s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
-  uint32_t ddw = 0, dsh = 0;
-  if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw, dsh);
-
-  const int vpr = a.slots / 8;
-  for (int i = threadIdx.x; i < cnt * vpr; i += 256) {
-    const int n = i / vpr, c = i - n * vpr;
-    const int64_t p = start + n;
+  for (int r = 0; r < R; ++r) {
+    const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)(rtb + 4 * r) * tbytes;
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-      *reinterpret_cast<uint4 *>(xb[q] + n * rs + c * 16) =
-          reinterpret_cast<const uint4 *>(a.hp + q * a.hp_plane + p * a.slots)[c];
+    for (int s = 0; s < F; ++s) dd[r][s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
+    ddw[r] = dsh[r] = 0;
+    if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw[r], dsh[r]);
+    sd[r] = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + (rtb + 4 * r) * 16 + 4 * g);
   }
+
+  constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
+  copy16<256>(
+      3 * cnt * VPR,
+      [&](int i) {
+        const int row = i / VPR, c = i - row * VPR;
+        const int q = row >= 2 * cnt ? 2 : (row >= cnt ? 1 : 0), n = row - q * cnt;
+        return reinterpret_cast<const uint4 *>(a.hp + q * a.hp_plane + (int64_t)(start + n) * a.slots)[c];
+      },
+      [&](int i) {
+        const int row = i / VPR, c = i - row * VPR;
+        const int q = row >= 2 * cnt ? 2 : (row >= cnt ? 1 : 0), n = row - q * cnt;
+        return reinterpret_cast<uint4 *>(xb[q] + n * rs + c * 16);
+      },
+      [&](int i, uint4 v) { return keep_live(v, live_in_chunk<F, RT>(a.gd.K, i % VPR)); });
 #pragma unroll
   for (int q = 0; q < 3; ++q) zero_row(xb[q] + 16 * rs, a.slots, threadIdx.x, 256);
   __syncthreads();
 
-  const int n = lane & 15, g = lane >> 4;
+  const int n = lane & 15;
   const int boff = (n < cnt ? n : 16) * rs + g * M * 16;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < F; ++s) {
-    uint32_t pw[20];
-    unpack8(dd[s], pw);
+    u32x4 bx[5][3];
 #pragma unroll
     for (int m = 0; m < 5; ++m)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(xb[q] + boff + (5 * s + m) * 16), acc);
+      for (int q = 0; q < 3; ++q) bx[m][q] = lds16(xb[q] + boff + (5 * s + m) * 16);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t pw[20];
+      unpack8(dd[r][s], pw);
+#pragma unroll
+      for (int m = 0; m < 5; ++m)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) acc[r] = mfma_bf16(pw + 4 * m, bx[m][q], acc[r]);
+    }
   }
   if constexpr (RT > 0) {
-    uint32_t pw[16];
-    unpack_tail<RT>(ddw, dsh, pw);
+    u32x4 bx[tail_mfmas(RT)][3];
 #pragma unroll
     for (int m = 0; m < tail_mfmas(RT); ++m)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(xb[q] + boff + (5 * F + m) * 16), acc);
+      for (int q = 0; q < 3; ++q) bx[m][q] = lds16(xb[q] + boff + (5 * F + m) * 16);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t pw[16];
+      unpack_tail<RT>(ddw[r], dsh[r], pw);
+#pragma unroll
+      for (int m = 0; m < tail_mfmas(RT); ++m)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) acc[r] = mfma_bf16(pw + 4 * m, bx[m][q], acc[r]);
+    }
   }
   if (n >= cnt) return;
   const int64_t p = start + n;
-  const int row0 = rt * 16 + 4 * g;
-  const float4 sd = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + row0);
-  float4 o;  // the trits entered as 2t
-  o.x = (acc[0] * 0.5f) * sd.x;
-  o.y = (acc[1] * 0.5f) * sd.y;
-  o.z = (acc[2] * 0.5f) * sd.z;
-  o.w = (acc[3] * 0.5f) * sd.w;
-  *reinterpret_cast<float4 *>(a.O + p * a.H + row0) = o;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row0 = (rtb + 4 * r) * 16 + 4 * g;
+    float4 o;  // the trits entered as 2t
+    o.x = (acc[r][0] * 0.5f) * sd[r].x;
+    o.y = (acc[r][1] * 0.5f) * sd[r].y;
+    o.z = (acc[r][2] * 0.5f) * sd[r].z;
+    o.w = (acc[r][3] * 0.5f) * sd[r].w;
+    *reinterpret_cast<float4 *>(a.O + p * a.H + row0) = o;
+  }
 }
 
 // ------------------------------------------------- down + combine (decode)
@@ -542,6 +611,7 @@ struct DownCombineArgs {
   const int32_t *tiles, *ntiles, *sorted_token;
   const float *pair_w;  // [pairs] routing weight of each grouped pair
   int P, T, H, max_tiles;
+  Geom gd;  // operand geometry of the down projection (K = I)
   float *Y;                   // [T][H] or null
   const uint16_t *resid_in;   // [T][H] bf16 or null
   uint16_t *resid_out;        // [T][H] bf16 or null (may alias resid_in)
@@ -569,9 +639,12 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   const int nt = *a.ntiles;
   int4 td0 = make_int4(0, 0, 1, 0);
   if (wave < a.max_tiles) td0 = reinterpret_cast<const int4 *>(a.tiles)[wave];  // first tile, before nt is known
-  const int nchunk = 3 * a.P * a.slots / 8;
-  for (int c = threadIdx.x; c < nchunk; c += 64 * kDcWaves)
-    reinterpret_cast<uint4 *>(hps)[c] = reinterpret_cast<const uint4 *>(a.hp)[c];
+  constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
+  copy16<64 * kDcWaves>(
+      3 * a.P * VPR,
+      [&](int c) { return reinterpret_cast<const uint4 *>(a.hp)[c]; },
+      [&](int c) { return reinterpret_cast<uint4 *>(hps) + c; },
+      [&](int c, uint4 v) { return keep_live(v, live_in_chunk<F, RT>(a.gd.K, c % VPR)); });
   if ((int)threadIdx.x < a.P) {
     s_tok[threadIdx.x] = a.sorted_token[threadIdx.x];
     s_pw[threadIdx.x] = a.pair_w[threadIdx.x];
@@ -672,7 +745,21 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   const uint8_t *wt = a.pt + (int64_t)(active ? rt : 0) * tbytes;
   char *xs = smem;
 
-  for (int n = 0; n < cnt; ++n) stage_row(xs + n * rs, a.X + (t0 + n) * a.ldx, a.g, a.contig, threadIdx.x, 256);
+  if (a.contig) {
+    const int vec = a.g.slots / 8, kv = (int)(a.g.K / 8);
+    copy16<256>(
+        cnt * vec,
+        [&](int i) {
+          const int n = i / vec, c = i - n * vec;
+          return c < kv ? reinterpret_cast<const uint4 *>(a.X + (t0 + n) * a.ldx)[c] : make_uint4(0, 0, 0, 0);
+        },
+        [&](int i) {
+          const int n = i / vec, c = i - n * vec;
+          return reinterpret_cast<uint4 *>(xs + n * rs + c * 16);
+        });
+  } else {
+    for (int n = 0; n < cnt; ++n) stage_row(xs + n * rs, a.X + (t0 + n) * a.ldx, a.g, threadIdx.x, 256);
+  }
   zero_row(xs + 16 * rs, a.g.slots, threadIdx.x, 256);
   __syncthreads();
 
@@ -820,14 +907,14 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   return f;
 }
 
-template <int F, int RT, int KS, int RNPL>
+template <int F, int RT, int KS, int RNPL, int R = 1>
 static int run_gateup(hipStream_t st, const GateUpArgs &a, int64_t max_tiles, int I) {
   const int rs = lds_row_bytes(a.gx.slots);
   size_t lds = (size_t)17 * rs + (KS > 1 ? 4 * 64 * 8 * 4 : 0);
-  dim3 grid((unsigned)max_tiles, (unsigned)(I / 16 / (4 / KS)));
-  int rc = allow_lds<gateup_kernel<F, RT, KS, RNPL>>(lds);
+  dim3 grid((unsigned)max_tiles, (unsigned)(I / 16 / (4 / KS) / R));
+  int rc = allow_lds<gateup_kernel<F, RT, KS, RNPL, R>>(lds);
   if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS, RNPL>), grid, dim3(256), lds, st, a);
+  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS, RNPL, R>), grid, dim3(256), lds, st, a);
   TMOE_LAUNCHED("gateup");
   return TMOE_OK;
 }
@@ -863,6 +950,17 @@ static int check_ffn_shapes(const tmoe_moe_weights *W) {
   return TMOE_OK;
 }
 
+template <int R>
+static int run_down_r(hipStream_t st, const DownArgs &da, int64_t max_tiles, int64_t H) {
+  const size_t lds = (size_t)3 * 17 * lds_row_bytes(da.slots);
+  int rc = allow_lds<down_kernel<3, 2, R>>(lds);
+  if (rc) return rc;
+  TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_kernel<3, 2, R>), dim3((unsigned)max_tiles, (unsigned)(H / 64 / R)), dim3(256),
+              lds, st, da);
+  TMOE_LAUNCHED("down");
+  return TMOE_OK;
+}
+
 static int run_down(hipStream_t st, const tmoe_moe_weights *W, const FfnWs &fw, int64_t P, int64_t max_tiles,
                     float *O) {
   const Geom gi = make_geom(W->inter);
@@ -877,13 +975,9 @@ static int run_down(hipStream_t st, const tmoe_moe_weights *W, const FfnWs &fw, 
   da.O = O;
   da.H = (int)W->hidden;
   da.slots = gi.slots;
-  const size_t lds = (size_t)3 * 17 * lds_row_bytes(gi.slots);
-  int rc = allow_lds<down_kernel<3, 2>>(lds);
-  if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_kernel<3, 2>), dim3((unsigned)max_tiles, (unsigned)(W->hidden / 64)), dim3(256),
-              lds, st, da);
-  TMOE_LAUNCHED("down");
-  return TMOE_OK;
+  da.gd = gi;
+  if (P < 1024) return run_down_r<2>(st, da, max_tiles, W->hidden);
+  return run_down_r<4>(st, da, max_tiles, W->hidden);
 }
 
 int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float clamp,
@@ -924,6 +1018,7 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
     da.pair_w = fw.pw;
     da.P = (int)P;
     da.max_tiles = (int)nx;
+    da.gd = gi;
     da.T = (int)T;
     da.H = (int)H;
     da.Y = Y;
@@ -947,7 +1042,7 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
 }
 
 int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
-               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw) {
+               const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool tiles_ready) {
   int rc = check_ffn_shapes(W);
   if (rc) return rc;
   const int64_t E = W->n_experts, H = W->hidden, I = W->inter, P = T * W->top_k;
@@ -955,12 +1050,19 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   const int64_t max_tiles = ffn_max_tiles(P, E);
   if (max_tiles > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too many tokens");
 
-  TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
-              fw.ntiles);
-  TMOE_LAUNCHED("make_tiles");
+  if (!tiles_ready) {
+    TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
+                fw.ntiles);
+    TMOE_LAUNCHED("make_tiles");
+  }
 
   GateUpArgs ga = gateup_args(W, X, P, clamp, Hout, fw, sorted_token);
-  rc = P <= 64 ? run_gateup<13, 0, 4, 0>(st, ga, max_tiles, (int)I) : run_gateup<13, 0, 1, 0>(st, ga, max_tiles, (int)I);
+  if (P <= 64)
+    rc = run_gateup<13, 0, 4, 0>(st, ga, max_tiles, (int)I);
+  else if (P < 1024)
+    rc = run_gateup<13, 0, 1, 0, 1>(st, ga, max_tiles, (int)I);
+  else
+    rc = run_gateup<13, 0, 1, 0, 2>(st, ga, max_tiles, (int)I);
   if (rc) return rc;
 
   return run_down(st, W, fw, P, max_tiles, O);

@@ -75,18 +75,32 @@ __device__ inline void scatter_block(const uint32_t *bits, const int *base, cons
   }
 }
 
+// Work tiles of up to 16 grouped pairs of one expert, in expert order, from
+// the per-expert counts c[] and offsets off[] (tc[], tmp[]: LDS scratch).
+__device__ inline void write_tiles(const int *c, const int *off, int E, int *tc, int *tmp, int32_t *tiles,
+                                   int32_t *ntiles) {
+  for (int e = threadIdx.x; e < E; e += kBlockTok) tc[e] = (c[e] + 15) / 16;
+  __syncthreads();
+  const int total = block_exclusive_scan<kBlockTok>(tc, E, tmp);
+  for (int e = threadIdx.x; e < E; e += kBlockTok)
+    for (int i = 0; 16 * i < c[e]; ++i)
+      reinterpret_cast<int4 *>(tiles)[tc[e] + i] = make_int4(e, off[e] + 16 * i, min(16, c[e] - 16 * i), 0);
+  if (threadIdx.x == 0) *ntiles = total;
+}
+
 // Whole grouping in one workgroup (T <= 256).
 __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *idx, int64_t T, int k, int E,
                                                                 int32_t *counts, int32_t *offsets,
                                                                 int32_t *sorted_token, int32_t *sorted_slot,
-                                                                int32_t *pos) {
+                                                                int32_t *pos, int32_t *tiles, int32_t *ntiles) {
   __shared__ uint32_t bits[1024 * 8];
-  __shared__ int cnt[1024];
+  __shared__ int cnt[1024], c0[1024], tc[1024];
   __shared__ int tmp[kBlockTok];
   build_bitmask(bits, idx, T, k, E, 0);
   for (int e = threadIdx.x; e < E; e += kBlockTok) {
     int c = block_count(bits, e);
     cnt[e] = c;
+    c0[e] = c;
     counts[e] = c;
   }
   __syncthreads();
@@ -94,6 +108,7 @@ __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *i
   for (int e = threadIdx.x; e < E; e += kBlockTok) offsets[e] = cnt[e];
   if (threadIdx.x == 0) offsets[E] = total;
   scatter_block(bits, cnt, idx, T, k, E, 0, sorted_token, sorted_slot, pos);
+  if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles);
 }
 
 __global__ __launch_bounds__(kBlockTok) void group_count_kernel(const int32_t *idx, int64_t T, int k, int E,
@@ -104,8 +119,9 @@ __global__ __launch_bounds__(kBlockTok) void group_count_kernel(const int32_t *i
 }
 
 __global__ __launch_bounds__(kBlockTok) void group_scan_kernel(const int32_t *bcount, int nb, int E, int32_t *bbase,
-                                                               int32_t *counts, int32_t *offsets) {
-  __shared__ int cnt[1024];
+                                                               int32_t *counts, int32_t *offsets, int32_t *tiles,
+                                                               int32_t *ntiles) {
+  __shared__ int cnt[1024], c0[1024], tc[1024];
   __shared__ int tmp[kBlockTok];
   for (int e = threadIdx.x; e < E; e += kBlockTok) {
     int run = 0;
@@ -114,12 +130,14 @@ __global__ __launch_bounds__(kBlockTok) void group_scan_kernel(const int32_t *bc
       run += bcount[(int64_t)b * E + e];
     }
     cnt[e] = run;
+    c0[e] = run;
     counts[e] = run;
   }
   __syncthreads();
   int total = block_exclusive_scan<kBlockTok>(cnt, E, tmp);
   for (int e = threadIdx.x; e < E; e += kBlockTok) offsets[e] = cnt[e];
   if (threadIdx.x == 0) offsets[E] = total;
+  if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles);
 }
 
 __global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t *idx, int64_t T, int k, int E,
@@ -134,11 +152,12 @@ __global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t 
 }
 
 int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
-                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw) {
+                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw, int32_t *tiles,
+                 int32_t *ntiles) {
   const int64_t nb = cdiv(T, kBlockTok);
   if (nb <= 1) {
-    TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_fused_kernel, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts, offsets,
-                       sorted_token, sorted_slot, pos);
+    TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_fused_kernel, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts,
+                offsets, sorted_token, sorted_slot, pos, tiles, ntiles);
     TMOE_LAUNCHED("group_fused");
     return TMOE_OK;
   }
@@ -146,7 +165,7 @@ int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E
   TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_count_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, gw.bcount);
   TMOE_LAUNCHED("group_count");
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kBlockTok), 0, st, gw.bcount, (int)nb, (int)E, gw.bbase, counts,
-                     offsets);
+                     offsets, tiles, ntiles);
   TMOE_LAUNCHED("group_scan");
   hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, offsets,
                      gw.bbase, sorted_token, sorted_slot, pos);

@@ -287,7 +287,7 @@ int tmoe_group_by_expert(void *stream, const int32_t *idx, int64_t T, int k, int
   REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), TMOE_E_WORKSPACE, "workspace needs %zu bytes",
           need);
   return launch_group((hipStream_t)stream, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos,
-                      group_ws_carve(ws, T, k, E));
+                      group_ws_carve(ws, T, k, E), nullptr, nullptr);
 }
 
 // --------------------------------------------------------------- expert FFN
@@ -327,7 +327,7 @@ int tmoe_expert_ffn(void *stream, const tmoe_moe_weights *W, const uint16_t *X, 
   size_t need = ffn_ws_bytes(T, W->top_k, W->n_experts, W->hidden, W->inter);
   REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes", need);
   return launch_ffn((hipStream_t)stream, W, X, T, offsets, sorted_token, clamp, O, Hout,
-                    ffn_ws_carve(ws, T, W->top_k, W->n_experts, W->hidden, W->inter));
+                    ffn_ws_carve(ws, T, W->top_k, W->n_experts, W->hidden, W->inter), false);
 }
 
 // ------------------------------------------------------------------ combine
@@ -433,9 +433,10 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   }
   rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup, rw);
   if (rc) return rc;
-  rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos, group_ws_carve(base + L.off_group, T, k, E));
+  rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos, group_ws_carve(base + L.off_group, T, k, E),
+                    fw.tiles, fw.ntiles);
   if (rc) return rc;
-  rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw);
+  rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw, true);
   if (rc) return rc;
   return launch_combine(st, O, wt, pos, T, k, H, Y, o.resid_out ? X : nullptr, o.resid_out);
 }

@@ -24,8 +24,6 @@ size_t router_ws_bytes(int64_t T, int64_t E) {
   size_t o = 0;
   o = align_up(o + T * 8, 256);      // bnd
   o = align_up(o + T * E * 8, 256);  // lg
-  o = align_up(o + 4, 256);          // fix_count
-  o = align_up(o + T * 4, 256);      // fix_list
   return o;
 }
 
@@ -36,10 +34,6 @@ RouterWs router_ws_carve(void *ws, int64_t T, int64_t E) {
   r.bnd = (uint64_t *)(b + o);
   o = align_up(o + T * 8, 256);
   r.lg = (double *)(b + o);
-  o = align_up(o + T * E * 8, 256);
-  r.fix_count = (int32_t *)(b + o);
-  o = align_up(o + 4, 256);
-  r.fix_list = (int32_t *)(b + o);
   return r;
 }
 
@@ -101,24 +95,22 @@ __device__ inline void logits_rows(const uint16_t *xs, int nt, const float *Wr, 
 
 __device__ inline void stage_x(uint16_t *xs, const uint16_t *X, int64_t t0, int nt, int H) {
   const int vpr = H / 8;
-  for (int i = threadIdx.x; i < nt * vpr; i += blockDim.x) {
-    int n = i / vpr, c = i % vpr;
-    reinterpret_cast<uint4 *>(xs + (size_t)n * H)[c] = reinterpret_cast<const uint4 *>(X + (t0 + n) * H)[c];
-  }
+  copy16<256>(
+      nt * vpr, [&](int i) { return reinterpret_cast<const uint4 *>(X + t0 * H)[i]; },
+      [&](int i) { return reinterpret_cast<uint4 *>(xs) + i; });
 }
-
 
 // Workgroup = 4 wavefronts = 4 experts; grid.y walks token chunks.
 template <int NC>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *X, int64_t T, const float *Wr,
                                                             const float *bias, int64_t E, int tchunk, double *lg,
-                                                            uint64_t *bnd, int32_t *fix_count) {
+                                                            uint64_t *bnd, int32_t *n_fixup) {
   extern __shared__ __align__(16) uint16_t xs[];
   __shared__ double lgs[4 * 128], abs_s[4 * 128];
   const int64_t e0 = (int64_t)blockIdx.x * 4;
   const int64_t t0 = (int64_t)blockIdx.y * tchunk;
   const int nt = (int)min<int64_t>(tchunk, T - t0);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *fix_count = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && n_fixup) *n_fixup = 0;
   stage_x(xs, X, t0, nt, NC * 256);
   __syncthreads();
   logits_rows<NC>(xs, nt, Wr, bias, e0 + (threadIdx.x >> 6), (int)E, lgs, abs_s);
@@ -133,33 +125,112 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *X, i
   }
 }
 
-// One wavefront per token; resets the token's bound slot for the next call.
+// ------------------------------------------------- fp64 matrix-core logits
+// Batched logits: workgroup = 16 tokens x 16 experts, wavefront w accumulates
+// the input range [w H/4, (w+1) H/4) on the fp64 matrix core (16x16x4: lane l
+// supplies token / expert l mod 16 at input kb(l / 16) + step, each lane group
+// owning a contiguous run of H/16 inputs). Every product bf16 x fp32 is exact
+// in fp64; the four partial sums are added in fixed order (+ bias). The error
+// bound uses Cauchy-Schwarz, sum_i |x_i w_ei| <= |x|_2 |w_e|_2, with the norms
+// accumulated in fp64 alongside, and the depth of a sequential sum over H
+// inputs (an upper bound for any order the matrix core adds in).
+template <int NC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void router_mfma_kernel(const uint16_t *X, int64_t T, const float *Wr,
+                                                          const float *bias, int E, double *lg, uint64_t *bnd,
+                                                          int32_t *n_fixup) {
+  constexpr int H = NC * 256;
+  __shared__ double part[4][64][4];
+  __shared__ double nx2[4][16], nw2[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.y * 16;
+  const int e0 = blockIdx.x * 16;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && n_fixup) *n_fixup = 0;
+  const bool tv = t0 + i < T, ev = e0 + i < E;
+  constexpr int kl = H / 16;
+  const int kb = wave * (H / 4) + g * kl;
+  const uint16_t *xr = X + (tv ? t0 + i : 0) * (int64_t)H + kb;
+  const float *wr = Wr + (int64_t)(ev ? e0 + i : 0) * H + kb;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  double sx = 0.0, sw = 0.0;
+  // every load of the lane's run is issued before the first product
+  constexpr int NCH = kl / 8;
+  uint4 xv[NCH];
+  float4 wv[2 * NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    xv[c] = *reinterpret_cast<const uint4 *>(xr + 8 * c);
+    wv[2 * c] = *reinterpret_cast<const float4 *>(wr + 8 * c);
+    wv[2 * c + 1] = *reinterpret_cast<const float4 *>(wr + 8 * c + 4);
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t xw[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+    const float wf[8] = {wv[2 * c].x, wv[2 * c].y, wv[2 * c].z, wv[2 * c].w,
+                         wv[2 * c + 1].x, wv[2 * c + 1].y, wv[2 * c + 1].z, wv[2 * c + 1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t bits = (j & 1) ? (xw[j >> 1] & 0xFFFF0000u) : (xw[j >> 1] << 16);
+      const double xd = tv ? (double)__uint_as_float(bits) : 0.0;
+      const double wd = ev ? (double)wf[j] : 0.0;
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xd, wd, acc, 0, 0, 0);
+      sx = fma(xd, xd, sx);
+      sw = fma(wd, wd, sw);
+    }
+  }
+  // squared norms of token / expert i over this wavefront's inputs
+  sx += __shfl_xor(sx, 16, 64);
+  sx += __shfl_xor(sx, 32, 64);
+  sw += __shfl_xor(sw, 16, 64);
+  sw += __shfl_xor(sw, 32, 64);
+  if (g == 0) {
+    nx2[wave][i] = sx;
+    nw2[wave][i] = sw;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) part[wave][lane][v] = acc[v];
+  __syncthreads();
+  if (wave == 0) {
+    // the fp64 16x16x4 result: lane l holds tokens t0 + l/16 + 4v, expert e0 + l%16
+    const int e = e0 + i;
+    const double b = (bias && e < E) ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t t = t0 + g + 4 * v;
+      const double d = ((part[0][lane][v] + part[1][lane][v]) + part[2][lane][v]) + part[3][lane][v];
+      if (t < T && e < E) lg[t * E + e] = d + b;
+    }
+  } else if (wave == 1 && lane < 16) {
+    // per-token bound contribution: max over this workgroup's experts of |x_t| |w_e| + |b_e|
+    const int64_t t = t0 + lane;
+    if (t < T) {
+      const double nx = sqrt(((nx2[0][lane] + nx2[1][lane]) + nx2[2][lane]) + nx2[3][lane]);
+      double m = 0.0;
+      for (int j = 0; j < 16 && e0 + j < E; ++j) {
+        const double nw = sqrt(((nw2[0][j] + nw2[1][j]) + nw2[2][j]) + nw2[3][j]);
+        m = fmax(m, nx * nw + (bias ? fabs((double)bias[e0 + j]) : 0.0));
+      }
+      atomicMax((unsigned long long *)&bnd[t], (unsigned long long)dbits(m));
+    }
+  }
+}
+
+// One wavefront per token: certified top-k from the fp64 logits, else the
+// double-double recompute (counted in *n_fixup); resets the token's bound slot.
 template <int NPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(int64_t T, const double *lg, uint64_t *bnd, int E, int k,
-                                                          int depth, int32_t *idx, float *wout, int32_t *fix_count,
-                                                          int32_t *fix_list) {
+__global__ __launch_bounds__(256) void router_topk_kernel(int64_t T, const uint16_t *X, int H, const float *Wr,
+                                                          const float *bias, const double *lg, uint64_t *bnd, int E,
+                                                          int k, int depth, int32_t *idx, float *wout,
+                                                          int32_t *n_fixup) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const double B = 1.01 * gamma_d(depth) * bitsd(bnd[t]);
-  if (!topk_certified<NPL>(lg + t * E, E, k, B, idx + t * k, wout + t * k) && lane == 0)
-    fix_list[atomicAdd(fix_count, 1)] = (int32_t)t;
-  if (lane == 0) bnd[t] = 0;
-}
-
-// Double-double recompute of the listed tokens (one wavefront per token).
-template <int NPL>
-__global__ __launch_bounds__(256) void router_fixup_kernel(const uint16_t *X, int H, const float *Wr,
-                                                           const float *bias, int E, int k, const int32_t *fix_count,
-                                                           const int32_t *fix_list, int32_t *idx, float *wout,
-                                                           int32_t *n_fixup) {
-  const int nfix = *fix_count;
-  if (blockIdx.x == 0 && threadIdx.x == 0 && n_fixup) *n_fixup = nfix;
-  const int wave = threadIdx.x >> 6;
-  for (int i = blockIdx.x * 4 + wave; i < nfix; i += gridDim.x * 4) {
-    const int64_t t = fix_list[i];
+  if (!topk_certified<NPL>(lg + t * E, E, k, B, idx + t * k, wout + t * k)) {
+    if (lane == 0 && n_fixup) atomicAdd(n_fixup, 1);
     topk_dd<NPL>(X + t * H, H, Wr, bias, E, k, idx + t * k, wout + t * k, nullptr);
   }
+  if (lane == 0) bnd[t] = 0;
 }
 
 __global__ void copy_d2f_kernel(const double *a, int64_t n, float *b) {
@@ -168,42 +239,40 @@ __global__ void copy_d2f_kernel(const double *a, int64_t n, float *b) {
 }
 
 // ---------------------------------------------------------------- launchers
+template <int NC>
+static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
+                            int64_t E, const RouterWs &rw, int32_t *n_fixup, int *depth) {
+  constexpr int H = NC * 256;
+  int tchunk = kTokChunkBytes / (H * 2);
+  if (tchunk > 128) tchunk = 128;
+  if (tchunk > T) tchunk = (int)T;
+  dim3 grid((unsigned)cdiv(E, 4), (unsigned)cdiv(T, tchunk));
+  size_t lds = (size_t)tchunk * H * 2;
+  TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, (router_logits_kernel<NC>), grid, dim3(256), lds, st, X, T, Wr, bias, E,
+              tchunk, rw.lg, rw.bnd, n_fixup);
+  TMOE_LAUNCHED("router_logits");
+  *depth = 4 * NC + 8;
+  return TMOE_OK;
+}
+
 template <int NC, int NPL>
 static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
                             int64_t E, int k, int32_t *idx, float *w, int32_t *n_fixup, const RouterWs &rw) {
   constexpr int H = NC * 256;
-  int tchunk = kTokChunkBytes / (H * 2);
-  if (tchunk > 128) tchunk = 128;
-  if (tchunk > T) tchunk = (int)T;
-  dim3 grid((unsigned)cdiv(E, 4), (unsigned)cdiv(T, tchunk));
-  size_t lds = (size_t)tchunk * H * 2;
-  TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, (router_logits_kernel<NC>), grid, dim3(256), lds, st, X, T, Wr, bias, E,
-              tchunk, rw.lg, rw.bnd, rw.fix_count);
+  int depth;
+  if (T <= kDecodeMaxT) {
+    int rc = launch_logits_nc<NC>(st, X, T, Wr, bias, E, rw, n_fixup, &depth);
+    if (rc) return rc;
+  } else {
+    if (cdiv(T, 16) > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
+    TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, (router_mfma_kernel<NC>), dim3((unsigned)cdiv(E, 16), (unsigned)cdiv(T, 16)),
+                dim3(256), 0, st, X, T, Wr, bias, (int)E, rw.lg, rw.bnd, n_fixup);
+    depth = H + 8;
+  }
   TMOE_LAUNCHED("router_logits");
-  const int depth = 4 * NC + 8;
-  TMOE_LAUNCH(TMOE_KERNEL_ROUTER_TOPK, (router_topk_kernel<NPL>), dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, T,
-              rw.lg, rw.bnd, (int)E, k, depth, idx, w, rw.fix_count, rw.fix_list);
+  TMOE_LAUNCH(TMOE_KERNEL_ROUTER_TOPK, (router_topk_kernel<NPL>), dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, T, X,
+              H, Wr, bias, rw.lg, rw.bnd, (int)E, k, depth, idx, w, n_fixup);
   TMOE_LAUNCHED("router_topk");
-  const unsigned fx = (unsigned)(T < 64 ? T : 64);
-  TMOE_LAUNCH(TMOE_KERNEL_ROUTER_FIXUP, (router_fixup_kernel<NPL>), dim3(fx), dim3(256), 0, st, X, H, Wr, bias,
-              (int)E, k, rw.fix_count, rw.fix_list, idx, w, n_fixup);
-  TMOE_LAUNCHED("router_fixup");
-  return TMOE_OK;
-}
-
-template <int NC>
-static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
-                            int64_t E, const RouterWs &rw, int *depth) {
-  constexpr int H = NC * 256;
-  int tchunk = kTokChunkBytes / (H * 2);
-  if (tchunk > 128) tchunk = 128;
-  if (tchunk > T) tchunk = (int)T;
-  dim3 grid((unsigned)cdiv(E, 4), (unsigned)cdiv(T, tchunk));
-  size_t lds = (size_t)tchunk * H * 2;
-  TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, (router_logits_kernel<NC>), grid, dim3(256), lds, st, X, T, Wr, bias, E,
-              tchunk, rw.lg, rw.bnd, rw.fix_count);
-  TMOE_LAUNCHED("router_logits");
-  *depth = 4 * NC + 8;
   return TMOE_OK;
 }
 
@@ -224,11 +293,11 @@ static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
 int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                          int64_t E, const RouterWs &rw, int *depth) {
   switch (H / 256) {
-    case 1: return launch_logits_nc<1>(st, X, T, Wr, bias, E, rw, depth);
-    case 2: return launch_logits_nc<2>(st, X, T, Wr, bias, E, rw, depth);
-    case 4: return launch_logits_nc<4>(st, X, T, Wr, bias, E, rw, depth);
-    case 8: return launch_logits_nc<8>(st, X, T, Wr, bias, E, rw, depth);
-    case 16: return launch_logits_nc<16>(st, X, T, Wr, bias, E, rw, depth);
+    case 1: return launch_logits_nc<1>(st, X, T, Wr, bias, E, rw, nullptr, depth);
+    case 2: return launch_logits_nc<2>(st, X, T, Wr, bias, E, rw, nullptr, depth);
+    case 4: return launch_logits_nc<4>(st, X, T, Wr, bias, E, rw, nullptr, depth);
+    case 8: return launch_logits_nc<8>(st, X, T, Wr, bias, E, rw, nullptr, depth);
+    case 16: return launch_logits_nc<16>(st, X, T, Wr, bias, E, rw, nullptr, depth);
     default: return fail(TMOE_E_UNSUPPORTED, "router hidden size must be 256, 512, 1024, 2048 or 4096");
   }
 }
