@@ -239,6 +239,45 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
     s.nfix = 0;
   }
   __syncthreads();
+  if (T == 1) {
+    // one token: wavefront 0 selects its k experts; their ranks among the k
+    // (all distinct) are the grouped positions and the tile indices
+    if (wave == 0) {
+      const double B = 1.01 * gamma_d(r.depth) * bnd[0];
+      int nfix = 0;
+      if (!topk_select<NPL>(key[0], E, k, B, s.sidx, s.sw)) {
+        nfix = 1;
+        topk_dd<NPL>(a.X, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx, s.sw, nullptr);
+      }
+      const int e = lane < k ? s.sidx[lane] : 0x7FFFFFFF;
+      const float wv = lane < k ? s.sw[lane] : 0.f;
+      int rank = 0;
+      for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(e, j) < e;
+      if (lane < k && rank == (int)blockIdx.x) {
+        s.tok[0] = 0;
+        s.info[1] = rank;
+        s.info[2] = 1;
+        s.info[0] = e;
+      }
+      if (publish) {
+        if (lane < k) {
+          r.idx[lane] = e;
+          r.w[lane] = wv;
+          r.pos[lane] = rank;
+          r.sorted_token[rank] = 0;
+          r.sorted_slot[rank] = lane;
+          r.pair_w[rank] = wv;
+          reinterpret_cast<int4 *>(r.tiles)[rank] = make_int4(e, rank, 1, 0);
+        }
+        if (lane == 0) {
+          *r.ntiles = k;
+          if (r.n_fixup) *r.n_fixup = nfix;
+        }
+      }
+    }
+    __syncthreads();
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
@@ -434,6 +473,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     }
   }
   if constexpr (KS > 1) {
+    static_assert(KS == 4, "the K split is four wavefronts");
     float *red = reinterpret_cast<float *>(smem + 17 * rs);  // [4 waves][64 lanes][8]
     float *mine = red + (wave * 64 + lane) * 8;
 #pragma unroll
@@ -442,20 +482,34 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
       mine[4 + v] = accu[0][v];
     }
     __syncthreads();
-    if (kp != 0) return;
+    // wavefront w finishes row 4g + w of every lane's column (partials summed in wave order)
+    const int v = wave;
+    float gs = 0.f, us = 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      accg[0][v] = 0.f;
-      accu[0][v] = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      gs += red[(q * 64 + lane) * 8 + v];
+      us += red[(q * 64 + lane) * 8 + 4 + v];
     }
-    for (int q = 0; q < KS; ++q) {
-      const float *o = red + ((wave + q) * 64 + lane) * 8;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        accg[0][v] += o[v];
-        accu[0][v] += o[4 + v];
-      }
-    }
+    if (n >= cnt) return;
+    const float sgv[4] = {sg[0].x, sg[0].y, sg[0].z, sg[0].w}, suv[4] = {su[0].x, su[0].y, su[0].z, su[0].w};
+    const float c = a.clamp;
+    const float gg = (gs * 0.5f) * sgv[v];
+    const float uu = (us * 0.5f) * suv[v];
+    const float hv = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
+    const uint16_t b0 = f32_to_bf16_rne(hv);
+    const float r1 = hv - __uint_as_float((uint32_t)b0 << 16);
+    const uint16_t b1 = f32_to_bf16_rne(r1);
+    const float r2 = r1 - __uint_as_float((uint32_t)b1 << 16);
+    const uint16_t b2 = f32_to_bf16_rne(r2);
+    const int nn = rtb * 16 + 4 * g + v;
+    const int q5 = 5 * a.gd.Q;
+    const int64_t p = start + n;
+    const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
+    a.hp[o] = b0;
+    a.hp[a.hp_plane + o] = b1;
+    a.hp[2 * a.hp_plane + o] = b2;
+    if (a.h) a.h[p * a.I + nn] = hv;
+    return;
   }
   if (n >= cnt) return;
   const float c = a.clamp;
@@ -636,15 +690,48 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rt = blockIdx.x;
   constexpr int M = 5 * F + tail_mfmas(RT);
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
   const int nt = *a.ntiles;
   int4 td0 = make_int4(0, 0, 1, 0);
   if (wave < a.max_tiles) td0 = reinterpret_cast<const int4 *>(a.tiles)[wave];  // first tile, before nt is known
+  // first staging batch in flight, then the first tile's weights, then the stores
   constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
-  copy16<64 * kDcWaves>(
-      3 * a.P * VPR,
-      [&](int c) { return reinterpret_cast<const uint4 *>(a.hp)[c]; },
-      [&](int c) { return reinterpret_cast<uint4 *>(hps) + c; },
-      [&](int c, uint4 v) { return keep_live(v, live_in_chunk<F, RT>(a.gd.K, c % VPR)); });
+  constexpr int NT = 64 * kDcWaves, NB = 8;
+  const int nchunk = 3 * a.P * VPR;
+  uint4 sv[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int c = threadIdx.x + j * NT;
+    if (c < nchunk) sv[j] = reinterpret_cast<const uint4 *>(a.hp)[c];
+  }
+  uint2 dd0[F];
+  uint32_t ddw0 = 0, dsh0 = 0;
+  float4 sd0 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (wave < nt) {
+    const uint8_t *dt = a.down_p + (int64_t)td0.x * a.stride_d + (int64_t)rt * tbytes;
+#pragma unroll
+    for (int s = 0; s < F; ++s) dd0[s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
+    if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw0, dsh0);
+    sd0 = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)td0.x * a.H + rt * 16 + 4 * g);
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int c = threadIdx.x + j * NT;
+    if (c < nchunk) reinterpret_cast<uint4 *>(hps)[c] = keep_live(sv[j], live_in_chunk<F, RT>(a.gd.K, c % VPR));
+  }
+  for (int base = threadIdx.x + NB * NT; base < nchunk; base += NT * NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int c = base + j * NT;
+      if (c < nchunk) sv[j] = reinterpret_cast<const uint4 *>(a.hp)[c];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int c = base + j * NT;
+      if (c < nchunk) reinterpret_cast<uint4 *>(hps)[c] = keep_live(sv[j], live_in_chunk<F, RT>(a.gd.K, c % VPR));
+    }
+  }
   if ((int)threadIdx.x < a.P) {
     s_tok[threadIdx.x] = a.sorted_token[threadIdx.x];
     s_pw[threadIdx.x] = a.pair_w[threadIdx.x];
@@ -652,19 +739,24 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   for (int i = lane; i < kDecodeMaxT * 16; i += 64) (&yacc[wave][0][0])[i] = 0.f;
   if (blockIdx.x == 0 && (int)threadIdx.x < a.T) a.bnd[threadIdx.x] = 0;
   __syncthreads();
-  const int n = lane & 15, g = lane >> 4;
-  const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
   const int plane = a.P * a.slots * 2;
   for (int tile = wave; tile < nt; tile += kDcWaves) {
-    const int4 td = tile == wave ? td0 : reinterpret_cast<const int4 *>(a.tiles)[tile];
+    const bool first = tile == wave;
+    const int4 td = first ? td0 : reinterpret_cast<const int4 *>(a.tiles)[tile];
     const int e = td.x, start = td.y, cnt = td.z;
-    const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)rt * tbytes;
     uint2 dd[F];
+    uint32_t ddw = ddw0, dsh = dsh0;
+    float4 sd = sd0;
+    if (first) {
 #pragma unroll
-    for (int s = 0; s < F; ++s) dd[s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
-    uint32_t ddw = 0, dsh = 0;
-    if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw, dsh);
-    const float4 sd = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + rt * 16 + 4 * g);
+      for (int s = 0; s < F; ++s) dd[s] = dd0[s];
+    } else {
+      const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)rt * tbytes;
+#pragma unroll
+      for (int s = 0; s < F; ++s) dd[s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
+      if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw, dsh);
+      sd = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + rt * 16 + 4 * g);
+    }
     const bool live = n < cnt;
     const int p = start + (live ? n : cnt - 1);
     const char *hb = hps + p * a.slots * 2 + g * 16 * M;

@@ -175,30 +175,40 @@ __device__ inline void topk_keys(const double *lg, int E, uint64_t key[NPL]) {
   }
 }
 
-// Certified top-k of one token by one wavefront from its order keys. Each of
-// the k+1 rounds takes the wave maximum (high words first; low words only
-// among the lanes that share the highest high word), and among equal keys the
-// lowest lane, then the lowest j, i.e. the lower expert index. Returns false,
+// Certified top-k of one token by one wavefront from its order keys. The lane's
+// keys are sorted once; each of the k+1 rounds takes the wave maximum of the
+// lanes' head keys (high words first; low words only among the lanes that
+// share the highest high word), and among equal keys the lowest lane, then the
+// lowest j, i.e. the lower expert index. Returns false,
 // writing nothing, when an adjacent gap of the top k+1 is not above 2B.
 // Otherwise lane r < k writes rank r: idx, and the softmax weight over the k
 // (fp64, summed in rank order).
 template <int NPL>
 __device__ inline bool topk_select(uint64_t key[NPL], int E, int k, double B, int32_t *idx, float *w) {
   const int lane = threadIdx.x & 63;
+  // sort the lane's keys in descending order (stable: equal keys keep the lower j first)
+  int sj[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) sj[j] = j;
+#pragma unroll
+  for (int pass = 0; pass < NPL; ++pass)
+#pragma unroll
+    for (int j = pass & 1; j + 1 < NPL; j += 2)
+      if (key[j] < key[j + 1]) {
+        const uint64_t tk = key[j];
+        key[j] = key[j + 1];
+        key[j + 1] = tk;
+        const int tj = sj[j];
+        sj[j] = sj[j + 1];
+        sj[j + 1] = tj;
+      }
   const int m = min(k + 1, E);
   bool ok = true;
   double prev = 0.0, v0 = 0.0, myv = 0.0;
   int myi = 0;
   for (int r = 0; r < m; ++r) {
-    uint64_t bk = 0;
-    int bj = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (key[j] > bk) {
-        bk = key[j];
-        bj = j;
-      }
-    const uint32_t hi = (uint32_t)(bk >> 32), lo = (uint32_t)bk;
+    // the lane's best is its head key; the winner lane drops its head
+    const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
     const uint32_t mh = wave_max_u32(hi);
     uint64_t cand = __ballot(hi == mh);
     uint32_t ml;
@@ -209,11 +219,14 @@ __device__ inline bool topk_select(uint64_t key[NPL], int E, int k, double B, in
       cand = __ballot(hi == mh && lo == ml);
     }
     const int wl = (int)__builtin_ctzll(cand);
-    const int wj = __builtin_amdgcn_readlane(bj, wl);
+    const int wj = __builtin_amdgcn_readlane(sj[0], wl);
     if (lane == wl) {
 #pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (j == wj) key[j] = 0ull;
+      for (int j = 0; j + 1 < NPL; ++j) {
+        key[j] = key[j + 1];
+        sj[j] = sj[j + 1];
+      }
+      key[NPL - 1] = 0ull;
     }
     const double v = from_okey(((uint64_t)mh << 32) | ml);
     if (r == 0) v0 = v;
