@@ -184,6 +184,8 @@ struct FfnWs {
   uint16_t *hp;      // [3][T*k][slots_I] bf16 parts hi + mid + lo = h of each grouped pair,
                      // in the down projection's operand layout
   float *pw;         // [T*k] routing weight of each grouped pair (decode path)
+  int32_t *blocks;   // [max_blocks][4]: expert, start, count (<= 64), 0 (token-blocked gate/up)
+  int32_t *nblocks;  // [1]
 };
 int64_t ffn_max_tiles(int64_t pairs, int64_t E);
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I);

@@ -149,18 +149,19 @@ __device__ inline uint4 keep_live(uint4 v, int nlive) {
 }
 
 // ---------------------------------------------------------------- tiles
-// Work tiles of up to 16 grouped pairs of one expert, in expert order.
+// Work tiles of up to TILE grouped pairs of one expert, in expert order.
+template <int TILE>
 __global__ __launch_bounds__(256) void make_tiles_kernel(const int32_t *offsets, int E, int32_t *tiles,
                                                           int32_t *ntiles) {
   __shared__ int nt[1024];
   __shared__ int tmp[256];
-  for (int e = threadIdx.x; e < E; e += 256) nt[e] = (offsets[e + 1] - offsets[e] + 15) / 16;
+  for (int e = threadIdx.x; e < E; e += 256) nt[e] = (offsets[e + 1] - offsets[e] + TILE - 1) / TILE;
   __syncthreads();
   int total = block_exclusive_scan<256>(nt, E, tmp);
   for (int e = threadIdx.x; e < E; e += 256) {
     int c = offsets[e + 1] - offsets[e], base = nt[e];
-    for (int i = 0; 16 * i < c; ++i) {
-      int4 tv = make_int4(e, offsets[e] + 16 * i, min(16, c - 16 * i), 0);
+    for (int i = 0; TILE * i < c; ++i) {
+      int4 tv = make_int4(e, offsets[e] + TILE * i, min(TILE, c - TILE * i), 0);
       reinterpret_cast<int4 *>(tiles)[base + i] = tv;
     }
   }
@@ -180,10 +181,46 @@ struct GateUpArgs {
   Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
   int I;
   float clamp;
+  const int32_t *offsets;  // [E+1] grouping offsets (token-blocked kernel)
   // routing prologue (decode path only)
   DecodeRoute r;
   int T, E, k;
 };
+
+__device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
+                                const float4 &sg, const float4 &su) {
+  const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+  const float c = a.clamp;
+  float hv[4];
+  uint32_t part[3][2];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float gg = (gs[v] * 0.5f) * sgv[v];
+    const float uu = (us[v] * 0.5f) * suv[v];
+    const float z = fminf(gg, c);
+    hv[v] = __fdividef(z, 1.f + __expf(-z)) * fminf(fmaxf(uu, -c), c);
+    // h = hi + mid + lo exactly (each bf16 rounding keeps the next 8 bits)
+    const uint32_t b0 = f32_to_bf16_rne(hv[v]);
+    const float r1 = hv[v] - __uint_as_float(b0 << 16);
+    const uint32_t b1 = f32_to_bf16_rne(r1);
+    const float r2 = r1 - __uint_as_float(b1 << 16);
+    const uint32_t b2 = f32_to_bf16_rne(r2);
+    const int sh = (v & 1) * 16;
+    if ((v & 1) == 0) part[0][v >> 1] = part[1][v >> 1] = part[2][v >> 1] = 0u;
+    part[0][v >> 1] |= b0 << sh;
+    part[1][v >> 1] |= b1 << sh;
+    part[2][v >> 1] |= b2 << sh;
+  }
+  const int q5 = 5 * a.gd.Q;
+#pragma unroll
+  for (int hpair = 0; hpair < 2; ++hpair) {
+    const int nn = row0 + 2 * hpair;
+    const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<uint32_t *>(a.hp + q * a.hp_plane + o) = part[q][hpair];
+  }
+  if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+}
 
 // ------------------------------------------------------ routing prologue
 // Decode path (T <= 16 tokens, so one work tile per hit expert): every
@@ -335,7 +372,18 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   __syncthreads();
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
+// SiLU with the hardware exponential and a fast divide (a few ulp in fp32)
+__device__ __forceinline__ float silu(float z) { return __fdividef(z, 1.f + __expf(-z)); }
+
+// h = SiLU(min(g, c)) * clip(u, -c, c) of four consecutive intermediate rows
+// row0 .. row0+3 of grouped pair p, from the gate / up sums (trits entered as
+// 2t) and the row scales; stored as three exact bf16 parts in the down
+// operand layout, two rows per 32-bit store (row0 is a multiple of 4 and a
+// quarter holds an even number of inputs, so a row pair never straddles two
+// quarters), and as fp32 if requested.
+struct GateUpArgs;
+__device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
+                                const float4 &sg, const float4 &su);
 
 // Workgroup = 4 wavefronts. KS wavefronts split the K steps of one 16-row tile
 // (partial sums reduced in LDS in fixed order); with KS = 1 each wavefront
@@ -512,32 +560,139 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
     return;
   }
   if (n >= cnt) return;
-  const float c = a.clamp;
   const int64_t p = start + n;
-  const int q5 = 5 * a.gd.Q;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row0 = (rtb + RTB * r) * 16 + 4 * g;
-    const float sgv[4] = {sg[r].x, sg[r].y, sg[r].z, sg[r].w}, suv[4] = {su[r].x, su[r].y, su[r].z, su[r].w};
-    float hv[4];
+  for (int r = 0; r < R; ++r) store_h4(a, p, (rtb + RTB * r) * 16 + 4 * g, accg[r], accu[r], sg[r], su[r]);
+}
+
+// ------------------------------------------- gate / up, token-blocked
+// Many pairs per expert (prefill): a workgroup takes a block of up to 64 pairs
+// of one expert and 128 rows (eight wavefronts, a row tile each, all K steps
+// of its weights in registers). Each wavefront decodes its weights of a K step
+// once and applies them to all four token tiles, so the trit decoding is
+// amortized over 64 tokens. Activations stream through LDS one K step at a
+// time by direct global-to-LDS loads, kTbDepth steps in flight; a step's
+// buffer is [token tile][slice m][quarter g][column n] x 16 B, so the 16
+// columns of an operand read are consecutive (no bank conflicts). Inputs past
+// K are read from a valid address (their trits are zero).
+constexpr int kTbWaves = 8, kTbDepth = 4, kTbStepBytes = 4 * 5 * 64 * 16;
+
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt not waited)
+#define TMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// Waits until at most `later` steps of this wavefront's loads (nj per step) are in flight.
+__device__ __forceinline__ void wait_steps(int later, int nj) {
+  switch (later * 4 + nj) {
+    case 0 * 4 + 2: case 0 * 4 + 3: TMOE_WAIT_VM(0); break;
+    case 1 * 4 + 2: TMOE_WAIT_VM(2); break;
+    case 1 * 4 + 3: TMOE_WAIT_VM(3); break;
+    case 2 * 4 + 2: TMOE_WAIT_VM(4); break;
+    case 2 * 4 + 3: TMOE_WAIT_VM(6); break;
+    case 3 * 4 + 2: TMOE_WAIT_VM(6); break;
+    default: TMOE_WAIT_VM(9); break;
+  }
+}
+
+// LDS reads of this wavefront done, then the workgroup barrier (no wait on loads in flight)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int F>
+__global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) {
+  extern __shared__ __align__(16) char xs[];  // [kTbDepth][kTbStepBytes]
+  const int blk = blockIdx.x;
+  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
+  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
+  const int e = td.x, start = td.y;
+  const int nb = td.z;  // pairs of this block (<= 64)
+  const int ntt = (nb + 15) / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int rt = blockIdx.y * kTbWaves + wave;
+  constexpr int Q5 = 5 * 8 * F;  // inputs per quarter (H = 2048: 520)
+  const int K = (int)a.gx.K;
+
+  // weights of all K steps and the row scales
+  const int64_t tbytes = 64 * (int64_t)(8 * F);
+  const uint8_t *gt = a.gate_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
+  const uint8_t *ut = a.up_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
+  uint2 gd[F], ud[F];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float gg = (accg[r][v] * 0.5f) * sgv[v];
-      const float uu = (accu[r][v] * 0.5f) * suv[v];
-      hv[v] = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
-      // h = hi + mid + lo exactly (each bf16 rounding keeps the next 8 bits)
-      const uint16_t b0 = f32_to_bf16_rne(hv[v]);
-      const float r1 = hv[v] - __uint_as_float((uint32_t)b0 << 16);
-      const uint16_t b1 = f32_to_bf16_rne(r1);
-      const float r2 = r1 - __uint_as_float((uint32_t)b1 << 16);
-      const uint16_t b2 = f32_to_bf16_rne(r2);
-      const int nn = row0 + v;  // intermediate index = down input index
-      const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
-      a.hp[o] = b0;
-      a.hp[a.hp_plane + o] = b1;
-      a.hp[2 * a.hp_plane + o] = b2;
+  for (int s = 0; s < F; ++s) {
+    gd[s] = *reinterpret_cast<const uint2 *>(gt + (int64_t)s * 512 + lane * 8);
+    ud[s] = *reinterpret_cast<const uint2 *>(ut + (int64_t)s * 512 + lane * 8);
+  }
+  const int row0 = rt * 16 + 4 * g;
+  const float4 sg = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
+  const float4 su = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
+
+  // this wavefront's load instructions of a step: j = wave, wave + 8, wave + 16 (< 20),
+  // j = (token tile, slice m); lane (g, n) fetches 16 B of column n, quarter g
+  constexpr int NJ = 3;
+  const int nj = wave + 16 < 20 ? 3 : 2;
+  const uint16_t *srow[NJ];
+  int kq[NJ];
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    const int j = wave + 8 * q;
+    const int tt = j / 5, m = j - tt * 5;
+    const int col = min(16 * tt + n, nb - 1);
+    srow[q] = a.X + (int64_t)a.sorted_token[start + col] * K;
+    kq[q] = Q5 * g + 8 * m;  // input index at step 0
+  }
+  auto issue = [&](int s) {
+    char *buf = xs + (s % kTbDepth) * kTbStepBytes;
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      if (q < nj) {
+        const int j = wave + 8 * q;
+        int k0 = kq[q] + 40 * s;
+        k0 = k0 < K ? k0 : K - 8;
+        __builtin_amdgcn_global_load_lds((const void *)(srow[q] + k0),
+                                         (__attribute__((address_space(3))) void *)(buf + j * 1024), 16, 0, 0);
+      }
     }
-    if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+  };
+#pragma unroll
+  for (int s = 0; s < kTbDepth - 1; ++s) issue(s);
+
+  f32x4 accg[4], accu[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    accg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < F; ++s) {
+    if (s + kTbDepth - 1 < F) issue(s + kTbDepth - 1);
+    uint32_t pg[20], pu[20];
+    unpack8(gd[s], pg);
+    unpack8(ud[s], pu);
+    // wait for this wavefront's loads of step s, then for everyone's
+    static_assert(kTbDepth == 4, "wait_steps covers three steps in flight");
+    wait_steps((F - 1 - s) < (kTbDepth - 1) ? (F - 1 - s) : (kTbDepth - 1), nj);
+    __builtin_amdgcn_s_barrier();
+    const char *buf = xs + (s % kTbDepth) * kTbStepBytes + (g * 16 + n) * 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntt) {
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          const u32x4 bx = lds16(buf + (t * 5 + m) * 1024);
+          accg[t] = mfma_bf16(pg + 4 * m, bx, accg[t]);
+          accu[t] = mfma_bf16(pu + 4 * m, bx, accu[t]);
+        }
+      }
+    }
+    lds_barrier();  // the buffer of step s is refilled by the next issue
+  }
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = 16 * t + n;
+    if (t >= ntt || col >= nb) continue;
+    store_h4(a, start + col, row0, accg[t], accu[t], sg, su);
   }
 }
 
@@ -970,6 +1125,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *O, const floa
 
 // ----------------------------------------------------------------- host side
 int64_t ffn_max_tiles(int64_t pairs, int64_t E) { return cdiv(pairs, 16) + (pairs < E ? pairs : E); }
+static int64_t ffn_max_blocks(int64_t pairs, int64_t E) { return cdiv(pairs, 64) + (pairs < E ? pairs : E); }
 
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   (void)H;
@@ -980,6 +1136,8 @@ size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   o = align_up(o + 16, 256);
   o = align_up(o + (size_t)3 * P * gi.slots * 2, 256);
   o = align_up(o + (size_t)P * 4, 256);
+  o = align_up(o + ffn_max_blocks(P, E) * 16, 256);
+  o = align_up(o + 16, 256);
   return o;
 }
 
@@ -996,6 +1154,10 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   f.hp = (uint16_t *)(b + o);
   o = align_up(o + (size_t)3 * P * make_geom(I).slots * 2, 256);
   f.pw = (float *)(b + o);
+  o = align_up(o + (size_t)P * 4, 256);
+  f.blocks = (int32_t *)(b + o);
+  o = align_up(o + ffn_max_blocks(P, E) * 16, 256);
+  f.nblocks = (int32_t *)(b + o);
   return f;
 }
 
@@ -1143,13 +1305,27 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   if (max_tiles > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too many tokens");
 
   if (!tiles_ready) {
-    TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
+    TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel<16>, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
                 fw.ntiles);
     TMOE_LAUNCHED("make_tiles");
   }
 
   GateUpArgs ga = gateup_args(W, X, P, clamp, Hout, fw, sorted_token);
-  if (P <= 64)
+  ga.offsets = offsets;
+  if (P >= 32 * E) {
+    // many pairs per expert: token-blocked (64 pairs x 128 rows per workgroup)
+    hipLaunchKernelGGL(make_tiles_kernel<64>, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.blocks, fw.nblocks);
+    TMOE_LAUNCHED("make_blocks");
+    GateUpArgs gb = ga;
+    gb.tiles = fw.blocks;
+    gb.ntiles = fw.nblocks;
+    const size_t lds = (size_t)kTbDepth * kTbStepBytes;
+    rc = allow_lds<gateup_tb_kernel<13>>(lds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_GATEUP, gateup_tb_kernel<13>,
+                dim3((unsigned)ffn_max_blocks(P, E), (unsigned)(I / (16 * kTbWaves))), dim3(64 * kTbWaves), lds, st, gb);
+    TMOE_LAUNCHED("gateup_tb");
+  } else if (P <= 64)
     rc = run_gateup<13, 0, 4, 0>(st, ga, max_tiles, (int)I);
   else if (P < 1024)
     rc = run_gateup<13, 0, 1, 0, 1>(st, ga, max_tiles, (int)I);

@@ -366,6 +366,32 @@ def test_layer_few_experts(tm, E, k, T):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("E,k,T", [(8, 2, 600), (16, 4, 333)])
+def test_layer_token_blocked(tm, E, k, T):
+    """Many pairs per expert (the token-blocked gate/up path): every output of
+    the layer, and h and the expert outputs of the step-by-step ABI."""
+    from ternary_weight_moe_base_amd import synthetic
+    say(f"layer token-blocked E={E} k={k} T={T}")
+    cfg = 4
+    W = synthetic.build_layer(cfg, 0, None, experts=E, top_k=k)
+    xb = ti.activations(cfg, T)
+    got = _run_layer(tm, W, xb)
+    ref = O.moe_layer(xb, ti.router_matrix(cfg, 0)[:E], None, lambda e: _raw_expert(cfg, 0, e), k=k)
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert np.array_equal(got["pos"], ref["pos"])
+    say(f"  pairs per expert: {np.bincount(ref['idx'].ravel(), minlength=E).tolist()}")
+    err = O.max_normalized_error(got["Y"], ref["Y"])
+    say(f"  Y max normalized error {err:.2e}")
+    assert err <= TOL
+    g = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k, T * k)]
+    tm.group_by_expert(dev(got["idx"]), E, *g, ws=ws_bytes(tm.group_workspace_bytes(T, k, E)))
+    O_ = torch.empty((T * k, 2048), dtype=torch.float32, device="cuda")
+    Hh = torch.empty((T * k, 512), dtype=torch.float32, device="cuda")
+    tm.expert_ffn(W, bf16_dev(xb), g[1], g[2], O_, ws_bytes(tm.ffn_workspace_bytes(T, W)), Hout=Hh)
+    assert O.max_normalized_error(host(Hh), ref["H"]) <= TOL
+    assert O.max_normalized_error(host(O_), ref["O"]) <= TOL
+
+
 def test_layer_prefill_sampled(tm, layers):
     # prefill of 4096 tokens: router and grouping checked on every token, the
     # expert outputs on a sample of tokens (their experts computed by the oracle)
