@@ -261,8 +261,10 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
  * Measurement hook. Between tmoe_profile_begin and tmoe_profile_end every
  * launch of one kernel (TMOE_KERNEL_*) carries a HIP start/stop event pair
  * that its own dispatch records on its stream (hipExtLaunchKernelGGL), for at
- * most `capacity` launches (later launches are not recorded). Use it on eager
- * launches, not inside HIP graph capture. The events
+ * most `capacity` launches (later launches are not recorded). Before a timed
+ * launch the host waits for its stream to drain, so the interval holds that
+ * dispatch alone (the window is for measurement, never for throughput). Use it
+ * on eager launches, not inside HIP graph capture. The events
  * are created by tmoe_profile_begin (not on the hot path) and destroyed by
  * tmoe_profile_end, which waits for them and writes the per-launch durations
  * in milliseconds to ms[0..*count). The events carry no system-scope fence

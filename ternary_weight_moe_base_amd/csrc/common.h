@@ -120,13 +120,17 @@ bool prof_events(int kid, hipEvent_t *start, hipEvent_t *stop);
 
 // Launch that, under a profiling window for `kid`, carries start/stop events
 // recorded by the dispatch itself (hipExtLaunchKernelGGL).
+// A timed launch first waits for the stream to drain, so that its events
+// bracket the kernel alone (no queued predecessor inside the interval).
 #define TMOE_LAUNCH(kid, kernel, grid, block, lds, st, ...)                              \
   do {                                                                                 \
     hipEvent_t ev0_, ev1_;                                                             \
-    if (::tmoe::prof_events(kid, &ev0_, &ev1_))                                        \
+    if (::tmoe::prof_events(kid, &ev0_, &ev1_)) {                                      \
+      (void)hipStreamSynchronize(st);                                                  \
       hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev0_, ev1_, 0, __VA_ARGS__); \
-    else                                                                               \
+    } else {                                                                           \
       hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);                   \
+    }                                                                                  \
   } while (0)
 
 // Kernels using more than 64 KiB of LDS opt in once per kernel (gfx950 has 160 KiB).
