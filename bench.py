@@ -34,7 +34,10 @@ WORKLOADS = {
     2: dict(name="moe_layer_decode_T1", tokens=1, bias=None, layers=24, steps=2400, warmup=48),
     3: dict(name="moe_layer_decode_T64_zipf1.1", tokens=64, bias="zipf", layers=24, steps=480, warmup=48),
     4: dict(name="moe_layer_prefill_T4096_uniform", tokens=4096, bias="uniform", layers=4, steps=40, warmup=4),
-    5: dict(name="moe_stack24_T256_residual", tokens=256, bias=None, layers=24, steps=20, warmup=2),
+    5: dict(name="moe_stack24_T256_residual", tokens=256, bias=None, layers=24, steps=20, warmup=2, stack=True),
+    # one token at a time through the same 24-layer stack: per-token decode latency
+    6: dict(name="moe_stack24_decode_T1_residual", tokens=1, bias=None, layers=24, steps=100, warmup=4, stack=True,
+            model_cfg=5),
 }
 
 
@@ -53,7 +56,8 @@ def roofline(name, ms, n_hit, T, cfg, bias):
 
     P = T * K_TOP
     mean_s = float(np.mean(ms)) * 1e-3
-    x_b, y_b = T * H * 2, T * H * (2 if cfg == 5 else 4)
+    stack = WORKLOADS[cfg].get("stack", False)
+    x_b, y_b = T * H * 2, T * H * (2 if stack else 4)
     flops = None
     if name == "router_logits":
         b = np.full(len(n_hit), ROUTER_BYTES + x_b + (E * 4 if bias else 0) + (T * K_TOP * 8 if T <= 16 else 0))
@@ -65,7 +69,7 @@ def roofline(name, ms, n_hit, T, cfg, bias):
         b = n_hit * (PACKED_D + 4 * H)
         flops, fpeak = 2.0 * P * I * H, BF16_PEAK_TFLOPS
     elif name == "combine":
-        b = np.full(len(n_hit), y_b + (x_b if cfg == 5 else 0) + T * K_TOP * 8)
+        b = np.full(len(n_hit), y_b + (x_b if stack else 0) + T * K_TOP * 8)
     else:  # top-k, grouping, tiles: index arrays only
         b = np.full(len(n_hit), T * K_TOP * 4 * 4)
     mean_b = float(np.mean(b))
@@ -125,7 +129,9 @@ def cpu_baseline(cfg: int, wl: dict, n_tok: int | None, budget_s: float = 12.0):
         blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas = 1
-    if cfg == 2:
+    cfg = wl.get("model_cfg", cfg)
+    one = wl["tokens"] == 1
+    if one:
         batches = ((i % wl["layers"], ti.activations(cfg, i + 1)[i:i + 1]) for i in range(n_tok or 1000))
     else:
         x = ti.activations(cfg, wl["tokens"])
@@ -143,7 +149,7 @@ def cpu_baseline(cfg: int, wl: dict, n_tok: int | None, budget_s: float = 12.0):
             tokens += xb.shape[0]
             if timed >= budget_s:
                 break
-    what = "token i through layer i mod 24" if cfg == 2 else "batches of 8 tokens through layer 0"
+    what = "token i through layer i mod 24" if one else "batches of 8 tokens through layer 0"
     sample = (f"{tokens} token(s) of the {wl['name']} workload ({what}) through the oracle's moe_layer; "
               f"{timed:.1f} s of oracle time; router and raw fp32 experts drawn beforehand, untimed")
     return {"value": tokens / timed, "unit": "tokens/s", "cores": blas if blas > 1 else 1,
@@ -172,11 +178,13 @@ def main():
     W_ = args.warmup if args.warmup is not None else wl["warmup"]
     L = args.layers if args.layers is not None else wl["layers"]
     T = wl["tokens"]
+    stack = wl.get("stack", False)
+    mcfg = wl.get("model_cfg", cfg)  # seeds of the model's weights and activations
     dev = torch.device("cuda")
     torch.cuda.init()
 
     t0 = time.perf_counter()
-    layers = [synthetic.build_layer(cfg, l, wl["bias"]) for l in range(L)]
+    layers = [synthetic.build_layer(mcfg, l, wl["bias"]) for l in range(L)]
     torch.cuda.synchronize()
     log(f"built {L} layers in {time.perf_counter() - t0:.1f} s")
 
@@ -184,7 +192,11 @@ def main():
     Y = torch.empty((T, H), dtype=torch.float32, device=dev)
     n_steps = W_ + K
     if cfg == 5:
-        X = synthetic.activations(cfg, T)
+        X = synthetic.activations(mcfg, T)
+        idx_buf = torch.empty((n_steps * L, T, K_TOP), dtype=torch.int32, device=dev)
+    elif cfg == 6:
+        X = synthetic.activations(mcfg, n_steps).view(n_steps, 1, H)  # token i = row i of the stack batch
+        Xw = torch.empty((1, H), dtype=X.dtype, device=dev)  # the token's residual stream
         idx_buf = torch.empty((n_steps * L, T, K_TOP), dtype=torch.int32, device=dev)
     else:
         n_batches = n_steps if cfg == 2 else min(n_steps, 64)
@@ -195,6 +207,9 @@ def main():
         if cfg == 5:
             for l in range(L):
                 tm.moe_forward(layers[l], X, None, ws, idx=idx_buf[i * L + l], resid_out=X)
+        elif cfg == 6:
+            for l in range(L):
+                tm.moe_forward(layers[l], X[i] if l == 0 else Xw, None, ws, idx=idx_buf[i * L + l], resid_out=Xw)
         else:
             tm.moe_forward(layers[i % L], X[i % X.shape[0]], Y, ws, idx=idx_buf[i])
 
@@ -203,7 +218,7 @@ def main():
     torch.cuda.synchronize()
 
     use_graph = not args.no_graph
-    prof_cap = K * (L if cfg == 5 else 1)
+    prof_cap = K * (L if stack else 1)
     graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
@@ -242,17 +257,17 @@ def main():
     torch.cuda.synchronize()
 
     ms_per_step = 1e3 * elapsed / K
-    layer_passes = K * (L if cfg == 5 else 1)
+    layer_passes = K * (L if stack else 1)
     tokens_per_layer_s = T * layer_passes / elapsed
 
     # algorithmic bytes: packed experts (+ scales) with >= 1 routed token, router, X, Y
     idx_h = idx_buf.cpu().numpy()
-    if cfg == 5:
+    if stack:
         sel = idx_h[W_ * L:(W_ + K) * L]
     else:
         sel = idx_h[W_:W_ + K]
     n_hit = np.array([len(np.unique(s)) for s in sel])
-    step_bytes = ROUTER_BYTES + n_hit * EXPERT_BYTES + T * H * 2 + T * H * (2 if cfg == 5 else 4)
+    step_bytes = ROUTER_BYTES + n_hit * EXPERT_BYTES + T * H * 2 + T * H * (2 if stack else 4)
     hbm_gbs = float(step_bytes.sum()) / elapsed / 1e9
 
     # roofline of the dominant kernel (largest total time per step)
@@ -261,6 +276,9 @@ def main():
     roof = roofline(dom, kern[dom], n_hit, T, cfg, bias=wl["bias"] is not None)
     roof["kernels_us_per_layer"] = {n: round(v, 3) for n, v in per_step_us.items()}
 
+    extra = {}
+    if stack and T == 1:  # one token through the whole stack per step: its latency
+        extra = {"token_latency_us": 1e6 * elapsed / K, "stack_tokens_per_s": K / elapsed}
     out = {
         "metric": METRIC,
         "value": tokens_per_layer_s,
@@ -274,13 +292,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["name"], "tokens_per_step": T, "layers_per_step": L if cfg == 5 else 1,
+        "config": {"workload": wl["name"], "tokens_per_step": T, "layers_per_step": L if stack else 1,
                    "distinct_layers": L, "hidden": H, "experts": E, "top_k": K_TOP, "moe_intermediate": I,
                    "weights": "ternary, 5 trits/byte, fp32 row scales", "hip_graph": use_graph},
         "achieved_hbm_gbs": hbm_gbs,
         "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
-        "algorithmic_bytes_per_step": float(np.mean(step_bytes)) * (L if cfg == 5 else 1),
+        "algorithmic_bytes_per_step": float(np.mean(step_bytes)) * (L if stack else 1),
         "roofline": roof,
+        **extra,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

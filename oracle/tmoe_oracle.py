@@ -252,7 +252,9 @@ def group_by_expert(idx: np.ndarray, E: int):
 # O7 expert FFN, O8 combine, O9 residual
 # ----------------------------------------------------------------------------
 def silu(z: np.ndarray) -> np.ndarray:
-    return z / (1.0 + np.exp(-z))
+    # for z below about -709, e^(-z) is +inf in fp64 and z / inf = -0, the limit
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def expert_ffn(x: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray, clamp: float = 7.0):

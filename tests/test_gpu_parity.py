@@ -499,3 +499,58 @@ def test_stack_teacher_forced(tm, layers):
             say(f"  stack layer {layer} token {t}: max normalized error {err:.2e}")
             assert err <= TOL
         xb = xn
+
+
+def test_stack_decode_one_token(tm, layers):
+    """One token through all 24 layers of the stack workload, each layer's
+    output feeding the next through the bf16 residual stream (the one-token
+    decode chain): every layer's top-8 and residual checked, Y against the
+    oracle (teacher-forced) on sampled layers; the same chain captured in one
+    HIP graph and replayed gives the eager result bit for bit."""
+    cfg, L = 5, 24
+    xb0 = ti.activations(cfg, 3)[2:3]
+    Ws = [layers(cfg, l, None) for l in range(L)]
+    ws = ws_bytes(tm.moe_workspace_bytes(1, Ws[0]))
+    Y = torch.empty((1, 2048), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, 1, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, 1, 8), dtype=torch.float32, device="cuda")
+    xs = [bf16_dev(xb0)] + [torch.empty((1, 2048), dtype=torch.int16, device="cuda") for _ in range(L)]
+    xb = xb0
+    for l in range(L):
+        tm.moe_forward(Ws[l], xs[l], Y, ws, idx=idx[l], w=w[l], resid_out=xs[l + 1])
+        Yh, xn = host(Y), host(xs[l + 1]).view(np.uint16)
+        ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), ti.router_matrix(cfg, l), None, 8)
+        assert np.array_equal(host(idx[l]), ridx), l
+        assert np.array_equal(xn, O.residual_bf16(xb, Yh)), l
+        if l in (0, 11, 23):
+            x = O.bf16_to_f64(xb)
+            y = np.zeros(2048)
+            for j in range(8):
+                deq = [O.dequantize(*O.ternarize_absmean(m)) for m in _raw_expert(cfg, l, int(ridx[0, j]))]
+                y += rw[0, j] * O.expert_ffn(x, *deq)[3][0]
+            err = O.max_normalized_error(Yh, y[None])
+            say(f"  one-token stack layer {l}: max normalized error {err:.2e}")
+            assert err <= TOL
+        xb = xn
+    final = host(xs[L]).copy()
+    idx_eager = host(idx).copy()
+
+    # the whole chain as one graph (in place on one residual buffer), replayed
+    Xw = torch.empty((1, 2048), dtype=torch.int16, device="cuda")
+    idx_g = torch.zeros_like(idx)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        for l in range(L):
+            tm.moe_forward(Ws[l], xs[0] if l == 0 else Xw, None, ws, idx=idx_g[l], resid_out=Xw)
+        g.capture_end()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        Xw.fill_(0)
+        idx_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        assert np.array_equal(host(Xw), final), rep
+        assert np.array_equal(host(idx_g), idx_eager), rep
