@@ -35,6 +35,10 @@ def _load() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise ImportError(f"{_LIB_PATH} not built; run `python -m ternary_weight_moe_base_amd.build`")
+        # PyTorch first: its HIP runtime (soname libamdhip64.so.7) is then the one
+        # libtmoe.so binds to. Loaded the other way round, the process holds two
+        # HIP runtimes, and the second to initialise finds no device.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(_LIB_PATH)
         _abi.declare(lib)
         _abi.bind_status(lib)

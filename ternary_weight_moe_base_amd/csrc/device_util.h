@@ -74,4 +74,12 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// LDS accesses of this wavefront done, then the workgroup barrier. Unlike
+// __syncthreads() it does not wait for the wavefront's global loads and stores
+// in flight (vmcnt), so they may cross the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
 }  // namespace tmoe

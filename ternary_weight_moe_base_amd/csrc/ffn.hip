@@ -246,14 +246,14 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   const DecodeRoute &r = a.r;
   const int T = a.T, E = a.E, k = a.k, P = T * k;
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
-  // order keys of this wavefront's tokens (t = wave + 4q), in flight with the staging below
-  uint64_t key[kDecodeMaxT / 4][NPL];
+  // logits of this wavefront's tokens (t = wave + 4q), in flight with the staging below
+  double lv[kDecodeMaxT / 4][NPL];
   double bnd[kDecodeMaxT / 4];
 #pragma unroll
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
     if (t < T) {
-      topk_keys<NPL>(r.lg + (int64_t)t * E, E, key[q]);
+      topk_load<NPL>(r.lg + (int64_t)t * E, E, lv[q]);
       bnd[q] = bitsd(r.bnd[t]);
     }
   }
@@ -275,14 +275,14 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
     s.info[0] = -1;
     s.nfix = 0;
   }
-  __syncthreads();
+  lds_barrier();  // the logits may still be in flight
   if (T == 1) {
     // one token: wavefront 0 selects its k experts; their ranks among the k
     // (all distinct) are the grouped positions and the tile indices
     if (wave == 0) {
       const double B = 1.01 * gamma_d(r.depth) * bnd[0];
       int nfix = 0;
-      if (!topk_select<NPL>(key[0], E, k, B, s.sidx, s.sw)) {
+      if (!topk_certified_v<NPL>(lv[0], r.lg, E, k, B, s.sidx, s.sw)) {
         nfix = 1;
         topk_dd<NPL>(a.X, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx, s.sw, nullptr);
       }
@@ -312,7 +312,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
         }
       }
     }
-    __syncthreads();
+    lds_barrier();  // the published stores need not land before the expert work starts
     return;
   }
 #pragma unroll
@@ -320,7 +320,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
     const int t = wave + 4 * q;
     if (t < T) {
       const double B = 1.01 * gamma_d(r.depth) * bnd[q];
-      if (!topk_select<NPL>(key[q], E, k, B, s.sidx + t * k, s.sw + t * k)) {
+      if (!topk_certified_v<NPL>(lv[q], r.lg + (int64_t)t * E, E, k, B, s.sidx + t * k, s.sw + t * k)) {
         if (lane == 0) atomicAdd(&s.nfix, 1);
         topk_dd<NPL>(a.X + (int64_t)t * a.gx.K, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx + t * k, s.sw + t * k,
                      nullptr);
@@ -369,7 +369,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
     *r.ntiles = nh;
     if (r.n_fixup) *r.n_fixup = s.nfix;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // SiLU with the hardware exponential and a fast divide (a few ulp in fp32)
@@ -470,8 +470,9 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
           return reinterpret_cast<uint4 *>(xs + n * rs + c * 16);
         });
     zero_row(xs + 16 * rs, a.gx.slots, threadIdx.x, 256);
+    __syncthreads();
   }
-  __syncthreads();
+  // (with the routing prologue the activations were staged before its last barrier)
 
   const int n = lane & 15, g = lane >> 4;
   const int brow = n < cnt ? (RNPL > 0 ? toks[n] : n) : 16;
@@ -590,12 +591,6 @@ __device__ __forceinline__ void wait_steps(int later, int nj) {
     case 3 * 4 + 2: TMOE_WAIT_VM(6); break;
     default: TMOE_WAIT_VM(9); break;
   }
-}
-
-// LDS reads of this wavefront done, then the workgroup barrier (no wait on loads in flight)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
 }
 
 template <int F>
@@ -893,7 +888,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   }
   for (int i = lane; i < kDecodeMaxT * 16; i += 64) (&yacc[wave][0][0])[i] = 0.f;
   if (blockIdx.x == 0 && (int)threadIdx.x < a.T) a.bnd[threadIdx.x] = 0;
-  __syncthreads();
+  lds_barrier();  // the first tile's weights and the bound reset may still be in flight
   const int plane = a.P * a.slots * 2;
   for (int tile = wave; tile < nt; tile += kDcWaves) {
     const bool first = tile == wave;

@@ -164,15 +164,23 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Order keys of one token's logits: lane l holds experts l*NPL + j (0 past E).
+// One token's logits: lane l holds experts l*NPL + j (0 past E).
 template <int NPL>
-__device__ inline void topk_keys(const double *lg, int E, uint64_t key[NPL]) {
+__device__ inline void topk_load(const double *lg, int E, double v[NPL]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane * NPL + j;
-    key[j] = e < E ? okey(lg[e]) : 0ull;
+    v[j] = e < E ? lg[e] : 0.0;
   }
+}
+
+// Order keys of the logits held as by topk_load (0 past E).
+template <int NPL>
+__device__ inline void topk_keys(const double v[NPL], int E, uint64_t key[NPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) key[j] = lane * NPL + j < E ? okey(v[j]) : 0ull;
 }
 
 // Certified top-k of one token by one wavefront from its order keys. The lane's
@@ -248,11 +256,88 @@ __device__ inline bool topk_select(uint64_t key[NPL], int E, int k, double B, in
   return true;
 }
 
+// Fast certified top-k on unique 32-bit keys. The key of expert e is its
+// "bucket" (the logit rounded to fp32, order-preserving, with the low IB bits
+// cleared: a non-decreasing function of the logit) above E - 1 - e in those
+// bits, so keys are distinct, and a wave maximum needs one 32-bit pass per
+// round and identifies the winner by equality. The buckets order the logits
+// only coarsely; the result is that of the exact logits when
+//  - no unselected expert shares the bucket of the last selected one (then
+//    every unselected logit is strictly below every selected one), and
+//  - the selected fp64 logits, read back from lg, decrease with every
+//    adjacent gap above 2B (the same test as topk_select).
+// Otherwise it returns false and writes nothing (about 0.1% of tokens with
+// logits ~ N(0, 1); the caller then runs topk_select). When it returns true,
+// idx and w are those topk_select writes: same ranks, same fp64 softmax.
+template <int NPL>
+__device__ inline bool topk_fast(const double v[NPL], const double *lg, int E, int k, double B, int32_t *idx,
+                                 float *w) {
+  constexpr int IB = NPL * 64 <= 256 ? 8 : (NPL * 64 <= 1024 ? 10 : 12);
+  static_assert(NPL * 64 <= (1 << IB), "expert index must fit the low key bits");
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane * NPL + j;
+    uint32_t u = __float_as_uint((float)v[j]);  // round to nearest: non-decreasing
+    if (u == 0x80000000u) u = 0u;               // -0 and +0 share a bucket
+    const uint32_t o = (u >> 31) ? ~u : (u | 0x80000000u);
+    key[j] = e < E ? (((o >> IB) << IB) | (uint32_t)(E - 1 - e)) : 0u;
+  }
+  // descending within the lane
+#pragma unroll
+  for (int pass = 0; pass < NPL; ++pass)
+#pragma unroll
+    for (int j = pass & 1; j + 1 < NPL; j += 2)
+      if (key[j] < key[j + 1]) {
+        const uint32_t t = key[j];
+        key[j] = key[j + 1];
+        key[j + 1] = t;
+      }
+  const int m = min(k + 1, E);
+  uint32_t mine = 0u;  // lane r: the key of rank r
+  for (int r = 0; r < m; ++r) {
+    const uint32_t mx = wave_max_u32(key[0]);  // > 0: fewer than E experts taken
+    if (key[0] == mx) {                        // the one lane holding it
+#pragma unroll
+      for (int j = 0; j + 1 < NPL; ++j) key[j] = key[j + 1];
+      key[NPL - 1] = 0u;
+    }
+    if (lane == r) mine = mx;
+  }
+  const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)mine, m - 1);
+  if (__ballot(key[0] >= ((last >> IB) << IB)) != 0ull) return false;  // bucket shared with an unselected expert
+  const int myi = E - 1 - (int)(mine & ((1u << IB) - 1u));
+  const double myv = lane < m ? lg[myi] : 0.0;
+  const double nxt = __shfl_down(myv, 1, 64);
+  if (__ballot(lane + 1 < m && !(myv - nxt > 2.0 * B)) != 0ull) return false;
+  const double v0 = readlane_d(myv, 0);
+  const double p = lane < k ? exp(myv - v0) : 0.0;
+  double den = 0.0;
+  for (int r = 0; r < k; ++r) den += readlane_d(p, r);
+  if (lane < k) {
+    idx[lane] = myi;
+    w[lane] = (float)(p / den);
+  }
+  return true;
+}
+
+// Certified top-k of one token's logits lg[0..E) by one wavefront: the fast
+// 32-bit path, then the 64-bit tournament. False: not certifiable in fp64.
+template <int NPL>
+__device__ inline bool topk_certified_v(const double v[NPL], const double *lg, int E, int k, double B, int32_t *idx,
+                                        float *w) {
+  if (topk_fast<NPL>(v, lg, E, k, B, idx, w)) return true;
+  uint64_t key[NPL];
+  topk_keys<NPL>(v, E, key);
+  return topk_select<NPL>(key, E, k, B, idx, w);
+}
+
 template <int NPL>
 __device__ inline bool topk_certified(const double *lg, int E, int k, double B, int32_t *idx, float *w) {
-  uint64_t key[NPL];
-  topk_keys<NPL>(lg, E, key);
-  return topk_select<NPL>(key, E, k, B, idx, w);
+  double v[NPL];
+  topk_load<NPL>(lg, E, v);
+  return topk_certified_v<NPL>(v, lg, E, k, B, idx, w);
 }
 
 // Double-double logits of one token by one wavefront (lane-strided partial

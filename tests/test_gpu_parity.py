@@ -231,6 +231,35 @@ def test_router_ties_take_exact_path(tm, T):
     assert O.max_normalized_error(w, rw) <= TOL
 
 
+def _near_tie_router(seed):
+    # three equal router rows whose biases differ by one and two fp32 ulps of
+    # 5.0: the logits differ by ~5e-7, far below fp32 resolution of their
+    # ordering near 5 but far above the fp64 error bound, and the value order
+    # (250 > 99 > 3) is the reverse of the index order
+    Wr = ti.router_matrix(seed, 0).copy()
+    Wr[99] = Wr[3]
+    Wr[250] = Wr[3]
+    b = np.zeros(256, np.float32)
+    b[3] = 5.0
+    b[99] = np.nextafter(np.float32(5.0), np.float32(6.0))
+    b[250] = np.nextafter(b[99], np.float32(6.0))
+    return Wr, b
+
+
+@pytest.mark.parametrize("T", [40, 8])
+def test_router_near_ties_certified_in_fp64(tm, T):
+    # logits that share an fp32 bucket but are separated in fp64: certified
+    # without the double-double recompute, in value order
+    xb = ti.activations(10, T)
+    Wr, b = _near_tie_router(10)
+    idx, w, nfix, _ = _router(tm, xb, Wr, b, 8)
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
+    assert nfix == 0
+    assert np.array_equal(idx, ridx)
+    assert np.all(idx[:, :3] == [250, 99, 3])
+    assert O.max_normalized_error(w, rw) <= TOL
+
+
 @pytest.mark.parametrize("k,E,H,T", [(1, 256, 2048, 33), (16, 256, 2048, 9), (8, 64, 256, 100), (4, 1000, 512, 7),
                                      (64 // 8, 8, 256, 5)])
 def test_router_shapes(tm, k, E, H, T):
@@ -463,6 +492,22 @@ def test_layer_decode_ties(tm, layers):
     assert got["nfix"] == 6
     assert np.array_equal(got["idx"], ridx)
     assert np.all(got["idx"][:, :3] == [3, 99, 250])
+
+
+@pytest.mark.parametrize("T", [1, 6])
+def test_layer_decode_near_ties(tm, layers, T):
+    # the decode front end with logits separated only in fp64 (value order
+    # reverses index order): certified in fp64, no double-double recompute
+    W = layers(2, 0, None)
+    Wr, b = _near_tie_router(2)
+    W2 = type(W)(dev(Wr), dev(b), *W.tensors[2:], top_k=8)
+    xb = ti.activations(12, T)
+    got = _run_layer(tm, W2, xb)
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
+    assert got["nfix"] == 0
+    assert np.array_equal(got["idx"], ridx)
+    assert np.all(got["idx"][:, :3] == [250, 99, 3])
+    assert O.max_normalized_error(got["w"], rw) <= TOL
 
 
 def test_layer_empty_batch(tm, layers):
