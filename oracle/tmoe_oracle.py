@@ -222,6 +222,64 @@ def router_topk(x: np.ndarray, Wr: np.ndarray, bias: np.ndarray | None, k: int):
 
 
 # ----------------------------------------------------------------------------
+# LM head: untied bf16 output embedding, logits over the vocabulary, top-k
+# ----------------------------------------------------------------------------
+def lm_head_topk(x_bits: np.ndarray, W_bits: np.ndarray, k: int, chunk: int = 16384):
+    """Output head of the model and the k most likely next tokens.
+
+    ai.thesatyajit.com, "The 5.31 GB claim reconciles, and the leftover is the
+    vocabulary": the input and output embedding tables (151,936 tokens x 2048)
+    are untied and stay un-quantized; at the model's compression they are
+    about a quarter of the file. Readings: the output table is bf16 [V][H]
+    (two bytes per entry, which is what the page's file-size arithmetic
+    implies), the head's input is the final hidden state in bf16 (the final
+    norm is outside this step), logits l[t][v] = sum_i x[t][i] * W[v][i], and
+    the k largest logits are returned in descending order with equal logits to
+    the lower token id (the router's reading).
+
+    float64 decides unless two candidates lie within the float64 error bound,
+    in which case they are recomputed exactly as rationals (as in router_topk).
+    W_bits may be any array-like of uint16 rows (it is read `chunk` rows at a
+    time). Returns (idx int32 [T][k], val float64 [T][k], logits float64
+    [T][V], n_exact).
+    """
+    x = bf16_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    T, H = x.shape
+    V = W_bits.shape[0]
+    if not (1 <= k <= V):
+        raise ValueError("need 1 <= k <= V")
+    L = np.empty((T, V))
+    A = np.empty((T, V))
+    for v0 in range(0, V, chunk):
+        Wc = bf16_to_f64(np.asarray(W_bits[v0:v0 + chunk], dtype=np.uint16))
+        L[:, v0:v0 + Wc.shape[0]] = x @ Wc.T
+        A[:, v0:v0 + Wc.shape[0]] = np.abs(x) @ np.abs(Wc).T
+    u = 2.0 ** -53
+    n = H + 2
+    err = 2.0 * (n * u / (1.0 - n * u)) * A
+    idx = np.zeros((T, k), dtype=np.int32)
+    val = np.zeros((T, k))
+    n_exact = 0
+    ids = np.arange(V)
+    for t in range(T):
+        order = np.lexsort((ids, -L[t]))
+        m = min(k + 1, V)
+        top = order[:m]
+        ambiguous = any(L[t, a_] - L[t, b_] <= err[t, a_] + err[t, b_] for a_, b_ in zip(top[:-1], top[1:]))
+        if ambiguous:
+            n_exact += 1
+            floor = L[t, top[-1]] - err[t, top[-1]]
+            cand = [int(v) for v in np.nonzero(L[t] + err[t] >= floor)[0]]
+            ex = {v: _exact_logit(x[t], bf16_to_f64(np.asarray(W_bits[v], dtype=np.uint16)), None) for v in cand}
+            cand.sort(key=lambda v: (-ex[v], v))
+            rest = [int(v) for v in order[: m + len(cand)] if int(v) not in ex]
+            order = np.array(cand + rest, dtype=np.int64)
+        idx[t] = order[:k]
+        val[t] = L[t, order[:k]]
+    return idx, val, L, n_exact
+
+
+# ----------------------------------------------------------------------------
 # O6 token -> expert grouping
 # ----------------------------------------------------------------------------
 def group_by_expert(idx: np.ndarray, E: int):

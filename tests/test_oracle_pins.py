@@ -262,6 +262,77 @@ def test_router_exact_path_resolves_float64_collision():
     assert idx[0].tolist() == [1, 0]
 
 
+# ------------------------------------------------------------------ LM head
+def test_lm_head_table_size_matches_page():
+    figs = {r[0]: float(r[1]) for r in _read_golden("page_figures.txt")}
+    V, H = int(figs["vocab"]), int(figs["hidden"])
+    table = V * H * 2  # one bf16 table
+    assert table == 622329856
+    # two untied tables plus the 24 full-precision routers are the page's
+    # ~0.64B full-precision parameters at two bytes each (1.27 GB)
+    routers = int(figs["n_layers"]) * int(figs["n_experts"]) * H
+    assert abs(2 * V * H + routers - figs["full_precision_params"]) / figs["full_precision_params"] < 0.01
+    assert abs(2 * (2 * V * H + routers) - figs["embedding_tables_bytes"]) / figs["embedding_tables_bytes"] < 0.01
+    # "about a quarter of the entire file"
+    assert 0.2 < 2 * table / figs["packed_checkpoint_bytes"] < 0.3
+
+
+def _exact_sorted(xb, Wb):
+    xf, Wf = O.bf16_to_f64(xb), O.bf16_to_f64(Wb)
+    out = []
+    for t in range(xf.shape[0]):
+        ex = []
+        for v in range(Wf.shape[0]):
+            acc = Fraction(0)
+            for a, b in zip(xf[t].tolist(), Wf[v].tolist()):
+                acc += Fraction(a) * Fraction(b)
+            ex.append(acc)
+        out.append((ex, sorted(range(Wf.shape[0]), key=lambda v: (-ex[v], v))))
+    return out
+
+
+@pytest.mark.parametrize("V,H,k", [(23, 9, 5), (40, 33, 1), (17, 64, 17)])
+def test_lm_head_brute_force(V, H, k):
+    # exact rational logits by a plain double loop; the oracle's float64 logits
+    # lie within its bound and its ranking is the exact one
+    g = np.random.default_rng(V * 100 + H)
+    xb = O.f32_to_bf16_rne(g.standard_normal((2, H)).astype(np.float32))
+    Wb = O.f32_to_bf16_rne((g.standard_normal((V, H)) * 0.05).astype(np.float32))
+    idx, val, L, _ = O.lm_head_topk(xb, Wb, k)
+    for t, (ex, order) in enumerate(_exact_sorted(xb, Wb)):
+        assert idx[t].tolist() == order[:k]
+        for v in range(V):
+            assert abs(L[t, v] - float(ex[v])) <= 1e-12 * (1.0 + abs(float(ex[v])))
+        assert np.array_equal(val[t], L[t, idx[t]])
+
+
+def test_lm_head_duplicate_rows_and_float64_collision():
+    H = 4
+    x = np.zeros((1, H), np.float32)
+    x[0, 0] = 1.0
+    x[0, 1] = 2.0 ** -60
+    W = np.zeros((5, H), np.float32)
+    W[1, 0] = 1.0            # logit 1
+    W[3, 0] = 1.0            # logit 1 + 2^-60: collides with row 1 in float64
+    W[3, 1] = 1.0
+    W[4] = W[1]              # exact duplicate of row 1
+    W[0, 2] = 1.0            # logit 0
+    xb, Wb = O.f32_to_bf16_rne(x), O.f32_to_bf16_rne(W)
+    idx, _, L, n_exact = O.lm_head_topk(xb, Wb, 3)
+    assert L[0, 1] == L[0, 3] == L[0, 4]
+    assert n_exact == 1
+    assert idx[0].tolist() == [3, 1, 4]
+
+
+def test_lm_head_k1_is_library_argmax():
+    g = np.random.default_rng(5)
+    xb = O.f32_to_bf16_rne(g.standard_normal((3, 128)).astype(np.float32))
+    Wb = O.f32_to_bf16_rne((g.standard_normal((500, 128)) * 0.02).astype(np.float32))
+    idx, _, L, _ = O.lm_head_topk(xb, Wb, 1)
+    ref = O.bf16_to_f64(xb) @ O.bf16_to_f64(Wb).T
+    assert np.array_equal(idx[:, 0], np.argmax(ref, axis=1))
+
+
 # ---------------------------------------------------------------- grouping (O6)
 def test_grouping_matches_stable_argsort():
     g = np.random.default_rng(7)
