@@ -38,7 +38,11 @@ WORKLOADS = {
     # one token at a time through the same 24-layer stack: per-token decode latency
     6: dict(name="moe_stack24_decode_T1_residual", tokens=1, bias=None, layers=24, steps=100, warmup=4, stack=True,
             model_cfg=5),
+    # the model's untied bf16 output head (151,936 x 2048, 622 MB) and its top-16, one token per step
+    7: dict(name="lm_head_topk16_T1", tokens=1, bias=None, layers=1, steps=400, warmup=10, model_cfg=5, lm_head=True),
 }
+LMH_K = 16
+LMH_KERNELS = ("lmh_logits", "lmh_topk", "lmh_merge")
 
 
 # kernels each path launches (names of the C ABI's timing hook)
@@ -156,6 +160,126 @@ def cpu_baseline(cfg: int, wl: dict, n_tok: int | None, budget_s: float = 12.0):
             "host_cpus": threads, "kind": "oracle", "sample": sample}
 
 
+# ------------------------------------------------------------------ LM head
+def cpu_baseline_lm_head(wl: dict, budget_s: float = 12.0):
+    """The oracle's lm_head_topk on this host for successive tokens until
+    budget_s seconds of oracle time; the table is drawn once beforehand
+    (untimed)."""
+    import numpy as np
+
+    import oracle as O
+    import tmoe_inputs as ti
+
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    cfg, V = wl["model_cfg"], ti.VOCAB
+    with concurrent.futures.ThreadPoolExecutor(min(16, threads)) as ex:
+        parts = list(ex.map(lambda v0: ti.lm_head_rows(cfg, v0, min(v0 + 8192, V)), range(0, V, 8192)))
+    Wh = np.concatenate(parts)
+    x = ti.activations(cfg, 64)
+    tokens, timed = 0, 0.0
+    for i in range(64):
+        t0 = time.perf_counter()
+        O.lm_head_topk(x[i:i + 1], Wh, LMH_K)
+        timed += time.perf_counter() - t0
+        tokens += 1
+        if timed >= budget_s:
+            break
+    sample = (f"{tokens} token(s) of the {wl['name']} workload through the oracle's lm_head_topk over the full "
+              f"151,936-token table; {timed:.1f} s of oracle time; the table drawn beforehand, untimed")
+    return {"value": tokens / timed, "unit": "tokens/s", "cores": blas if blas > 1 else 1, "host_cpus": threads,
+            "kind": "oracle", "sample": sample}
+
+
+def main_lm_head(args, wl: dict):
+    import numpy as np
+    import torch
+
+    ensure_built()
+    import ternary_weight_moe_base_amd as tm
+    import tmoe_inputs as ti
+    from ternary_weight_moe_base_amd import synthetic
+
+    K = args.steps if args.steps is not None else wl["steps"]
+    W_ = args.warmup if args.warmup is not None else wl["warmup"]
+    T, V, k = wl["tokens"], ti.VOCAB, LMH_K
+    dev = torch.device("cuda")
+    torch.cuda.init()
+    Wd = synthetic.lm_head_table(wl["model_cfg"])
+    X = synthetic.activations(wl["model_cfg"], 64 * T).view(64, T, H)
+    idx = torch.empty((K + W_, T, k), dtype=torch.int32, device=dev)
+    val = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(tm.lm_head_workspace_bytes(T, V, k), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        tm.lm_head_topk(X[i % 64], Wd, k, idx[i], val, ws)
+
+    for i in range(W_):
+        step(i)
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph.capture_begin()
+            for i in range(W_, W_ + K):
+                step(i)
+            graph.capture_end()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(W_, W_ + K):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    kern = {}
+    for name in LMH_KERNELS:
+        tm.profile_begin(name, K)
+        for i in range(W_, W_ + K):
+            step(i)
+        ms = tm.profile_end(K)
+        if len(ms):
+            kern[name] = ms
+    torch.cuda.synchronize()
+    per_step_us = {n: float(np.mean(v)) * 1e3 for n, v in kern.items()}
+    table_bytes = V * H * 2
+    step_bytes = table_bytes + T * H * 2 + T * k * 8
+    mean_s = float(np.mean(kern["lmh_logits"])) * 1e-3
+    achieved = (table_bytes + T * H * 2) / mean_s / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None, "kernel": "lmh_logits", "mean_launch_us": mean_s * 1e6, "launches": int(len(kern["lmh_logits"])),
+            "algorithmic_bytes_per_launch": float(table_bytes + T * H * 2),
+            "kernels_us_per_step": {n: round(v, 3) for n, v in per_step_us.items()}}
+    out = {
+        "metric": METRIC, "value": T * K / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W_,
+        "ms_per_step": 1e3 * elapsed / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["name"], "tokens_per_step": T, "vocab": V, "hidden": H, "top_k": k,
+                   "table": "bf16 [151936][2048], untied output embedding", "hip_graph": use_graph},
+        "achieved_hbm_gbs": step_bytes * K / elapsed / 1e9,
+        "hbm_frac": step_bytes * K / elapsed / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": float(step_bytes),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline_lm_head(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ workload
 def main():
     args = parse()
@@ -174,6 +298,8 @@ def main():
 
     cfg = args.config
     wl = dict(WORKLOADS[cfg])
+    if wl.get("lm_head"):
+        return main_lm_head(args, wl)
     K = args.steps if args.steps is not None else wl["steps"]
     W_ = args.warmup if args.warmup is not None else wl["warmup"]
     L = args.layers if args.layers is not None else wl["layers"]

@@ -257,6 +257,33 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------------ LM head
+ * Output head over the vocabulary (ai.thesatyajit.com, "The 5.31 GB claim
+ * reconciles, and the leftover is the vocabulary": the 151,936 x 2048 input
+ * and output embeddings are untied and un-quantized; the output table alone
+ * is 622 MB in bf16, the largest per-token byte stream of the model).
+ *   logits[t][v] = sum_i X[t][i] * W[v][i]
+ *   idx[t][0..k)  = the k largest logits, descending, equal logits -> lower v
+ *   val[t][0..k)  = those logits (fp32 of the fp64 value)
+ * Certified like the router: fp64 sums of exact products with a rigorous
+ * error bound; equal fp64 logits of bitwise identical rows are exact ties;
+ * any other top-(k+1) pair closer than the bound sends the token to a
+ * double-double recompute of every token id within the bound of the
+ * (k+1)-th logit. Indices equal those of the exact logits except for logits
+ * closer than ~1e-30 relative.
+ *   X bf16 [T][H]; W bf16 [V][H] (row-major, 16-B aligned); idx int32 [T][k];
+ *   val fp32 [T][k]; logits fp32 [T][V] or NULL;
+ *   n_fixup: int32 device scalar or NULL, incremented by the number of tokens
+ *   ranked by the double-double path (and by 65536 for a token whose
+ *   uncertain set exceeded 256 ids: that token keeps the float64 ranking).
+ * Limits: T in {1, 2, 4} (decode), H in {512, 1024, 2048, 4096},
+ * 1 <= k <= 16, k < V <= 262,144.
+ * ws: tmoe_lm_head_workspace_bytes(T, V, k) bytes (fp64 logits, per-block
+ * bounds, per-chunk candidate lists); no zero-fill needed. */
+size_t tmoe_lm_head_workspace_bytes(int64_t T, int64_t V, int k);
+int tmoe_lm_head_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const uint16_t *W, int64_t V, int k,
+                      int32_t *idx, float *val, float *logits, int32_t *n_fixup, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------ kernel timing
  * Measurement hook. Between tmoe_profile_begin and tmoe_profile_end every
  * launch of one kernel (TMOE_KERNEL_*) carries a HIP start/stop event pair
@@ -279,7 +306,10 @@ enum {
   TMOE_KERNEL_GATEUP = 7,        /* for T <= 16 with the top-k and grouping in its prologue */
   TMOE_KERNEL_DOWN = 9,          /* for T*k <= 32 with the combine fused */
   TMOE_KERNEL_COMBINE = 10,
-  TMOE_KERNEL_LINEAR = 11
+  TMOE_KERNEL_LINEAR = 11,
+  TMOE_KERNEL_LMH_LOGITS = 12, /* LM head: the fp64 logit stream */
+  TMOE_KERNEL_LMH_TOPK = 13,   /* LM head: per-chunk top-(k+1) */
+  TMOE_KERNEL_LMH_MERGE = 14   /* LM head: merge, certification, fallback */
 };
 int tmoe_profile_begin(int kernel, int capacity);
 int tmoe_profile_end(float *ms, int capacity, int *count);

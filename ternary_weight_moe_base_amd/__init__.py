@@ -189,6 +189,21 @@ def router_topk(X, Wr, bias, k: int, idx, w, ws, logits=None, n_fixup=None, stre
            "router_topk")
 
 
+# ------------------------------------------------------------------- LM head
+def lm_head_workspace_bytes(T: int, V: int, k: int) -> int:
+    return _load().tmoe_lm_head_workspace_bytes(T, V, k)
+
+
+def lm_head_topk(X, W, k: int, idx, val, ws, logits=None, n_fixup=None, stream=None) -> None:
+    """Logits of the bf16 output table W [V][H] for X [T][H] (bf16 bit patterns)
+    and the certified top-k token ids / logits."""
+    T, H = X.shape
+    V = W.shape[0]
+    _check(_load().tmoe_lm_head_topk(_stream(stream), _ptr(X), T, H, _ptr(W), V, k, _ptr(idx), _ptr(val),
+                                     _ptr(logits), _ptr(n_fixup), _ptr(ws), ws.numel() * ws.element_size()),
+           "lm_head_topk")
+
+
 # ------------------------------------------------------------------ grouping
 def group_workspace_bytes(T: int, k: int, E: int) -> int:
     return _load().tmoe_group_workspace_bytes(T, k, E)

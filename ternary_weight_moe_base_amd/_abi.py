@@ -76,12 +76,15 @@ SIGNATURES = {
                              c_void_p]),
     "tmoe_moe_workspace_bytes": (c_int, [c_int64, c_void_p, POINTER(c_size_t)]),
     "tmoe_moe_forward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t]),
+    "tmoe_lm_head_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
+    "tmoe_lm_head_topk": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_size_t]),
     "tmoe_profile_begin": (c_int, [c_int, c_int]),
     "tmoe_profile_end": (c_int, [c_void_p, c_int, POINTER(c_int)]),
 }
 
 KERNELS = {"router_logits": 1, "router_topk": 2, "group": 4, "make_tiles": 5, "gateup": 7, "down": 9, "combine": 10,
-           "linear": 11}
+           "linear": 11, "lmh_logits": 12, "lmh_topk": 13, "lmh_merge": 14}
 
 
 def declare(lib) -> None:

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtmoe.so")
-SOURCES = ["host_api.cpp", "quant.hip", "router.hip", "group.hip", "ffn.hip"]
+SOURCES = ["host_api.cpp", "quant.hip", "router.hip", "group.hip", "ffn.hip", "lmhead.hip"]
 ARCH = "gfx950"
 
 

@@ -267,6 +267,33 @@ int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, cons
                        router_ws_carve(ws, T, E));
 }
 
+// ------------------------------------------------------------------- LM head
+size_t tmoe_lm_head_workspace_bytes(int64_t T, int64_t V, int k) {
+  if (T <= 0 || V <= 0 || k <= 0 || V > (int64_t)1 << 31) return 0;
+  return lmh_ws_bytes(T, V, k);
+}
+
+int tmoe_lm_head_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const uint16_t *W, int64_t V, int k,
+                      int32_t *idx, float *val, float *logits, int32_t *n_fixup, void *ws, size_t ws_bytes) {
+  clear_error();
+  REQUIRE(T >= 0 && H > 0 && V > 0 && k >= 1, TMOE_E_ARG, "bad sizes");
+  if (T == 0) return TMOE_OK;
+  REQUIRE(X && W && idx && val, TMOE_E_ARG, "null pointer");
+  REQUIRE(T == 1 || T == 2 || T == 4, TMOE_E_UNSUPPORTED, "lm head: T must be 1, 2 or 4");
+  REQUIRE(H == 512 || H == 1024 || H == 2048 || H == 4096, TMOE_E_UNSUPPORTED,
+          "lm head: hidden must be 512, 1024, 2048 or 4096");
+  REQUIRE(k <= 16, TMOE_E_UNSUPPORTED, "lm head: k <= 16");
+  REQUIRE(k < V, TMOE_E_SHAPE, "lm head: need k < V");
+  REQUIRE(V <= (int64_t)lmh_max_chunks() * lmh_chunk_tokens(), TMOE_E_UNSUPPORTED, "lm head: V <= %lld",
+          (long long)lmh_max_chunks() * lmh_chunk_tokens());
+  REQUIRE(aligned16(X) && aligned16(W) && aligned4(idx) && aligned4(val) && (!logits || aligned4(logits)) &&
+              (!n_fixup || aligned4(n_fixup)),
+          TMOE_E_ALIGN, "misaligned pointer");
+  const size_t need = lmh_ws_bytes(T, V, k);
+  REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes", need);
+  return launch_lm_head((hipStream_t)stream, X, T, H, W, V, k, idx, val, logits, n_fixup, ws);
+}
+
 // ------------------------------------------------------------------ grouping
 size_t tmoe_group_workspace_bytes(int64_t T, int k, int64_t E) {
   if (T < 0 || k <= 0 || E <= 0) return 0;
@@ -443,7 +470,7 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
 
 int tmoe_profile_begin(int kernel, int capacity) {
   clear_error();
-  REQUIRE(kernel >= TMOE_KERNEL_ROUTER_LOGITS && kernel <= TMOE_KERNEL_LINEAR, TMOE_E_ARG, "unknown kernel id %d",
+  REQUIRE(kernel >= TMOE_KERNEL_ROUTER_LOGITS && kernel <= TMOE_KERNEL_LMH_MERGE, TMOE_E_ARG, "unknown kernel id %d",
           kernel);
   REQUIRE(capacity > 0 && capacity <= (1 << 20), TMOE_E_ARG, "capacity out of range");
   REQUIRE(g_prof.kernel == 0, TMOE_E_ARG, "a profiling window is already open");

@@ -183,6 +183,57 @@ __device__ inline void topk_keys(const double v[NPL], int E, uint64_t key[NPL]) 
   for (int j = 0; j < NPL; ++j) key[j] = lane * NPL + j < E ? okey(v[j]) : 0ull;
 }
 
+// Top m of the wavefront's 64 NPL order keys (lane l holds slots NPL l + j):
+// the lane sorts its keys once (equal keys keep the lower j first), then each
+// of the m rounds takes the wave maximum of the lane heads (high words, then
+// low words among the lanes that share the highest high word; equal keys to
+// the lowest lane) and the winner drops its head. Lane r < m receives the key
+// of rank r and its slot. sj must hold 0..NPL-1 on entry.
+template <int NPL>
+__device__ inline void wave_top_u64(uint64_t key[NPL], int sj[NPL], int m, uint64_t &mykey, int &myslot) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int pass = 0; pass < NPL; ++pass)
+#pragma unroll
+    for (int j = pass & 1; j + 1 < NPL; j += 2)
+      if (key[j] < key[j + 1]) {
+        const uint64_t tk = key[j];
+        key[j] = key[j + 1];
+        key[j + 1] = tk;
+        const int tj = sj[j];
+        sj[j] = sj[j + 1];
+        sj[j + 1] = tj;
+      }
+  mykey = 0ull;
+  myslot = 0;
+  for (int r = 0; r < m; ++r) {
+    const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+    const uint32_t mh = wave_max_u32(hi);
+    uint64_t cand = __ballot(hi == mh);
+    uint32_t ml;
+    if (__popcll(cand) == 1) {
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__builtin_ctzll(cand));
+    } else {
+      ml = wave_max_u32(hi == mh ? lo : 0u);
+      cand = __ballot(hi == mh && lo == ml);
+    }
+    const int wl = (int)__builtin_ctzll(cand);
+    const int wj = __builtin_amdgcn_readlane(sj[0], wl);
+    if (lane == wl) {
+#pragma unroll
+      for (int j = 0; j + 1 < NPL; ++j) {
+        key[j] = key[j + 1];
+        sj[j] = sj[j + 1];
+      }
+      key[NPL - 1] = 0ull;
+    }
+    if (lane == r) {
+      mykey = ((uint64_t)mh << 32) | ml;
+      myslot = wl * NPL + wj;
+    }
+  }
+}
+
 // Certified top-k of one token by one wavefront from its order keys. The lane's
 // keys are sorted once; each of the k+1 rounds takes the wave maximum of the
 // lanes' head keys (high words first; low words only among the lanes that

@@ -51,3 +51,15 @@ def activations(cfg: int, tokens: int, hidden: int = ti.HIDDEN, layer: int = 0) 
     """bf16 activations as an int16 device tensor of bit patterns [T][H]."""
     x = ti.activations(cfg, tokens, hidden, layer)
     return torch.from_numpy(x.view(np.int16)).to("cuda")
+
+
+def lm_head_table(cfg: int, vocab: int = ti.VOCAB, hidden: int = ti.HIDDEN) -> torch.Tensor:
+    """The bf16 output embedding [vocab][hidden] on the device, as int16 bit
+    patterns, bit-identical to tmoe_inputs.lm_head_rows (same Philox stream,
+    fp32 scale, nearest-even rounding to bf16)."""
+    w = torch.empty(vocab * hidden, dtype=torch.float32, device="cuda")
+    synth_ih12(w, ti.stream_id(cfg, 0, 0, ti.MAT_LMHEAD), mult=float(ti.LMHEAD_STD))
+    out = w.to(torch.bfloat16).view(torch.int16).view(vocab, hidden)
+    del w
+    return out
+

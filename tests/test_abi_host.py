@@ -124,6 +124,23 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
     assert lib.tmoe_repack_tiled(None, 16, 4, 23, 4, 16) == E.TMOE_E_SHAPE  # ldp < ceil(23/5)
 
 
+def test_lm_head_rejects_bad_arguments_without_gpu():
+    E = tm._abi
+    V, k = 151936, 16
+    ws = tm.lm_head_workspace_bytes(1, V, k)
+    assert ws >= V * 8  # the float64 logits of every token id
+    f = lib.tmoe_lm_head_topk
+    assert f(None, None, 1, 2048, 16, V, k, 16, 16, None, None, 16, ws) == E.TMOE_E_ARG
+    assert f(None, 16, 3, 2048, 16, V, k, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # T = 3
+    assert f(None, 16, 1, 3000, 16, V, k, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # H
+    assert f(None, 16, 1, 2048, 16, V, 17, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # k > 16
+    assert f(None, 16, 1, 2048, 16, 8, 8, 16, 16, None, None, 16, ws) == E.TMOE_E_SHAPE  # k >= V
+    assert f(None, 16, 1, 2048, 16, 1 << 19, k, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # V too large
+    assert f(None, 18, 1, 2048, 16, V, k, 16, 16, None, None, 16, ws) == E.TMOE_E_ALIGN
+    assert f(None, 16, 1, 2048, 16, V, k, 16, 16, None, None, 16, ws - 1) == E.TMOE_E_WORKSPACE
+    assert f(None, 16, 0, 2048, 16, V, k, 16, 16, None, None, None, 0) == E.TMOE_OK  # T = 0
+
+
 def test_layer_struct_validation_without_gpu():
     Ew = tm._abi
     s = tm._abi.MoEWeightsStruct()

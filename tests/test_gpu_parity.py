@@ -599,3 +599,80 @@ def test_stack_decode_one_token(tm, layers):
         g.replay()
         assert np.array_equal(host(Xw), final), rep
         assert np.array_equal(host(idx_g), idx_eager), rep
+
+
+# -------------------------------------------------------------------- LM head
+def _lm_head(tm, xb, Wd, k, with_logits=True):
+    T = xb.shape[0]
+    V = Wd.shape[0]
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    val = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, V), dtype=torch.float32, device="cuda") if with_logits else None
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(tm.lm_head_workspace_bytes(T, V, k), dtype=torch.uint8, device="cuda")
+    tm.lm_head_topk(bf16_dev(xb), Wd, k, idx, val, ws, logits=lg, n_fixup=nf)
+    return host(idx), host(val), (host(lg) if with_logits else None), int(host(nf)[0])
+
+
+@pytest.mark.parametrize("T,H,V,k", [(1, 2048, 3000, 8), (2, 512, 1537, 16), (4, 1024, 2049, 1), (1, 4096, 777, 5),
+                                     (4, 2048, 5000, 16), (1, 512, 17, 16)])
+def test_lm_head_parity(tm, T, H, V, k):
+    say(f"lm head T={T} H={H} V={V} k={k}")
+    g = np.random.default_rng(T * 1000 + V)
+    xb = ti.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    Wb = ti.f32_to_bf16_bits((g.standard_normal((V, H)) * 0.02).astype(np.float32))
+    idx, val, lg, nfix = _lm_head(tm, xb, dev(Wb.view(np.int16)), k)
+    ridx, rval, rL, _ = O.lm_head_topk(xb, Wb, k)
+    assert nfix == 0
+    assert np.array_equal(idx, ridx)
+    assert O.max_normalized_error(val, rval) <= TOL
+    assert O.max_normalized_error(lg, rL) <= TOL
+
+
+def test_lm_head_exact_ties_and_near_ties(tm):
+    # rows 700 and 1200 duplicate row 40 (exact ties: ids ascending, no
+    # recompute); then row 1500 differs from row 40 only where x is 2^-60, so
+    # its logit is larger by far less than a float64 ulp: only the
+    # double-double path ranks it first
+    H, V, k = 512, 2000, 4
+    g = np.random.default_rng(77)
+    x = g.standard_normal((1, H)).astype(np.float32)
+    x[0, 5] = 2.0 ** -60
+    xb = ti.f32_to_bf16_bits(x)
+    W = (g.standard_normal((V, H)) * 0.02).astype(np.float32)
+    W[40] = np.sign(x[0]) * 0.05  # the largest logit by far
+    W[40, 5] = 0.03125
+    Wb = ti.f32_to_bf16_bits(W)
+    Wb[700] = Wb[40]
+    Wb[1200] = Wb[40]
+    idx, val, _, nfix = _lm_head(tm, xb, dev(Wb.view(np.int16)), k, with_logits=False)
+    ridx, _, _, _ = O.lm_head_topk(xb, Wb, k)
+    assert nfix == 0
+    assert np.array_equal(idx, ridx) and idx[0, :3].tolist() == [40, 700, 1200]
+    Wb[1500] = Wb[40]
+    Wb[1500, 5] += 1  # one bf16 ulp more (positive value)
+    idx, val, _, nfix = _lm_head(tm, xb, dev(Wb.view(np.int16)), k, with_logits=False)
+    ridx, _, _, n_exact = O.lm_head_topk(xb, Wb, k)
+    assert n_exact == 1 and nfix == 1
+    assert np.array_equal(idx, ridx) and idx[0].tolist() == [1500, 40, 700, 1200]
+
+
+def test_lm_head_full_vocabulary(tm):
+    # the model's head: 151,936 x 2048 bf16 (622 MB), one token, k = 16; the
+    # device-drawn table equals the host draw on sampled rows, and the top-16
+    # and all logits match the oracle over the whole vocabulary
+    from ternary_weight_moe_base_amd import synthetic
+    cfg, V, H, k = 5, ti.VOCAB, 2048, 16
+    Wd = synthetic.lm_head_table(cfg)
+    for v0 in (0, 77777, V - 3):
+        assert np.array_equal(host(Wd[v0:v0 + 3]).view(np.uint16), ti.lm_head_rows(cfg, v0, v0 + 3))
+    xb = ti.activations(cfg, 1)
+    idx, val, lg, nfix = _lm_head(tm, xb, Wd, k)
+    say("  drawing the table on the host for the oracle")
+    Wh = np.concatenate([ti.lm_head_rows(cfg, v0, min(v0 + 16384, V)) for v0 in range(0, V, 16384)])
+    ridx, rval, rL, _ = O.lm_head_topk(xb, Wh, k)
+    assert nfix == 0
+    assert np.array_equal(idx, ridx)
+    assert O.max_normalized_error(val, rval) <= TOL
+    assert O.max_normalized_error(lg, rL) <= TOL
+    say(f"  top-{k} ids {idx[0].tolist()}")

@@ -41,6 +41,9 @@ TOP_K = 8
 N_LAYERS = 24
 
 MAT_GATE, MAT_UP, MAT_DOWN, MAT_ROUTER = 0, 1, 2, 3
+MAT_LMHEAD = 6
+VOCAB = 151936
+LMHEAD_STD = np.float32(0.02)
 IH12_OFFSET = 393210  # 12 * (2**16 - 1) / 2
 ROUTER_STD = np.float32(0.02)
 
@@ -92,6 +95,14 @@ def router_matrix(cfg: int, layer: int, experts: int = N_EXPERTS, hidden: int = 
     """fp32 router weights [E][H], fp32(0.02) * Irwin-Hall(12)."""
     w = ih12_normal(stream_id(cfg, layer, 1023, MAT_ROUTER), experts * hidden)
     return (w * ROUTER_STD).astype(np.float32).reshape(experts, hidden)
+
+
+def lm_head_rows(cfg: int, v0: int, v1: int, hidden: int = HIDDEN) -> np.ndarray:
+    """Rows v0..v1-1 of the bf16 output embedding, as uint16 bit patterns
+    [v1 - v0][hidden]: bf16 (nearest even) of fp32(0.02) * Irwin-Hall(12),
+    element v * hidden + i drawn from counter v * hidden + i of one stream."""
+    w = ih12_normal(stream_id(cfg, 0, 0, MAT_LMHEAD), (v1 - v0) * hidden, first=v0 * hidden)
+    return f32_to_bf16_bits((w * LMHEAD_STD).astype(np.float32)).reshape(v1 - v0, hidden)
 
 
 def _rng(*words: int) -> np.random.Generator:
