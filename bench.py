@@ -213,7 +213,7 @@ def main_lm_head(args, wl: dict):
     X = synthetic.activations(wl["model_cfg"], 64 * T).view(64, T, H)
     idx = torch.empty((K + W_, T, k), dtype=torch.int32, device=dev)
     val = torch.empty((T, k), dtype=torch.float32, device=dev)
-    ws = torch.empty(tm.lm_head_workspace_bytes(T, V, k), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(tm.lm_head_workspace_bytes(T, V, k), dtype=torch.uint8, device=dev)
 
     def step(i):
         tm.lm_head_topk(X[i % 64], Wd, k, idx[i], val, ws)

@@ -277,9 +277,10 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
  *   ranked by the double-double path (and by 65536 for a token whose
  *   uncertain set exceeded 256 ids: that token keeps the float64 ranking).
  * Limits: T in {1, 2, 4} (decode), H in {512, 1024, 2048, 4096},
- * 1 <= k <= 16, k < V <= 262,144.
+ * 1 <= k <= 16, k < V <= 2^20.
  * ws: tmoe_lm_head_workspace_bytes(T, V, k) bytes (fp64 logits, per-block
- * bounds, per-chunk candidate lists); no zero-fill needed. */
+ * maxima, candidate lists); no zero-fill needed. Calls that share a
+ * workspace must not overlap. */
 size_t tmoe_lm_head_workspace_bytes(int64_t T, int64_t V, int k);
 int tmoe_lm_head_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const uint16_t *W, int64_t V, int k,
                       int32_t *idx, float *val, float *logits, int32_t *n_fixup, void *ws, size_t ws_bytes);

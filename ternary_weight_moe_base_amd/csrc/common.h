@@ -230,8 +230,6 @@ int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t
 
 // LM head (lmhead.hip)
 size_t lmh_ws_bytes(int64_t T, int64_t V, int k);
-int lmh_max_chunks();
-int lmh_chunk_tokens();
 int launch_lm_head(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const uint16_t *W, int64_t V, int k,
                    int32_t *idx, float *val, float *logits, int32_t *n_fixup, void *ws);
 

@@ -17,53 +17,60 @@
 //  - otherwise every token whose float64 logit reaches the (k+1)-th minus 2B
 //    is recomputed in double-double and ranked by that value (ties to the
 //    lower token id).
-// Kernels: lmh_logits (the stream: fp64 logits and per-workgroup bound
-// maxima), lmh_chunk_topk (top-(k+1) of each 512-token chunk, float64 order),
-// lmh_merge (merge of the chunk lists, certification, rare fallback).
+// Kernels: lmh_logits (the stream: fp64 logits, per-workgroup maxima of the
+// logits and of the bound sums), lmh_select (a threshold below the (k+1)-th
+// logit from the per-workgroup maxima, and the ids at or above it),
+// lmh_merge (exact ranking of those candidates, certification, fallbacks).
 #include "route_util.h"
 
 namespace tmoe {
 
-constexpr int kLmhIter = 8;        // 4-value batches per wavefront in lmh_logits
-constexpr int kLmhNpl = 8;         // values per lane in a chunk (512 tokens per chunk)
-constexpr int kLmhChunk = 64 * kLmhNpl;
-constexpr int kLmhMergeNpl = 8;    // chunk lists per lane in the merge (<= 512 chunks)
+constexpr int kLmhGrid = 1024;     // workgroups of lmh_logits: four per CU, all resident at once
+constexpr int kLmhSelTokens = 1024;  // token ids scanned per workgroup of lmh_select
+constexpr int kLmhSelCap = 64;     // candidates one lmh_select workgroup may keep
+constexpr int kLmhCap = 2048;      // candidate ids ranked per token
 constexpr int kLmhFallbackCap = 256;
 
-__host__ __device__ inline int lmh_rows_per_wg(int T) { return 4 * kLmhIter * (4 / T); }
 
 struct LmhWs {
+  int32_t *cnt;    // [T][nsel]: candidates found by each lmh_select workgroup
   double *lg;      // [T][V]
   float *am;       // [T][nblk]: per-workgroup max of sum |x w|
-  uint64_t *ckey;  // [T][nchunks][m]
-  int32_t *cidx;   // [T][nchunks][m]
+  uint64_t *bm;    // [T][nblk]: per-workgroup max order key of the logits
+  uint64_t *ckey;  // [T][nsel][kLmhSelCap]
+  int32_t *cidx;   // [T][nsel][kLmhSelCap]
 };
 
-static int64_t lmh_nblk(int64_t T, int64_t V) { return cdiv(V, lmh_rows_per_wg((int)T)); }
+// workgroups of lmh_logits: one batch of 4 / T rows per wavefront at least
+static int64_t lmh_nblk(int64_t T, int64_t V) {
+  const int64_t nb = cdiv(cdiv(V, 4 / T), 4);
+  return nb < kLmhGrid ? nb : kLmhGrid;
+}
 
-size_t lmh_ws_bytes(int64_t T, int64_t V, int k) {
-  const int64_t nblk = lmh_nblk(T, V), nch = cdiv(V, kLmhChunk), m = k + 1;
+static int64_t lmh_nsel(int64_t V) { return cdiv(V, kLmhSelTokens); }
+
+static size_t lmh_ws_layout(void *ws, int64_t T, int64_t V, LmhWs *w) {
+  const int64_t nblk = lmh_nblk(T, V), nsel = lmh_nsel(V);
+  char *b = (char *)ws;
   size_t o = 0;
+  if (w) w->cnt = (int32_t *)(b + o);
+  o = align_up(o + (size_t)T * nsel * 4, 256);
+  if (w) w->lg = (double *)(b + o);
   o = align_up(o + (size_t)T * V * 8, 256);
+  if (w) w->am = (float *)(b + o);
   o = align_up(o + (size_t)T * nblk * 4, 256);
-  o = align_up(o + (size_t)T * nch * m * 8, 256);
-  o = align_up(o + (size_t)T * nch * m * 4, 256);
+  if (w) w->bm = (uint64_t *)(b + o);
+  o = align_up(o + (size_t)T * nblk * 8, 256);
+  if (w) w->ckey = (uint64_t *)(b + o);
+  o = align_up(o + (size_t)T * nsel * kLmhSelCap * 8, 256);
+  if (w) w->cidx = (int32_t *)(b + o);
+  o = align_up(o + (size_t)T * nsel * kLmhSelCap * 4, 256);
   return o;
 }
 
-static LmhWs lmh_ws_carve(void *ws, int64_t T, int64_t V, int k) {
-  const int64_t nblk = lmh_nblk(T, V), nch = cdiv(V, kLmhChunk), m = k + 1;
-  char *b = (char *)ws;
-  LmhWs w;
-  size_t o = 0;
-  w.lg = (double *)(b + o);
-  o = align_up(o + (size_t)T * V * 8, 256);
-  w.am = (float *)(b + o);
-  o = align_up(o + (size_t)T * nblk * 4, 256);
-  w.ckey = (uint64_t *)(b + o);
-  o = align_up(o + (size_t)T * nch * m * 8, 256);
-  w.cidx = (int32_t *)(b + o);
-  return w;
+size_t lmh_ws_bytes(int64_t T, int64_t V, int k) {
+  (void)k;
+  return lmh_ws_layout(nullptr, T, V, nullptr);
 }
 
 // ------------------------------------------------------------------ logits
@@ -87,14 +94,16 @@ __device__ inline V wave_sum4_transposed(V a0, V a1, V a2, V a3) {
   return k;
 }
 
-// Workgroup = 4 wavefronts; a wavefront takes kLmhIter batches of RB = 4 / T
-// consecutive rows (RB x T = 4 values). Lane l holds the activations
+// Workgroup = 4 wavefronts; the batches of RB = 4 / T consecutive rows (RB x T
+// = 4 values) are split evenly over all wavefronts of the grid, each taking a
+// contiguous run; the grid is sized so that every workgroup is resident at
+// once (no tail of late workgroups). Lane l holds the activations
 // x[t][512 c + 8 l + j] in fp32 and reads, per row, the 16-byte pieces
 // 512 c + 8 l .. +8 (each load instruction of the wavefront is one contiguous
 // 1 KB run of the row).
 template <int T, int NC>
 __global__ __launch_bounds__(256) void lmh_logits_kernel(const uint16_t *X, const uint16_t *W, int64_t V, double *lg,
-                                                         float *logits, float *am) {
+                                                         float *logits, float *am, uint64_t *bm) {
   constexpr int H = 512 * NC, RB = 4 / T;
   static_assert(RB * T == 4, "four (row, token) values per batch");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -111,20 +120,29 @@ __global__ __launch_bounds__(256) void lmh_logits_kernel(const uint16_t *X, cons
         xs[t][c][2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
       }
     }
-  const int64_t rbase = (int64_t)blockIdx.x * lmh_rows_per_wg(T) + (int64_t)wave * kLmhIter * RB;
+  const int64_t nbt = (V + RB - 1) / RB, nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t b0 = gw * nbt / nw, b1 = (gw + 1) * nbt / nw;
   const int q = lane >> 4;         // the value this lane ends with
   const int qr = q / T, qt = q % T;
   float amax = 0.f;
-  for (int it = 0; it < kLmhIter; ++it) {
-    const int64_t r0 = rbase + (int64_t)it * RB;
-    if (r0 >= V) break;
-    uint4 wv[RB][NC];
+  uint64_t kmax = 0ull;
+  // rows past V repeat the last row; their sums are dropped
+  auto load_batch = [&](int64_t r0, uint4 (&wv)[RB][NC]) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      const int64_t v = min(r0 + r, V - 1);  // rows past V repeat the last row; their sums are dropped
+      const int64_t v = min(r0 + r, V - 1);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) wv[r][c] = *reinterpret_cast<const uint4 *>(W + v * H + c * 512 + lane * 8);
+      for (int c = 0; c < NC; ++c) {
+        // the table is read once per call: non-temporal loads keep it from displacing cached data
+        const u32x4 t_ = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(W + v * H + c * 512 + lane * 8));
+        wv[r][c] = make_uint4(t_[0], t_[1], t_[2], t_[3]);
+      }
     }
+  };
+  for (int64_t bb = b0; bb < b1; ++bb) {
+    const int64_t r0 = bb * RB;
+    uint4 wv[RB][NC];
+    load_batch(r0, wv);
     double acc[4];
     float aab[4];
 #pragma unroll
@@ -155,50 +173,102 @@ __global__ __launch_bounds__(256) void lmh_logits_kernel(const uint16_t *X, cons
       lg[(int64_t)qt * V + v] = sum;
       if (logits) logits[(int64_t)qt * V + v] = (float)sum;
       amax = fmaxf(amax, asum);
+      const uint64_t kk = okey(sum);
+      kmax = kk > kmax ? kk : kmax;
     }
   }
-  // per-workgroup maxima of the bound sums, per token
+  // per-workgroup maxima of the bound sums and of the logits, per token
   __shared__ float red[4][4];
-  if ((lane & 15) == 0) red[wave][q] = amax;
+  __shared__ uint64_t redk[4][4];
+  if ((lane & 15) == 0) {
+    red[wave][q] = amax;
+    redk[wave][q] = kmax;
+  }
   __syncthreads();
   if (threadIdx.x < T) {
     float mx = 0.f;
+    uint64_t km = 0ull;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        if (qq % T == (int)threadIdx.x) mx = fmaxf(mx, red[w][qq]);
+        if (qq % T == (int)threadIdx.x) {
+          mx = fmaxf(mx, red[w][qq]);
+          km = redk[w][qq] > km ? redk[w][qq] : km;
+        }
     am[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = mx;
+    bm[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = km;
   }
 }
 
-// -------------------------------------------------------------- chunk top
-// Top m (float64 order, equal values to the lower token id) of each chunk of
-// 64 NPL tokens, one wavefront per chunk; lane l holds tokens
-// chunk base + NPL l + j. Ranks past the chunk's real tokens get key 0, id -1.
-template <int NPL>
-__global__ __launch_bounds__(256) void lmh_chunk_topk_kernel(const double *lg, int64_t V, int nchunks, int m,
-                                                             uint64_t *ckey, int32_t *cidx) {
+// ------------------------------------------------------------------ select
+// Any m = k+1 of the per-workgroup maxima are m distinct logits, so the least
+// of them lower-bounds the (k+1)-th logit. Lane l of wavefront 0 takes the
+// maximum over the workgroups b with b mod 64 = l; tau, the m-th largest of
+// these 64 lane maxima (m <= 64), is then at most the (k+1)-th logit: every
+// id of the top k+1 has an order key >= tau (typically a few more than m ids
+// do). Each workgroup computes the same tau (while its own logits are in
+// flight), scans its 1024 ids and keeps those at or above it (count in cnt,
+// up to kLmhSelCap of them in its own slots).
+__global__ __launch_bounds__(256) void lmh_select_kernel(const double *lg, int64_t V, const uint64_t *bm, int nblk,
+                                                         int m, int32_t *cnt, uint64_t *ckey, int32_t *cidx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.y, c = blockIdx.x * 4 + wave;
-  if (c >= nchunks) return;
-  const int64_t v0 = (int64_t)c * 64 * NPL + lane * NPL;
-  uint64_t key[NPL];
-  int sj[NPL];
+  const int t = blockIdx.y, nsel = gridDim.x;
+  __shared__ uint64_t s_max[256];
+  __shared__ uint64_t s_tau;
+  __shared__ int s_n;
+  // this workgroup's logits first: in flight while tau is formed
+  const int64_t v0 = (int64_t)blockIdx.x * kLmhSelTokens + threadIdx.x;
+  double lv[kLmhSelTokens / 256];
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    key[j] = v0 + j < V ? okey(lg[(int64_t)t * V + v0 + j]) : 0ull;
-    sj[j] = j;
+  for (int j = 0; j < kLmhSelTokens / 256; ++j) {
+    const int64_t v = v0 + 256 * j;
+    lv[j] = v < V ? lg[(int64_t)t * V + v] : -INFINITY;
   }
-  uint64_t mykey;
-  int myslot;
-  wave_top_u64<NPL>(key, sj, m, mykey, myslot);
-  if (lane < m) {
-    const int64_t o = ((int64_t)t * nchunks + c) * m + lane;
-    const int64_t v = (int64_t)c * 64 * NPL + myslot;
-    ckey[o] = mykey;
-    cidx[o] = (mykey != 0ull && v < V) ? (int32_t)v : -1;
+  {
+    uint64_t tk = 0ull;
+    for (int b0 = threadIdx.x; b0 < nblk; b0 += 256 * 4) {
+      uint64_t kb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kb[j] = b0 + 256 * j < nblk ? bm[(int64_t)t * nblk + b0 + 256 * j] : 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tk = kb[j] > tk ? kb[j] : tk;
+    }
+    s_max[threadIdx.x] = tk;
   }
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t lk = 0ull;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) lk = s_max[lane + 64 * w] > lk ? s_max[lane + 64 * w] : lk;
+    uint64_t key[1] = {lk};
+    int sj[1] = {0};
+    uint64_t mykey;
+    int myslot;
+    wave_top_u64<1>(key, sj, m, mykey, myslot);
+    const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mykey >> 32), m - 1);
+    const uint32_t tl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mykey, m - 1);
+    if (lane == 0) s_tau = ((uint64_t)th << 32) | tl;
+  }
+  __syncthreads();
+  const uint64_t tau = s_tau;
+  uint64_t *bk = ckey + ((int64_t)t * nsel + blockIdx.x) * kLmhSelCap;
+  int32_t *bi = cidx + ((int64_t)t * nsel + blockIdx.x) * kLmhSelCap;
+#pragma unroll
+  for (int j = 0; j < kLmhSelTokens / 256; ++j) {
+    const int64_t v = v0 + 256 * j;
+    const uint64_t kv = okey(lv[j]);
+    if (v < V && kv >= tau) {
+      const int slot = atomicAdd(&s_n, 1);
+      if (slot < kLmhSelCap) {
+        bk[slot] = kv;
+        bi[slot] = (int32_t)v;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[(int64_t)t * nsel + blockIdx.x] = s_n;
 }
 
 // ------------------------------------------------------------------- merge
@@ -208,10 +278,11 @@ struct LmhMergeArgs {
   int H;
   const double *lg;
   const float *am;
-  int nblk;
+  int nblk, nsel;
+  const int32_t *cnt;
   const uint64_t *ckey;
   const int32_t *cidx;
-  int nchunks, k;
+  int k;
   int32_t *idx;
   float *val;
   int32_t *n_fixup;
@@ -228,33 +299,55 @@ __device__ inline bool rows_equal(const uint16_t *W, int H, int64_t a, int64_t b
   return __ballot(!eq) == 0ull;
 }
 
-// One workgroup per token: merge of the chunk lists (wavefront 0, lane l owns
-// chunks NPL l + j), certification, and the double-double fallback.
-template <int NPL>
+// (key desc, id asc) order: whether (ka, ia) comes before (kb, ib)
+__device__ inline bool lmh_before(uint64_t ka, int ia, uint64_t kb, int ib) { return ka > kb || (ka == kb && ia < ib); }
+
+// One workgroup per token: the top m = k+1 of the candidates in (key desc,
+// id asc) order by rank counting (or, when the candidate list overflowed, m
+// passes of a workgroup-wide maximum over every id), certification, and the
+// double-double fallback.
 __global__ __launch_bounds__(256) void lmh_merge_kernel(LmhMergeArgs a) {
-  extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x, m = a.k + 1, nc = a.nchunks;
-  uint64_t *skey = reinterpret_cast<uint64_t *>(smem);
-  int32_t *sidx = reinterpret_cast<int32_t *>(smem + (size_t)nc * m * 8);
+  const int t = blockIdx.x, m = a.k + 1;
+  __shared__ uint64_t skey[kLmhCap + 8];
+  __shared__ int32_t sid[kLmhCap + 8];
+  __shared__ uint64_t topk_[64];
+  __shared__ int32_t topi_[64];
   __shared__ float sred[256];
+  __shared__ uint64_t rkey[256];
+  __shared__ int32_t rid[256];
   __shared__ int32_t cand[kLmhFallbackCap];
   __shared__ double dhi[kLmhFallbackCap], dlo[kLmhFallbackCap];
-  __shared__ int s_uncertain, s_cnt;
+  __shared__ int s_uncertain, s_cnt, s_over;
+  __shared__ int s_off[256];
+  __shared__ int s_boff[1024];
+  __shared__ int s_tmp[256];
   __shared__ double s_lo;
 
-  for (int i = threadIdx.x; i < nc * m; i += 256) {
-    skey[i] = a.ckey[(int64_t)t * nc * m + i];
-    sidx[i] = a.cidx[(int64_t)t * nc * m + i];
+  if (threadIdx.x == 0) {
+    s_uncertain = 0;
+    s_cnt = 0;
+    s_over = 0;
+  }
+  __syncthreads();
+  // candidate counts of the select workgroups (nsel <= 1024: up to 4 per thread)
+  int c4[4], mine_n = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = threadIdx.x * 4 + j;
+    c4[j] = b < a.nsel ? a.cnt[(int64_t)t * a.nsel + b] : 0;
   }
   float mx = 0.f;
   for (int i = threadIdx.x; i < a.nblk; i += 256) mx = fmaxf(mx, a.am[(int64_t)t * a.nblk + i]);
   sred[threadIdx.x] = mx;
-  if (threadIdx.x == 0) {
-    s_uncertain = 0;
-    s_cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (c4[j] > kLmhSelCap) s_over = 1;
+    mine_n += min(c4[j], kLmhSelCap);
   }
+  s_off[threadIdx.x] = mine_n;
   __syncthreads();
+  const int n = block_exclusive_scan<256>(s_off, 256, s_tmp);
   for (int s = 128; s >= 1; s >>= 1) {
     if ((int)threadIdx.x < s) sred[threadIdx.x] = fmaxf(sred[threadIdx.x], sred[threadIdx.x + s]);
     __syncthreads();
@@ -262,59 +355,96 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(LmhMergeArgs a) {
   const int depth = a.H / 64 + 8;  // per-lane chain of H / 64 terms, 6 butterfly levels, margin
   const double B = 1.02 * gamma_d(depth) * (double)sred[0];
 
-  uint64_t mykey = 0ull;
-  int myid = -1;
-  if (wave == 0) {
-    int ptr[NPL];
-    uint64_t head[NPL];
+  if (n <= kLmhCap && !s_over) {
+    // per-select-workgroup offsets, then every kept slot copied by its own thread
+    {
+      int o = s_off[threadIdx.x];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int c = lane * NPL + j;
-      ptr[j] = 0;
-      head[j] = c < nc ? skey[c * m] : 0ull;
+      for (int j = 0; j < 4; ++j) {
+        const int b = threadIdx.x * 4 + j;
+        if (b < a.nsel) s_boff[b] = o;
+        o += c4[j];
+      }
     }
-    for (int r = 0; r < m; ++r) {
-      // the lane's best head (lower j on equal keys: lower token ids)
-      uint64_t best = head[0];
-      int bj = 0;
+    __syncthreads();
+    // candidate j: the last select workgroup b whose offset is <= j (binary search), slot j - off[b]
+    for (int j = threadIdx.x; j < n; j += 256) {
+      int lo = 0, hi = a.nsel - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_boff[mid] <= j) lo = mid;
+        else hi = mid - 1;
+      }
+      const int64_t o = ((int64_t)t * a.nsel + lo) * kLmhSelCap + (j - s_boff[lo]);
+      skey[j] = a.ckey[o];
+      sid[j] = a.cidx[o];
+    }
+    // pad to a multiple of 8 with entries that precede no candidate
+    const int n8 = (n + 7) & ~7;
+    if ((int)threadIdx.x < n8 - n) {
+      skey[n + threadIdx.x] = 0ull;
+      sid[n + threadIdx.x] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const uint64_t ki = skey[i];
+      const int ii = sid[i];
+      int rank = 0;
+      for (int j0 = 0; j0 < n8; j0 += 8) {
+        uint64_t kj[8];
+        int ij[8];
 #pragma unroll
-      for (int j = 1; j < NPL; ++j)
-        if (head[j] > best) {
-          best = head[j];
-          bj = j;
+        for (int j = 0; j < 8; ++j) {
+          kj[j] = skey[j0 + j];
+          ij[j] = sid[j0 + j];
         }
-      const uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
-      const uint32_t mh = wave_max_u32(hi);
-      uint64_t cand_l = __ballot(hi == mh);
-      uint32_t ml;
-      if (__popcll(cand_l) == 1) {
-        ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__builtin_ctzll(cand_l));
-      } else {
-        ml = wave_max_u32(hi == mh ? lo : 0u);
-        cand_l = __ballot(hi == mh && lo == ml);
-      }
-      const int wl = (int)__builtin_ctzll(cand_l);
-      int vid = -1;
-      if (lane == wl) {
-        int pj = 0;
 #pragma unroll
-        for (int j = 0; j < NPL; ++j)
-          if (j == bj) pj = ptr[j];
-        const int c = lane * NPL + bj;
-        vid = sidx[c * m + pj];
-#pragma unroll
-        for (int j = 0; j < NPL; ++j)
-          if (j == bj) {
-            ptr[j] = pj + 1;
-            head[j] = pj + 1 < m ? skey[c * m + pj + 1] : 0ull;
-          }
+        for (int j = 0; j < 8; ++j) rank += lmh_before(kj[j], ij[j], ki, ii);
       }
-      vid = __builtin_amdgcn_readlane(vid, wl);
-      if (lane == r) {
-        mykey = ((uint64_t)mh << 32) | ml;
-        myid = vid;
+      if (rank < m) {
+        topk_[rank] = ki;
+        topi_[rank] = ii;
       }
     }
+  } else {
+    // too many ids at or above the threshold to keep:
+    // m passes, each the (key desc, id asc) maximum of every id after the last taken
+    uint64_t lk = ~0ull;
+    int li = -1;
+    for (int r = 0; r < m; ++r) {
+      uint64_t bk = 0ull;
+      int bi = 0x7FFFFFFF;
+      for (int64_t v = threadIdx.x; v < a.V; v += 256) {
+        const uint64_t kv = okey(a.lg[(int64_t)t * a.V + v]);
+        if (lmh_before(lk, li, kv, (int)v) && lmh_before(kv, (int)v, bk, bi)) {
+          bk = kv;
+          bi = (int)v;
+        }
+      }
+      rkey[threadIdx.x] = bk;
+      rid[threadIdx.x] = bi;
+      __syncthreads();
+      for (int s = 128; s >= 1; s >>= 1) {
+        if ((int)threadIdx.x < s && lmh_before(rkey[threadIdx.x + s], rid[threadIdx.x + s], rkey[threadIdx.x], rid[threadIdx.x])) {
+          rkey[threadIdx.x] = rkey[threadIdx.x + s];
+          rid[threadIdx.x] = rid[threadIdx.x + s];
+        }
+        __syncthreads();
+      }
+      lk = rkey[0];
+      li = rid[0];
+      if (threadIdx.x == 0) {
+        topk_[r] = lk;
+        topi_[r] = li;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    const uint64_t mykey = lane < m ? topk_[lane] : 0ull;
+    const int myid = lane < m ? topi_[lane] : -1;
     // certification of the float64 ranking of the top k+1
     const double myv = from_okey(mykey);
     const double nv = __shfl_down(myv, 1, 64);
@@ -322,7 +452,7 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(LmhMergeArgs a) {
     const bool pair = lane + 1 < m;
     const bool sep = pair && myv - nv > 2.0 * B;
     const bool eqv = pair && !sep && myv == nv;
-    bool uncertain = __ballot(pair && !sep && !eqv) != 0ull || __ballot(myid < 0 && lane < m) != 0ull;
+    bool uncertain = __ballot(pair && !sep && !eqv) != 0ull;
     uint64_t ties = __ballot(eqv);
     while (!uncertain && ties) {
       const int l = (int)__builtin_ctzll(ties);
@@ -341,7 +471,6 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(LmhMergeArgs a) {
   }
   __syncthreads();
   if (!s_uncertain) return;
-
   // fallback: every token whose float64 logit reaches the (k+1)-th minus 2B
   const double lo = s_lo;
   for (int64_t v0 = threadIdx.x; v0 < a.V; v0 += 256 * 8) {
@@ -359,19 +488,19 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(LmhMergeArgs a) {
       }
   }
   __syncthreads();
-  const int n = min(s_cnt, kLmhFallbackCap);
+  const int nf = min(s_cnt, kLmhFallbackCap);
   const bool overflow = s_cnt > kLmhFallbackCap;
   // candidates in token-id order (rank sort; ids are distinct)
   int my = 0, rank = 0;
-  if ((int)threadIdx.x < n) {
+  if ((int)threadIdx.x < nf) {
     my = cand[threadIdx.x];
-    for (int i = 0; i < n; ++i) rank += cand[i] < my;
+    for (int i = 0; i < nf; ++i) rank += cand[i] < my;
   }
   __syncthreads();
-  if ((int)threadIdx.x < n) cand[rank] = my;
+  if ((int)threadIdx.x < nf) cand[rank] = my;
   __syncthreads();
   // double-double logits of the candidates (exact fp64 products, lane-strided sums, fixed butterfly)
-  for (int i = wave; i < n; i += 4) {
+  for (int i = wave; i < nf; i += 4) {
     const int64_t row = cand[i];
     double hi = 0.0, lo2 = 0.0;
     for (int kk = lane; kk < a.H; kk += 64)
@@ -392,9 +521,9 @@ __global__ __launch_bounds__(256) void lmh_merge_kernel(LmhMergeArgs a) {
 #pragma unroll
     for (int j = 0; j < kLmhFallbackCap / 64; ++j) {
       const int c = lane + 64 * j;
-      tm.v[j] = c < n ? dhi[c] : -INFINITY;
-      tm.l[j] = c < n ? dlo[c] : 0.0;
-      if (c >= n) tm.taken |= 1u << j;
+      tm.v[j] = c < nf ? dhi[c] : -INFINITY;
+      tm.l[j] = c < nf ? dlo[c] : 0.0;
+      if (c >= nf) tm.taken |= 1u << j;
     }
     double sv, sl, v0;
     int si;
@@ -414,7 +543,7 @@ static int launch_lmh_logits(hipStream_t st, const uint16_t *X, const uint16_t *
   const int64_t nblk = lmh_nblk(T, V);
   if (nblk > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "vocabulary too large");
   TMOE_LAUNCH(TMOE_KERNEL_LMH_LOGITS, (lmh_logits_kernel<T, NC>), dim3((unsigned)nblk), dim3(256), 0, st, X, W, V,
-              w.lg, logits, w.am);
+              w.lg, logits, w.am, w.bm);
   TMOE_LAUNCHED("lmh_logits");
   return TMOE_OK;
 }
@@ -433,7 +562,8 @@ static int launch_lmh_logits_h(hipStream_t st, const uint16_t *X, int H, const u
 
 int launch_lm_head(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const uint16_t *W, int64_t V, int k,
                    int32_t *idx, float *val, float *logits, int32_t *n_fixup, void *ws) {
-  const LmhWs w = lmh_ws_carve(ws, T, V, k);
+  LmhWs w;
+  lmh_ws_layout(ws, T, V, &w);
   int rc;
   switch (T) {
     case 1: rc = launch_lmh_logits_h<1>(st, X, (int)H, W, V, logits, w); break;
@@ -442,10 +572,10 @@ int launch_lm_head(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, cons
     default: return fail(TMOE_E_UNSUPPORTED, "lm head: T must be 1, 2 or 4");
   }
   if (rc) return rc;
-  const int nch = (int)cdiv(V, kLmhChunk), m = k + 1;
-  TMOE_LAUNCH(TMOE_KERNEL_LMH_TOPK, lmh_chunk_topk_kernel<kLmhNpl>, dim3((unsigned)cdiv(nch, 4), (unsigned)T),
-              dim3(256), 0, st, w.lg, V, nch, m, w.ckey, w.cidx);
-  TMOE_LAUNCHED("lmh_chunk_topk");
+  const int nblk = (int)lmh_nblk(T, V), nsel = (int)lmh_nsel(V);
+  TMOE_LAUNCH(TMOE_KERNEL_LMH_TOPK, lmh_select_kernel, dim3((unsigned)nsel, (unsigned)T), dim3(256), 0, st, w.lg, V,
+              w.bm, nblk, k + 1, w.cnt, w.ckey, w.cidx);
+  TMOE_LAUNCHED("lmh_select");
   LmhMergeArgs ma;
   ma.X = X;
   ma.W = W;
@@ -453,23 +583,18 @@ int launch_lm_head(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, cons
   ma.H = (int)H;
   ma.lg = w.lg;
   ma.am = w.am;
-  ma.nblk = (int)lmh_nblk(T, V);
+  ma.nblk = nblk;
+  ma.nsel = nsel;
+  ma.cnt = w.cnt;
   ma.ckey = w.ckey;
   ma.cidx = w.cidx;
-  ma.nchunks = nch;
   ma.k = k;
   ma.idx = idx;
   ma.val = val;
   ma.n_fixup = n_fixup;
-  const size_t lds = (size_t)nch * m * 12;
-  rc = allow_lds<lmh_merge_kernel<kLmhMergeNpl>>(lds + 8192);  // the kernel's static LDS comes on top
-  if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_LMH_MERGE, lmh_merge_kernel<kLmhMergeNpl>, dim3((unsigned)T), dim3(256), lds, st, ma);
+  TMOE_LAUNCH(TMOE_KERNEL_LMH_MERGE, lmh_merge_kernel, dim3((unsigned)T), dim3(256), 0, st, ma);
   TMOE_LAUNCHED("lmh_merge");
   return TMOE_OK;
 }
-
-int lmh_max_chunks() { return 64 * kLmhMergeNpl; }
-int lmh_chunk_tokens() { return kLmhChunk; }
 
 }  // namespace tmoe

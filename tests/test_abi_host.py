@@ -135,7 +135,7 @@ def test_lm_head_rejects_bad_arguments_without_gpu():
     assert f(None, 16, 1, 3000, 16, V, k, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # H
     assert f(None, 16, 1, 2048, 16, V, 17, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # k > 16
     assert f(None, 16, 1, 2048, 16, 8, 8, 16, 16, None, None, 16, ws) == E.TMOE_E_SHAPE  # k >= V
-    assert f(None, 16, 1, 2048, 16, 1 << 19, k, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # V too large
+    assert f(None, 16, 1, 2048, 16, (1 << 20) + 1, k, 16, 16, None, None, 16, ws) == E.TMOE_E_UNSUPPORTED  # V too large
     assert f(None, 18, 1, 2048, 16, V, k, 16, 16, None, None, 16, ws) == E.TMOE_E_ALIGN
     assert f(None, 16, 1, 2048, 16, V, k, 16, 16, None, None, 16, ws - 1) == E.TMOE_E_WORKSPACE
     assert f(None, 16, 0, 2048, 16, V, k, 16, 16, None, None, None, 0) == E.TMOE_OK  # T = 0

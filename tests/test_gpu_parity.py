@@ -609,7 +609,7 @@ def _lm_head(tm, xb, Wd, k, with_logits=True):
     val = torch.empty((T, k), dtype=torch.float32, device="cuda")
     lg = torch.empty((T, V), dtype=torch.float32, device="cuda") if with_logits else None
     nf = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws = torch.empty(tm.lm_head_workspace_bytes(T, V, k), dtype=torch.uint8, device="cuda")
+    ws = ws_bytes(tm.lm_head_workspace_bytes(T, V, k))
     tm.lm_head_topk(bf16_dev(xb), Wd, k, idx, val, ws, logits=lg, n_fixup=nf)
     return host(idx), host(val), (host(lg) if with_logits else None), int(host(nf)[0])
 
