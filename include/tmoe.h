@@ -300,7 +300,7 @@ int tmoe_lm_head_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, con
  * dispatch. Global state: not thread-safe; one
  * profiling window at a time (TMOE_E_ARG otherwise). */
 enum {
-  TMOE_KERNEL_ROUTER_LOGITS = 1, /* fp64 logits (VALU for T <= 16, matrix cores above) */
+  TMOE_KERNEL_ROUTER_LOGITS = 1, /* fp64 logits (VALU for T <= 64, matrix cores above) */
   TMOE_KERNEL_ROUTER_TOPK = 2,   /* certified top-k (with its rare double-double recompute) */
   TMOE_KERNEL_GROUP = 4,         /* the fused grouping kernel (first kernel when T > 256) */
   TMOE_KERNEL_MAKE_TILES = 5,    /* tmoe_expert_ffn only (the layer's grouping writes the tiles) */

@@ -39,27 +39,38 @@ __device__ inline void copy16(int n, Src src, Dst dst, Fix fix = Fix()) {
 }
 
 // Exclusive prefix sum of cnt[0..n) in place by a workgroup of NT threads
-// (n <= 4 * NT); tmp holds NT ints. Returns the total to every thread.
+// (NT a multiple of 64, n <= 4 * NT); tmp holds NT ints. Returns the total to
+// every thread. Each thread sums a run of consecutive entries, the runs are
+// scanned within each wavefront by shuffles and across wavefronts through
+// tmp: three barriers.
 template <int NT>
 __device__ inline int block_exclusive_scan(int *cnt, int n, int *tmp) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int per = (n + NT - 1) / NT;
   const int b0 = threadIdx.x * per;
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (b0 + i < n) local += cnt[b0 + i];
-  tmp[threadIdx.x] = local;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    int v = (int)threadIdx.x >= off ? tmp[threadIdx.x - off] : 0;
-    __syncthreads();
-    tmp[threadIdx.x] += v;
-    __syncthreads();
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  int run = tmp[threadIdx.x] - local;
-  const int total = tmp[NT - 1];
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int tw = tmp[w];
+    before += w < wave ? tw : 0;
+    total += tw;
+  }
+  int run = before + incl - local;
   for (int i = 0; i < per; ++i)
     if (b0 + i < n) {
-      int c = cnt[b0 + i];
+      const int c = cnt[b0 + i];
       cnt[b0 + i] = run;
       run += c;
     }

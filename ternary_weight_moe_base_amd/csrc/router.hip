@@ -19,6 +19,7 @@
 namespace tmoe {
 
 static constexpr int kTokChunkBytes = 65536;  // LDS bytes of bf16 activations per workgroup
+static constexpr int kVectorRouterMaxT = 64;  // up to 64 tokens the VALU kernel beats the fp64 matrix cores
 
 size_t router_ws_bytes(int64_t T, int64_t E) {
   size_t o = 0;
@@ -248,8 +249,9 @@ template <int NC>
 static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
                             int64_t E, const RouterWs &rw, int32_t *n_fixup, int *depth) {
   constexpr int H = NC * 256;
+  // four tokens per workgroup: more workgroups in flight beat reusing a staged router row
   int tchunk = kTokChunkBytes / (H * 2);
-  if (tchunk > 128) tchunk = 128;
+  if (tchunk > 4) tchunk = 4;
   if (tchunk > T) tchunk = (int)T;
   dim3 grid((unsigned)cdiv(E, 4), (unsigned)cdiv(T, tchunk));
   size_t lds = (size_t)tchunk * H * 2;
@@ -265,7 +267,7 @@ static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
                             int64_t E, int k, int32_t *idx, float *w, int32_t *n_fixup, const RouterWs &rw) {
   constexpr int H = NC * 256;
   int depth;
-  if (T <= kDecodeMaxT) {
+  if (T <= kVectorRouterMaxT) {
     int rc = launch_logits_nc<NC>(st, X, T, Wr, bias, E, rw, n_fixup, &depth);
     if (rc) return rc;
   } else {
