@@ -250,9 +250,9 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 /* The layer: router -> top-k -> grouping -> expert FFN -> combine.
  * X bf16 [T][H]; Y fp32 [T][H] (may be NULL if opt->resid_out is set).
  * opt may be NULL (clamp 7, no optional outputs).
- * Kernels: for T <= 16 (decode) three: fp64 router logits; gate/up whose
+ * Kernels: for T <= 3 (decode) three: fp64 router logits; gate/up whose
  * prologue certifies the top-k and groups the pairs; down with the combine
- * (and residual) fused. For T > 16: router logits, certified top-k, fix-up,
+ * (and residual) fused. For T > 3: router logits, certified top-k, fix-up,
  * grouping, work tiles, gate/up, down, combine. */
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
@@ -304,7 +304,7 @@ enum {
   TMOE_KERNEL_ROUTER_TOPK = 2,   /* certified top-k (with its rare double-double recompute) */
   TMOE_KERNEL_GROUP = 4,         /* the fused grouping kernel (first kernel when T > 256) */
   TMOE_KERNEL_MAKE_TILES = 5,    /* tmoe_expert_ffn only (the layer's grouping writes the tiles) */
-  TMOE_KERNEL_GATEUP = 7,        /* for T <= 16 with the top-k and grouping in its prologue */
+  TMOE_KERNEL_GATEUP = 7,        /* for T <= 3 with the top-k and grouping in its prologue */
   TMOE_KERNEL_DOWN = 9,          /* for T*k <= 32 with the combine fused */
   TMOE_KERNEL_COMBINE = 10,
   TMOE_KERNEL_LINEAR = 11,

@@ -170,6 +170,8 @@ int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H
                          int64_t E, const RouterWs &rw, int *depth);
 // Decode path (T <= kDecodeMaxT): every (token, slot) pair of an expert fits one work tile.
 constexpr int kDecodeMaxT = 16;
+// Token counts that take the three-kernel decode path in the layer call.
+constexpr int kDecodePathMaxT = 3;  // measured: from 4 tokens on the batched path is faster
 
 struct GroupWs {
   int32_t *bcount;  // [nb][E]

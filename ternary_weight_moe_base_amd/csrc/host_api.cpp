@@ -400,7 +400,7 @@ static LayerWs layer_ws(int64_t T, const tmoe_moe_weights *W) {
   L.off_st = take(P * 4);
   L.off_ss = take(P * 4);
   // expert outputs; the decode path with few pairs fuses the combine and needs none
-  L.off_O = take(T <= kDecodeMaxT && P <= kDcMaxPairs ? 0 : (size_t)P * H * 4);
+  L.off_O = take(T <= kDecodePathMaxT && P <= kDcMaxPairs ? 0 : (size_t)P * H * 4);
   L.total = o;
   return L;
 }
@@ -448,7 +448,7 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   float *O = (float *)(base + L.off_O);
   const RouterWs rw = router_ws_carve(base + L.off_router, T, E);
   const FfnWs fw = ffn_ws_carve(base + L.off_ffn, T, k, E, H, W->inter);
-  if (T <= kDecodeMaxT) {
+  if (T <= kDecodePathMaxT) {
     // logits; gate/up with the certified top-k and grouping in its prologue; down + combine
     int depth = 0;
     rc = launch_router_logits(st, X, T, H, W->router_w, W->router_bias, E, rw, &depth);

@@ -377,10 +377,12 @@ def test_layer_parity(tm, layers, cfg, T, bias_kind, clamp):
         assert O.max_normalized_error(host(Y2), got["Y"]) <= 1e-6
 
 
-@pytest.mark.parametrize("E,k,T", [(8, 8, 3), (8, 8, 6), (8, 2, 16), (16, 4, 9), (16, 4, 17)])
+@pytest.mark.parametrize("E,k,T", [(8, 8, 3), (8, 8, 6), (8, 2, 16), (16, 4, 9), (16, 4, 17), (16, 12, 3),
+                                   (32, 16, 2)])
 def test_layer_few_experts(tm, E, k, T):
-    """Decode-path edge cases: more (token, slot) pairs than experts, every
-    expert hit, up to 16 pairs per tile, the fused and the separate combine."""
+    """Edge cases of both paths: more (token, slot) pairs than experts, every
+    expert hit, up to 16 pairs per tile; on the decode path (T <= 3) the fused
+    combine (T k <= 32) and the separate one (T k > 32)."""
     from ternary_weight_moe_base_amd import synthetic
     say(f"layer E={E} k={k} T={T}")
     cfg = 2
