@@ -1,4 +1,5 @@
-"""Builds libtmoe.so (host C++ + HIP kernels for gfx950) in the package directory.
+"""Builds libtmoe.so (host C++ + HIP kernels for gfx950) and the native driver
+tmoe_run (linked against it) in the package directory.
 
     python -m ternary_weight_moe_base_amd.build
 """
@@ -16,6 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtmoe.so")
+RUNNER = os.path.join(HERE, "tmoe_run")
 SOURCES = ["host_api.cpp", "quant.hip", "router.hip", "group.hip", "ffn.hip", "lmhead.hip"]
 ARCH = "gfx950"
 
@@ -59,8 +61,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = RUNNER + ".tmp"
+    cmd = [hipcc(), *_flags(), os.path.join(CSRC, "tmoe_run.hip"), "-o", tmp, "-L", HERE, "-ltmoe",
+           "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"runner build failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, RUNNER)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {RUNNER}")
     return LIB
 
 

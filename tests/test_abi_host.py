@@ -165,3 +165,16 @@ def test_layer_struct_validation_without_gpu():
     s.reserved = 0
     assert lib.tmoe_moe_forward(None, ctypes.byref(s), None, 4, None, None, None, 0) == Ew.TMOE_E_ARG
     assert lib.tmoe_moe_forward(None, ctypes.byref(s), None, 0, None, None, None, 0) == Ew.TMOE_OK
+
+
+def test_native_driver_rejects_bad_arguments_without_gpu():
+    """The native driver (built next to the library) parses and checks its
+    arguments before it touches HIP, so this runs on a machine with no GPU."""
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(tm.__file__), "tmoe_run")
+    assert os.access(exe, os.X_OK), "tmoe_run is built by ternary_weight_moe_base_amd.build"
+    for args, msg in ((["layer", "--tokens", "0"], "out of range"), (["layer", "--bogus", "1"], "unknown option"),
+                      (["layer", "--steps"], "missing value"), (["layer", "--layers", "65"], "out of range")):
+        r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=60)
+        assert r.returncode == 1 and msg in r.stderr, (args, r.returncode, r.stderr)
