@@ -23,6 +23,7 @@ import time
 METRIC = "ternary MoE layer tokens/s (decode & prefill); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA
+PCIE_PEAK_GBS = 64.0  # host link, PCIe 5.0 x16, one direction
 FP64_PEAK_TFLOPS = 78.6  # fp64 vector / matrix
 H, I, E, K_TOP = 2048, 512, 256, 8
 PACKED_GU = I * ((H + 4) // 5)  # bytes of one gate or up matrix
@@ -38,6 +39,9 @@ WORKLOADS = {
     # one token at a time through the same 24-layer stack: per-token decode latency
     6: dict(name="moe_stack24_decode_T1_residual", tokens=1, bias=None, layers=24, steps=100, warmup=4, stack=True,
             model_cfg=5),
+    # config 6 with every layer's experts in pinned host memory, read over PCIe on demand
+    8: dict(name="moe_stack24_decode_T1_host_experts", tokens=1, bias=None, layers=24, steps=40, warmup=2, stack=True,
+            model_cfg=5, host_experts=True),
     # the model's untied bf16 output head (151,936 x 2048, 622 MB) and its top-16, one token per step
     7: dict(name="lm_head_topk16_T1", tokens=1, bias=None, layers=1, steps=400, warmup=10, model_cfg=5, lm_head=True),
 }
@@ -46,7 +50,7 @@ LMH_KERNELS = ("lmh_logits", "lmh_topk", "lmh_merge")
 
 
 # kernels each path launches (names of the C ABI's timing hook)
-DECODE_KERNELS = ("router_logits", "gateup", "down")  # T <= 16 with few pairs: down also combines
+DECODE_KERNELS = ("router_logits", "gateup", "down")  # T <= 3: gate/up routes, down also combines
 BATCH_KERNELS = ("router_logits", "router_topk", "group", "gateup", "down", "combine")
 
 
@@ -77,7 +81,11 @@ def roofline(name, ms, n_hit, T, cfg, bias):
     else:  # top-k, grouping, tiles: index arrays only
         b = np.full(len(n_hit), T * K_TOP * 4 * 4)
     mean_b = float(np.mean(b))
-    if cfg == 4 and flops is not None:
+    if WORKLOADS[cfg].get("host_experts") and name in ("gateup", "down"):
+        achieved = mean_b / mean_s / 1e9  # the expert bytes cross the host link
+        r = {"bound": "pcie", "achieved": achieved, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+             "frac": achieved / PCIE_PEAK_GBS, "traffic": None}
+    elif cfg == 4 and flops is not None:
         achieved = flops / mean_s / 1e12
         r = {"bound": "alu" if name == "router_logits" else "mfma", "achieved": achieved, "peak": fpeak, "unit": "TFLOP/s", "frac": achieved / fpeak,
              "traffic": None, "algorithmic_flops_per_launch": flops}
@@ -312,6 +320,10 @@ def main():
     t0 = time.perf_counter()
     layers = [synthetic.build_layer(mcfg, l, wl["bias"]) for l in range(L)]
     torch.cuda.synchronize()
+    if wl.get("host_experts"):  # move each layer's experts to pinned host memory, free the device copies
+        for l in range(L):
+            layers[l] = tm.experts_on_host(layers[l])
+        torch.cuda.empty_cache()
     log(f"built {L} layers in {time.perf_counter() - t0:.1f} s")
 
     ws = torch.zeros(tm.moe_workspace_bytes(T, layers[0]), dtype=torch.uint8, device=dev)
@@ -320,7 +332,7 @@ def main():
     if cfg == 5:
         X = synthetic.activations(mcfg, T)
         idx_buf = torch.empty((n_steps * L, T, K_TOP), dtype=torch.int32, device=dev)
-    elif cfg == 6:
+    elif cfg in (6, 8):
         X = synthetic.activations(mcfg, n_steps).view(n_steps, 1, H)  # token i = row i of the stack batch
         Xw = torch.empty((1, H), dtype=X.dtype, device=dev)  # the token's residual stream
         idx_buf = torch.empty((n_steps * L, T, K_TOP), dtype=torch.int32, device=dev)
@@ -333,7 +345,7 @@ def main():
         if cfg == 5:
             for l in range(L):
                 tm.moe_forward(layers[l], X, None, ws, idx=idx_buf[i * L + l], resid_out=X)
-        elif cfg == 6:
+        elif cfg in (6, 8):
             for l in range(L):
                 tm.moe_forward(layers[l], X[i] if l == 0 else Xw, None, ws, idx=idx_buf[i * L + l], resid_out=Xw)
         else:
@@ -373,7 +385,7 @@ def main():
     # kernel at a time carrying start/stop events recorded by its own dispatch
     # on the stream it runs on.
     kern = {}
-    for name in (DECODE_KERNELS if T <= 16 else BATCH_KERNELS):
+    for name in (DECODE_KERNELS if T <= 3 else BATCH_KERNELS):
         tm.profile_begin(name, prof_cap)
         for i in range(W_, W_ + K):
             step(i)
@@ -420,7 +432,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["name"], "tokens_per_step": T, "layers_per_step": L if stack else 1,
                    "distinct_layers": L, "hidden": H, "experts": E, "top_k": K_TOP, "moe_intermediate": I,
-                   "weights": "ternary, 5 trits/byte, fp32 row scales", "hip_graph": use_graph},
+                   "weights": "ternary, 5 trits/byte, fp32 row scales", "hip_graph": use_graph,
+                   "expert_memory": "pinned host, read over PCIe" if wl.get("host_experts") else "hbm"},
         "achieved_hbm_gbs": hbm_gbs,
         "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": float(np.mean(step_bytes)) * (L if stack else 1),

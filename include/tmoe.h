@@ -258,6 +258,27 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
 
+/* --------------------------------------------------- host-resident experts
+ * Page-locked host memory the GPU reads in place over PCIe. Expert weights
+ * placed here (packed matrices and row scales; the router stays in HBM) are
+ * fetched on demand by the layer's own kernels: a call moves only the bytes
+ * of the experts its tokens select, and every step still runs on the GPU.
+ * This is the MI355X form of keeping the experts off the device and streaming
+ * the selected ones per layer (taozi.news, "Maple Preview 接入 Mference":
+ * Mference, a turbo-fieldfare fork, leaves the experts on SSD and reads them
+ * on demand). Fill the buffer, then pass `*device` addresses in
+ * tmoe_moe_weights exactly as device memory; strides and layout are unchanged.
+ *   bytes > 0; *host: CPU address of the buffer (write it before the first
+ *   call that reads it, e.g. with hipMemcpy); *device: the address kernels use.
+ * The memory is mapped and non-coherent (the GPU may cache what it reads), so
+ * it must not change while any call that reads it may be in flight.
+ * Errors: TMOE_E_ARG (zero size or null outputs), TMOE_E_HIP (allocation or
+ * mapping failed; nothing is left allocated). tmoe_host_free releases a buffer
+ * from tmoe_host_alloc (host address; NULL is a no-op); the device must not
+ * be reading it. */
+int tmoe_host_alloc(size_t bytes, void **host, void **device);
+int tmoe_host_free(void *host);
+
 /* ------------------------------------------------------------------ LM head
  * Output head over the vocabulary (ai.thesatyajit.com, "The 5.31 GB claim
  * reconciles, and the leftover is the vocabulary": the 151,936 x 2048 input

@@ -245,6 +245,60 @@ class MoEWeights:
         return ctypes.byref(self.struct)
 
 
+class HostBuffer:
+    """Page-locked host memory that kernels read in place over PCIe
+    (tmoe_host_alloc): `host` is its CPU address, `device` the address kernels
+    use. Freed when the object is collected."""
+
+    def __init__(self, nbytes: int):
+        lib = _load()
+        h, d = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib.tmoe_host_alloc(nbytes, ctypes.byref(h), ctypes.byref(d)), "host_alloc")
+        self._free = lib.tmoe_host_free
+        self.nbytes, self.host, self.device = int(nbytes), h.value, d.value
+
+    def view(self, offset: int, nbytes: int):
+        """A CPU uint8 tensor over bytes [offset, offset + nbytes) of the buffer."""
+        import torch
+
+        if offset < 0 or nbytes < 0 or offset + nbytes > self.nbytes:
+            raise ValueError("view outside the host buffer")
+        arr = (ctypes.c_uint8 * nbytes).from_address(self.host + offset)
+        return torch.frombuffer(arr, dtype=torch.uint8)
+
+    def __del__(self):
+        if getattr(self, "host", None):
+            self._free(self.host)
+            self.host = None
+
+
+def experts_on_host(W: MoEWeights) -> MoEWeights:
+    """The same layer with its experts (packed gate/up/down and their row
+    scales) copied into one pinned host buffer that the kernels read over PCIe
+    on demand; the router stays in device memory. Results are bit-identical to
+    W's: the same kernels run, only the experts' address space differs."""
+    import torch
+
+    router_w, router_bias, gate_p, up_p, down_p, gate_s, up_s, down_s = W.tensors
+    parts = (gate_p, up_p, down_p, gate_s, up_s, down_s)
+    offs, total = [], 0
+    for t in parts:
+        offs.append(total)
+        total += (t.numel() * t.element_size() + 255) // 256 * 256
+    buf = HostBuffer(total)
+    for t, o in zip(parts, offs):
+        buf.view(o, t.numel() * t.element_size()).copy_(t.contiguous().view(-1).view(torch.uint8))
+    out = MoEWeights.__new__(MoEWeights)
+    out.tensors = (router_w, router_bias)
+    out.host_buffer = buf
+    out.hidden, out.inter, out.n_experts, out.top_k = W.hidden, W.inter, W.n_experts, W.top_k
+    s = _abi.MoEWeightsStruct()
+    ctypes.memmove(ctypes.byref(s), ctypes.byref(W.struct), ctypes.sizeof(s))
+    s.gate_p, s.up_p, s.down_p, s.gate_s, s.up_s, s.down_s = (buf.device + o for o in offs)
+    out.struct = s
+    return out
+
+
 def ffn_workspace_bytes(T: int, W: MoEWeights) -> int:
     return _load().tmoe_ffn_workspace_bytes(T, W.ref)
 

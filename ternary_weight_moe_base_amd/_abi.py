@@ -76,6 +76,8 @@ SIGNATURES = {
                              c_void_p]),
     "tmoe_moe_workspace_bytes": (c_int, [c_int64, c_void_p, POINTER(c_size_t)]),
     "tmoe_moe_forward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t]),
+    "tmoe_host_alloc": (c_int, [c_size_t, POINTER(c_void_p), POINTER(c_void_p)]),
+    "tmoe_host_free": (c_int, [c_void_p]),
     "tmoe_lm_head_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
     "tmoe_lm_head_topk": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t]),

@@ -267,6 +267,32 @@ int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, cons
                        router_ws_carve(ws, T, E));
 }
 
+// ------------------------------------------------------ host-resident experts
+int tmoe_host_alloc(size_t bytes, void **host, void **device) {
+  clear_error();
+  REQUIRE(bytes > 0 && host && device, TMOE_E_ARG, "need bytes > 0 and both outputs");
+  *host = *device = nullptr;
+  void *h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocNonCoherent);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+  void *d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess || !d) {
+    (void)hipHostFree(h);
+    return hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "hipHostGetDevicePointer");
+  }
+  *host = h;
+  *device = d;
+  return TMOE_OK;
+}
+
+int tmoe_host_free(void *host) {
+  clear_error();
+  if (!host) return TMOE_OK;
+  hipError_t e = hipHostFree(host);
+  return e == hipSuccess ? TMOE_OK : hip_fail(e, "hipHostFree");
+}
+
 // ------------------------------------------------------------------- LM head
 size_t tmoe_lm_head_workspace_bytes(int64_t T, int64_t V, int k) {
   if (T <= 0 || V <= 0 || k <= 0 || V > (int64_t)1 << 31) return 0;

@@ -4,19 +4,21 @@
 // weight generator, device ternarization and packing, tiled repacking), then
 // runs one of three workloads on one stream and prints its timing:
 //
-//   tmoe_run layer  [--tokens T] [--layers L] [--steps N] [--warmup W] [--cfg C]
+//   tmoe_run layer  [--tokens T] [--layers L] [--steps N] [--warmup W] [--cfg C] [--host-experts 1]
 //       tmoe_moe_forward over T tokens; step i runs layer i % L, so the packed
 //       experts of consecutive steps are distinct HBM data. Weights are bit-
 //       identical to those the Python package draws for the same cfg (same
 //       Philox streams and key); activations come from the same generator on
 //       a stream of their own (N(0,1) in the Irwin-Hall(12) approximation,
-//       rounded to bf16).
+//       rounded to bf16). --host-experts 1 moves every layer's experts to
+//       pinned host memory (tmoe_host_alloc) that the kernels read over PCIe.
 //   tmoe_run lmhead [--tokens T] [--steps N] [--warmup W] [--vocab V] [--topk k]
 //       tmoe_lm_head_topk over a [V][2048] bf16 table (fp32(0.02) * IH12,
 //       rounded to bf16 on the device).
-//   tmoe_run copy   [--mib M] [--steps N]
+//   tmoe_run copy   [--mib M] [--steps N] [--host-experts 1]
 //       a plain 16-byte-per-lane device copy of M MiB: the known-size kernel
-//       that calibrates hardware byte counters.
+//       that calibrates hardware byte counters; with --host-experts 1 the
+//       source is pinned host memory (the host link's read rate).
 //
 // Model shape: hidden 2048, 256 experts, top-8, moe_intermediate 512 (the
 // Maple-Preview configuration as the jj-blog architecture section and
@@ -87,7 +89,7 @@ __global__ void to_bf16_kernel(const float *__restrict__ src, uint16_t *__restri
 struct Args {
   std::string mode = "layer";
   int64_t tokens = 1;
-  int layers = 24, steps = 240, warmup = 8, cfg = 2, topk = 16;
+  int layers = 24, steps = 240, warmup = 8, cfg = 2, topk = 16, host = 0;
   int64_t vocab = 151936, mib = 1024;
 };
 
@@ -110,6 +112,7 @@ Args parse(int argc, char **argv) {
     else if (k == "--vocab") a.vocab = v;
     else if (k == "--topk") a.topk = (int)v;
     else if (k == "--mib") a.mib = v;
+    else if (k == "--host-experts") a.host = (int)v;
     else {
       std::fprintf(stderr, "unknown option %s\n", k.c_str());
       std::exit(1);
@@ -174,6 +177,29 @@ int run_layer(const Args &a, hipStream_t st) {
     }
     CHECK_TMOE(tmoe_synth_ih12(st, kKey, 0, stream_id(a.cfg, l, 1023, kMatRouter), 0, kE * kH, 0.02f, rw));
     W[l] = tmoe_moe_weights{kH, kI, kE, kTopK, 0, rw, nullptr, gp, up, dp, sgu, sd, gs, us, ds};
+    if (a.host) {  // experts to pinned host memory: [gate | up | down | gate_s | up_s | down_s]
+      const int64_t sz[6] = {kE * sgu, kE * sgu, kE * sd, 4 * kE * kI, 4 * kE * kI, 4 * kE * kH};
+      void *src[6] = {gp, up, dp, gs, us, ds};
+      int64_t total = 0;
+      for (int64_t b : sz) total += b;
+      void *h = nullptr, *d = nullptr;
+      CHECK_TMOE(tmoe_host_alloc((size_t)total, &h, &d));
+      CHECK_HIP(hipStreamSynchronize(st));
+      int64_t off = 0;
+      const void *dst[6];
+      for (int i = 0; i < 6; ++i) {
+        CHECK_HIP(hipMemcpy(static_cast<char *>(h) + off, src[i], sz[i], hipMemcpyDeviceToHost));
+        CHECK_HIP(hipFree(src[i]));
+        dst[i] = static_cast<char *>(d) + off;
+        off += sz[i];
+      }
+      W[l].gate_p = static_cast<const uint8_t *>(dst[0]);
+      W[l].up_p = static_cast<const uint8_t *>(dst[1]);
+      W[l].down_p = static_cast<const uint8_t *>(dst[2]);
+      W[l].gate_s = static_cast<const float *>(dst[3]);
+      W[l].up_s = static_cast<const float *>(dst[4]);
+      W[l].down_s = static_cast<const float *>(dst[5]);
+    }
   }
   CHECK_HIP(hipStreamSynchronize(st));
   uint16_t *X = dalloc<uint16_t>(a.tokens * kH);
@@ -186,8 +212,8 @@ int run_layer(const Args &a, hipStream_t st) {
   const double us = time_loop(st, a.warmup, a.steps, [&](int i) {
     CHECK_TMOE(tmoe_moe_forward(st, &W[i % a.layers], X, a.tokens, Y, nullptr, ws, wsb));
   });
-  std::printf("layer: tokens %lld, %d distinct layers, %d steps: %.2f us/step, %.0f tokens/s\n", (long long)a.tokens,
-              a.layers, a.steps, us, a.tokens * 1e6 / us);
+  std::printf("layer: tokens %lld, %d distinct layers, experts in %s, %d steps: %.2f us/step, %.0f tokens/s\n",
+              (long long)a.tokens, a.layers, a.host ? "pinned host memory" : "HBM", a.steps, us, a.tokens * 1e6 / us);
   return 0;
 }
 
@@ -214,14 +240,22 @@ int run_lmhead(const Args &a, hipStream_t st) {
 
 int run_copy(const Args &a, hipStream_t st) {
   const int64_t bytes = a.mib << 20, n = bytes / 16;
-  uint4 *src = dalloc<uint4>(n), *dst = dalloc<uint4>(n);
-  CHECK_HIP(hipMemsetAsync(src, 1, bytes, st));
+  uint4 *src = nullptr, *dst = dalloc<uint4>(n);
+  if (a.host) {
+    void *h = nullptr, *d = nullptr;
+    CHECK_TMOE(tmoe_host_alloc((size_t)bytes, &h, &d));
+    std::memset(h, 1, bytes);
+    src = static_cast<uint4 *>(d);
+  } else {
+    src = dalloc<uint4>(n);
+    CHECK_HIP(hipMemsetAsync(src, 1, bytes, st));
+  }
   const double us = time_loop(st, 1, a.steps, [&](int) {
     copy16_kernel<<<4096, 256, 0, st>>>(src, dst, n);
     CHECK_HIP(hipGetLastError());
   });
-  std::printf("copy: %lld bytes read and written per launch, %d launches: %.2f us, %.1f GB/s (read + write)\n",
-              (long long)bytes, a.steps, us, 2e-3 * bytes / us);
+  std::printf("copy: %lld bytes read (from %s) and written per launch, %d launches: %.2f us, %.1f GB/s read\n",
+              (long long)bytes, a.host ? "pinned host memory" : "HBM", a.steps, us, 1e-3 * bytes / us);
   return 0;
 }
 

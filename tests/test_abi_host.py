@@ -178,3 +178,11 @@ def test_native_driver_rejects_bad_arguments_without_gpu():
                       (["layer", "--steps"], "missing value"), (["layer", "--layers", "65"], "out of range")):
         r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=60)
         assert r.returncode == 1 and msg in r.stderr, (args, r.returncode, r.stderr)
+
+
+def test_host_alloc_rejects_bad_arguments_without_gpu():
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.tmoe_host_alloc(0, ctypes.byref(h), ctypes.byref(d)) == -1  # TMOE_E_ARG
+    assert lib.tmoe_host_alloc(64, None, ctypes.byref(d)) == -1
+    assert lib.tmoe_host_alloc(64, ctypes.byref(h), None) == -1
+    assert lib.tmoe_host_free(None) == 0

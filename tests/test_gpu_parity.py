@@ -603,6 +603,45 @@ def test_stack_decode_one_token(tm, layers):
         assert np.array_equal(host(idx_g), idx_eager), rep
 
 
+@pytest.mark.parametrize("cfg,T,bias_kind", [(2, 1, None), (2, 3, None), (3, 64, "zipf")])
+def test_layer_experts_on_host(tm, layers, cfg, T, bias_kind):
+    """Experts in pinned host memory that the kernels read over PCIe (the
+    streaming variant): the oracle's top-8 and Y, and the device-resident
+    layer's result bit for bit (the same kernels run on the same bytes);
+    for one token, a captured graph replays it identically."""
+    say(f"layer with host-resident experts cfg={cfg} T={T}")
+    W = layers(cfg, 0, bias_kind)
+    Wh = tm.experts_on_host(W)
+    xb = ti.activations(cfg, T)
+    got = _run_layer(tm, Wh, xb)
+    on_dev = _run_layer(tm, W, xb)
+    for key in ("Y", "idx", "w", "pos"):
+        assert np.array_equal(got[key], on_dev[key]), key
+    ref = O.moe_layer(xb, ti.router_matrix(cfg, 0), ti.router_bias(cfg, bias_kind),
+                      lambda e: _raw_expert(cfg, 0, e), k=8)
+    assert np.array_equal(got["idx"], ref["idx"])
+    err = O.max_normalized_error(got["Y"], ref["Y"])
+    say(f"  Y max normalized error {err:.2e}")
+    assert err <= TOL
+    if T == 1:
+        X = bf16_dev(xb)
+        Y = torch.zeros((1, 2048), dtype=torch.float32, device="cuda")
+        ws = ws_bytes(tm.moe_workspace_bytes(1, Wh))
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            tm.moe_forward(Wh, X, Y, ws)
+            g.capture_end()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            Y.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            assert np.array_equal(host(Y), got["Y"]), rep
+
+
 # -------------------------------------------------------------------- LM head
 def _lm_head(tm, xb, Wd, k, with_logits=True):
     T = xb.shape[0]
