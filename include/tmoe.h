@@ -166,7 +166,7 @@ int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t
  *   n_fixup: int32 device scalar or NULL, receives the number of tokens that
  *   took the double-double path.
  * Limits: 1 <= k <= min(E, 16), E <= 1024, H in {256, 512, 1024, 2048, 4096}. */
-size_t tmoe_router_workspace_bytes(int64_t T, int64_t E); /* zero-fill once: per-token bound slots, left at zero */
+size_t tmoe_router_workspace_bytes(int64_t T, int64_t E); /* fp64 logits and bound slots; no zero-fill needed */
 int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                      int64_t E, int k, int32_t *idx, float *w, float *logits, int32_t *n_fixup, void *ws,
                      size_t ws_bytes);
@@ -241,11 +241,10 @@ typedef struct tmoe_moe_options {
   uint16_t *resid_out;/* [T][H] bf16: X + Y rounded to bf16 (the residual stream) */
 } tmoe_moe_options;
 
-/* Workspace bytes for tmoe_moe_forward with T tokens. The workspace must be
- * zero-filled once after allocation: it holds per-token bound slots that
- * every call leaves at zero again (so no per-call clearing, and the call can
- * be captured in a HIP graph). Calls sharing one workspace must not run
- * concurrently. */
+/* Workspace bytes for tmoe_moe_forward with T tokens. Every call writes each
+ * workspace byte it reads before reading it, so the workspace needs no
+ * zero-fill and no per-call clearing (the call can be captured in a HIP
+ * graph). Calls sharing one workspace must not run concurrently. */
 int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 
 /* The layer: router -> top-k -> grouping -> expert FFN -> combine.

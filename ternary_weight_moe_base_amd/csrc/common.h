@@ -154,8 +154,12 @@ int launch_unpack(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, int64_
 int launch_repack_tiled(hipStream_t st, const uint8_t *P, int64_t R, int64_t K, int64_t ldp, uint8_t *Pt);
 int launch_unpack_tiled(hipStream_t st, const uint8_t *Pt, int64_t R, int64_t K, int8_t *T);
 
+// Per-token error-bound inputs: bnd[t * nb + b] holds the bits of workgroup
+// b's maximum over its experts of (sum_i |x_i w_ei| + |b_e|) (fp64 >= 0), one
+// plain store per slot (no atomics, nothing to clear); a token's bound is the
+// maximum of its nb slots. nb = experts / 4 (VALU logits) or / 16 (matrix cores).
 struct RouterWs {
-  uint64_t *bnd;  // [T] bits of an upper bound of max_e (sum_i |x_i w_ei| + |b_e|) (fp64 >= 0); zero between calls
+  uint64_t *bnd;  // [T][nb], capacity T * ceil(E / 4)
   double *lg;     // [T][E] fp64 logits
 };
 size_t router_ws_bytes(int64_t T, int64_t E);
@@ -164,10 +168,11 @@ RouterWs router_ws_carve(void *ws, int64_t T, int64_t E);
 // top-k with its double-double fall-back (two kernels).
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                   int64_t E, int k, int32_t *idx, float *w, float *logits_out, int32_t *n_fixup, const RouterWs &rw);
-// Logits and per-token bounds only, T <= 16 (the decode layer path certifies
-// the top-k in the gate/up kernel's prologue). Returns the error-bound depth in *depth.
+// Logits and per-token bound slots only, T <= 16 (the decode layer path certifies
+// the top-k in the gate/up kernel's prologue). Returns the error-bound depth in
+// *depth and the bound slots per token in *nb.
 int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
-                         int64_t E, const RouterWs &rw, int *depth);
+                         int64_t E, const RouterWs &rw, int *depth, int *nb);
 // Decode path (T <= kDecodeMaxT): every (token, slot) pair of an expert fits one work tile.
 constexpr int kDecodeMaxT = 16;
 // Token counts that take the three-kernel decode path in the layer call.
@@ -209,8 +214,8 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
 // next call.
 struct DecodeRoute {
   const double *lg;
-  uint64_t *bnd;
-  int depth;
+  const uint64_t *bnd;
+  int depth, nb;  // error-bound depth; bound slots per token
   const float *Wr, *bias;
   int32_t *idx, *n_fixup, *sorted_token, *sorted_slot, *pos;
   float *w;

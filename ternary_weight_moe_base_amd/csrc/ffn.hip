@@ -269,13 +269,15 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
   // logits of this wavefront's tokens (t = wave + 4q), in flight with the staging below
   double lv[kDecodeMaxT / 4][NPL];
-  double bnd[kDecodeMaxT / 4];
+  uint64_t bm[kDecodeMaxT / 4];  // this lane's largest bound slot of each of the wavefront's tokens
 #pragma unroll
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
+    bm[q] = 0;
     if (t < T) {
       topk_load<NPL>(r.lg + (int64_t)t * E, E, lv[q]);
-      bnd[q] = bitsd(r.bnd[t]);
+      const uint64_t *slots = r.bnd + (int64_t)t * r.nb;
+      for (int j = lane; j < r.nb; j += 64) bm[q] = bm[q] > slots[j] ? bm[q] : slots[j];
     }
   }
   // every token's activations into LDS row t, zero row 16
@@ -301,7 +303,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
     // one token: wavefront 0 selects its k experts; their ranks among the k
     // (all distinct) are the grouped positions and the tile indices
     if (wave == 0) {
-      const double B = 1.01 * gamma_d(r.depth) * bnd[0];
+      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(bm[0]));
       int nfix = 0;
       if (!topk_certified_v<NPL>(lv[0], r.lg, E, k, B, s.sidx, s.sw)) {
         nfix = 1;
@@ -340,7 +342,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
     if (t < T) {
-      const double B = 1.01 * gamma_d(r.depth) * bnd[q];
+      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(bm[q]));
       if (!topk_certified_v<NPL>(lv[q], r.lg + (int64_t)t * E, E, k, B, s.sidx + t * k, s.sw + t * k)) {
         if (lane == 0) atomicAdd(&s.nfix, 1);
         topk_dd<NPL>(a.X + (int64_t)t * a.gx.K, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx + t * k, s.sw + t * k,
@@ -870,7 +872,6 @@ struct DownCombineArgs {
   float *Y;                   // [T][H] or null
   const uint16_t *resid_in;   // [T][H] bf16 or null
   uint16_t *resid_out;        // [T][H] bf16 or null (may alias resid_in)
-  uint64_t *bnd;              // per-token bound slots, cleared here for the next call
 };
 
 constexpr int kDcWaves = 8;
@@ -938,8 +939,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
     s_pw[threadIdx.x] = a.pair_w[threadIdx.x];
   }
   for (int i = lane; i < kDecodeMaxT * 16; i += 64) (&yacc[wave][0][0])[i] = 0.f;
-  if (blockIdx.x == 0 && (int)threadIdx.x < a.T) a.bnd[threadIdx.x] = 0;
-  lds_barrier();  // the first tile's weights and the bound reset may still be in flight
+  lds_barrier();  // the first tile's weights may still be in flight
   const int plane = a.P * a.slots * 2;
   for (int tile = wave; tile < nt; tile += kDcWaves) {
     const bool first = tile == wave;
@@ -999,11 +999,6 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
     if (a.Y) a.Y[o] = y;
     if (a.resid_out) a.resid_out[o] = f32_to_bf16_rne(__uint_as_float((uint32_t)a.resid_in[o] << 16) + y);
   }
-}
-
-// Clears the per-token bound slots (decode path with the separate combine).
-__global__ void clear_bounds_kernel(uint64_t *bnd, int T) {
-  if ((int)threadIdx.x < T) bnd[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------- ternary linear
@@ -1328,7 +1323,6 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
     da.Y = Y;
     da.resid_in = resid_in;
     da.resid_out = resid_out;
-    da.bnd = r.bnd;
     const size_t lds = (size_t)3 * P * gi.slots * 2;
     rc = allow_lds<down_combine_kernel<3, 2>>(lds);
     if (rc) return rc;
@@ -1340,8 +1334,6 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
   // more pairs: down over (tile, 64-row block) into O, then the combine
   rc = run_down(st, W, fw, P, nx, O);
   if (rc) return rc;
-  hipLaunchKernelGGL(clear_bounds_kernel, dim3(1), dim3(64), 0, st, r.bnd, (int)T);
-  TMOE_LAUNCHED("clear_bounds");
   return launch_combine(st, O, r.w, r.pos, T, k, H, Y, resid_in, resid_out);
 }
 

@@ -476,10 +476,10 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   const FfnWs fw = ffn_ws_carve(base + L.off_ffn, T, k, E, H, W->inter);
   if (T <= kDecodePathMaxT) {
     // logits; gate/up with the certified top-k and grouping in its prologue; down + combine
-    int depth = 0;
-    rc = launch_router_logits(st, X, T, H, W->router_w, W->router_bias, E, rw, &depth);
+    int depth = 0, nb = 0;
+    rc = launch_router_logits(st, X, T, H, W->router_w, W->router_bias, E, rw, &depth, &nb);
     if (rc) return rc;
-    const DecodeRoute r{rw.lg, rw.bnd, depth, W->router_w, W->router_bias, idx, o.n_fixup, st_tok, st_slot, pos,
+    const DecodeRoute r{rw.lg, rw.bnd, depth, nb, W->router_w, W->router_bias, idx, o.n_fixup, st_tok, st_slot, pos,
                         wt, nullptr, nullptr, nullptr};
     return launch_decode_tail(st, W, X, T, o.clamp, r, fw, O, Y, o.resid_out ? X : nullptr, o.resid_out);
   }

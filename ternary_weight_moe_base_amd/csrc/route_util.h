@@ -164,6 +164,20 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+  return ((uint64_t)mh << 32) | ml;
+}
+
+// Largest of a token's nb bound slots (fp64 bits, all >= 0), to every lane.
+__device__ inline double bound_of_slots(const uint64_t *slots, int nb) {
+  uint64_t m = 0;
+  for (int j = threadIdx.x & 63; j < nb; j += 64) m = m > slots[j] ? m : slots[j];
+  return __longlong_as_double((long long)wave_max_u64(m));
+}
+
 // One token's logits: lane l holds experts l*NPL + j (0 past E).
 template <int NPL>
 __device__ inline void topk_load(const double *lg, int E, double v[NPL]) {
@@ -359,6 +373,7 @@ __device__ inline bool topk_fast(const double v[NPL], const double *lg, int E, i
   const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)mine, m - 1);
   if (__ballot(key[0] >= ((last >> IB) << IB)) != 0ull) return false;  // bucket shared with an unselected expert
   const int myi = E - 1 - (int)(mine & ((1u << IB) - 1u));
+  // (a re-read of lg measured faster than fetching the values from other lanes)
   const double myv = lane < m ? lg[myi] : 0.0;
   const double nxt = __shfl_down(myv, 1, 64);
   if (__ballot(lane + 1 < m && !(myv - nxt > 2.0 * B)) != 0ull) return false;
@@ -373,8 +388,9 @@ __device__ inline bool topk_fast(const double v[NPL], const double *lg, int E, i
   return true;
 }
 
-// Certified top-k of one token's logits lg[0..E) by one wavefront: the fast
-// 32-bit path, then the 64-bit tournament. False: not certifiable in fp64.
+// Certified top-k of one token's logits lg[0..E) (also held as by topk_load)
+// by one wavefront: the fast 32-bit path, then the 64-bit tournament. False:
+// not certifiable in fp64.
 template <int NPL>
 __device__ inline bool topk_certified_v(const double v[NPL], const double *lg, int E, int k, double B, int32_t *idx,
                                         float *w) {

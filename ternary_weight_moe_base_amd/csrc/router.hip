@@ -23,7 +23,7 @@ static constexpr int kVectorRouterMaxT = 64;  // up to 64 tokens the VALU kernel
 
 size_t router_ws_bytes(int64_t T, int64_t E) {
   size_t o = 0;
-  o = align_up(o + T * 8, 256);      // bnd
+  o = align_up(o + T * cdiv(E, 4) * 8, 256);  // bnd
   o = align_up(o + T * E * 8, 256);  // lg
   return o;
 }
@@ -33,7 +33,7 @@ RouterWs router_ws_carve(void *ws, int64_t T, int64_t E) {
   RouterWs r;
   size_t o = 0;
   r.bnd = (uint64_t *)(b + o);
-  o = align_up(o + T * 8, 256);
+  o = align_up(o + T * cdiv(E, 4) * 8, 256);
   r.lg = (double *)(b + o);
   return r;
 }
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *X, i
   }
   for (int n = threadIdx.x; n < nt; n += 256) {
     const double a = fmax(fmax(abs_s[n * 4], abs_s[n * 4 + 1]), fmax(abs_s[n * 4 + 2], abs_s[n * 4 + 3]));
-    atomicMax((unsigned long long *)&bnd[t0 + n], (unsigned long long)dbits(a));
+    bnd[(t0 + n) * gridDim.x + blockIdx.x] = dbits(a);  // this workgroup's bound slot of token t0 + n
   }
 }
 
@@ -216,27 +216,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const double nw = sqrt(((nw2[0][j] + nw2[1][j]) + nw2[2][j]) + nw2[3][j]);
         m = fmax(m, nx * nw + (bias ? fabs((double)bias[e0 + j]) : 0.0));
       }
-      atomicMax((unsigned long long *)&bnd[t], (unsigned long long)dbits(m));
+      bnd[t * gridDim.x + blockIdx.x] = dbits(m);  // this workgroup's bound slot of token t
     }
   }
 }
 
 // One wavefront per token: certified top-k from the fp64 logits, else the
-// double-double recompute (counted in *n_fixup); resets the token's bound slot.
+// double-double recompute (counted in *n_fixup).
 template <int NPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(int64_t T, const uint16_t *X, int H, const float *Wr,
-                                                          const float *bias, const double *lg, uint64_t *bnd, int E,
-                                                          int k, int depth, int32_t *idx, float *wout,
+                                                          const float *bias, const double *lg, const uint64_t *bnd,
+                                                          int nb, int E, int k, int depth, int32_t *idx, float *wout,
                                                           int32_t *n_fixup) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const double B = 1.01 * gamma_d(depth) * bitsd(bnd[t]);
+  const double B = 1.01 * gamma_d(depth) * bound_of_slots(bnd + t * nb, nb);
   if (!topk_certified<NPL>(lg + t * E, E, k, B, idx + t * k, wout + t * k)) {
     if (lane == 0 && n_fixup) atomicAdd(n_fixup, 1);
     topk_dd<NPL>(X + t * H, H, Wr, bias, E, k, idx + t * k, wout + t * k, nullptr);
   }
-  if (lane == 0) bnd[t] = 0;
 }
 
 __global__ void copy_d2f_kernel(const double *a, int64_t n, float *b) {
@@ -247,7 +246,7 @@ __global__ void copy_d2f_kernel(const double *a, int64_t n, float *b) {
 // ---------------------------------------------------------------- launchers
 template <int NC>
 static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
-                            int64_t E, const RouterWs &rw, int32_t *n_fixup, int *depth) {
+                            int64_t E, const RouterWs &rw, int32_t *n_fixup, int *depth, int *nb) {
   constexpr int H = NC * 256;
   // four tokens per workgroup: more workgroups in flight beat reusing a staged router row
   int tchunk = kTokChunkBytes / (H * 2);
@@ -259,6 +258,7 @@ static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
               tchunk, rw.lg, rw.bnd, n_fixup);
   TMOE_LAUNCHED("router_logits");
   *depth = 4 * NC + 8;
+  *nb = (int)grid.x;
   return TMOE_OK;
 }
 
@@ -266,19 +266,20 @@ template <int NC, int NPL>
 static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
                             int64_t E, int k, int32_t *idx, float *w, int32_t *n_fixup, const RouterWs &rw) {
   constexpr int H = NC * 256;
-  int depth;
+  int depth, nb;
   if (T <= kVectorRouterMaxT) {
-    int rc = launch_logits_nc<NC>(st, X, T, Wr, bias, E, rw, n_fixup, &depth);
+    int rc = launch_logits_nc<NC>(st, X, T, Wr, bias, E, rw, n_fixup, &depth, &nb);
     if (rc) return rc;
   } else {
     if (cdiv(T, 16) > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
     TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, (router_mfma_kernel<NC>), dim3((unsigned)cdiv(E, 16), (unsigned)cdiv(T, 16)),
                 dim3(256), 0, st, X, T, Wr, bias, (int)E, rw.lg, rw.bnd, n_fixup);
     depth = H + 8;
+    nb = (int)cdiv(E, 16);
   }
   TMOE_LAUNCHED("router_logits");
   TMOE_LAUNCH(TMOE_KERNEL_ROUTER_TOPK, (router_topk_kernel<NPL>), dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, T, X,
-              H, Wr, bias, rw.lg, rw.bnd, (int)E, k, depth, idx, w, n_fixup);
+              H, Wr, bias, rw.lg, rw.bnd, nb, (int)E, k, depth, idx, w, n_fixup);
   TMOE_LAUNCHED("router_topk");
   return TMOE_OK;
 }
@@ -298,13 +299,13 @@ static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
   } while (0)
 
 int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
-                         int64_t E, const RouterWs &rw, int *depth) {
+                         int64_t E, const RouterWs &rw, int *depth, int *nb) {
   switch (H / 256) {
-    case 1: return launch_logits_nc<1>(st, X, T, Wr, bias, E, rw, nullptr, depth);
-    case 2: return launch_logits_nc<2>(st, X, T, Wr, bias, E, rw, nullptr, depth);
-    case 4: return launch_logits_nc<4>(st, X, T, Wr, bias, E, rw, nullptr, depth);
-    case 8: return launch_logits_nc<8>(st, X, T, Wr, bias, E, rw, nullptr, depth);
-    case 16: return launch_logits_nc<16>(st, X, T, Wr, bias, E, rw, nullptr, depth);
+    case 1: return launch_logits_nc<1>(st, X, T, Wr, bias, E, rw, nullptr, depth, nb);
+    case 2: return launch_logits_nc<2>(st, X, T, Wr, bias, E, rw, nullptr, depth, nb);
+    case 4: return launch_logits_nc<4>(st, X, T, Wr, bias, E, rw, nullptr, depth, nb);
+    case 8: return launch_logits_nc<8>(st, X, T, Wr, bias, E, rw, nullptr, depth, nb);
+    case 16: return launch_logits_nc<16>(st, X, T, Wr, bias, E, rw, nullptr, depth, nb);
     default: return fail(TMOE_E_UNSUPPORTED, "router hidden size must be 256, 512, 1024, 2048 or 4096");
   }
 }

@@ -40,7 +40,6 @@ def host(t):
 
 
 def ws_bytes(n):
-    # workspaces are zero-filled once after allocation (the layer keeps a counter there)
     return torch.zeros(max(int(n), 16), dtype=torch.uint8, device="cuda")
 
 
@@ -459,7 +458,7 @@ def test_layer_is_deterministic(tm, layers):
 
 
 def test_layer_workspace_reuse(tm, layers):
-    # one workspace, alternating decode sizes: the in-workspace counter is left at zero by every call
+    # one workspace, alternating sizes: whatever a call leaves there does not change the next call
     W = layers(2, 0, None)
     ws = ws_bytes(tm.moe_workspace_bytes(16, W))
     outs = {}
@@ -476,6 +475,28 @@ def test_layer_workspace_reuse(tm, layers):
                 assert np.array_equal(got[1], ridx)
             else:
                 assert np.array_equal(got[0], outs[T][0]) and np.array_equal(got[1], outs[T][1])
+
+
+@pytest.mark.parametrize("T", [1, 3, 64, 300])
+def test_layer_workspace_needs_no_zero_fill(tm, layers, T):
+    """A workspace full of 0xFF bytes (NaN as fp64, -1 as int32) gives the
+    zero-filled workspace's result bit for bit, and no token takes the
+    double-double path (a bound slot read before its write would be NaN and
+    fail every certification)."""
+    say(f"layer with a 0xFF-filled workspace T={T}")
+    W = layers(2, 0, None)
+    xb = ti.activations(11, T)
+    ref = _run_layer(tm, W, xb)
+    n = tm.moe_workspace_bytes(T, W)
+    ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+    Y = torch.empty((T, 2048), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+    nf = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        tm.moe_forward(W, bf16_dev(xb), Y, ws, idx=idx, n_fixup=nf)
+        assert np.array_equal(host(Y), ref["Y"]), rep
+        assert np.array_equal(host(idx), ref["idx"]), rep
+        assert int(host(nf)[0]) == ref["nfix"] == 0, rep
 
 
 def test_layer_decode_ties(tm, layers):
