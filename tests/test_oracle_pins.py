@@ -26,6 +26,14 @@ def _read_golden(name):
     return rows
 
 
+def _figs():
+    """Page figures by name: numbers as float, lists of numbers as int lists."""
+    out = {}
+    for name, value, _ in _read_golden("page_figures.txt"):
+        out[name] = [int(v) for v in value.split()] if " " in value else float(value)
+    return out
+
+
 # ---------------------------------------------------------------- packing (O2/O3)
 def test_pack_hand_examples():
     for trits, expect in _read_golden("pack_examples.txt"):
@@ -73,7 +81,7 @@ def test_unpack_rejects_invalid_bytes():
 
 
 def test_packed_sizes_closed_form():
-    figs = {r[0]: float(r[1]) for r in _read_golden("page_figures.txt")}
+    figs = _figs()
     assert 3 ** int(figs["trits_per_byte"]) == int(figs["codes_per_byte"]) <= 256
     assert abs(math.log2(3) - figs["entropy_floor_bits"]) < 5e-4
     H, I, E, L = int(figs["hidden"]), int(figs["moe_intermediate"]), int(figs["n_experts"]), int(figs["n_layers"])
@@ -155,7 +163,7 @@ def test_zero_fraction_gaussian_closed_form():
 def test_zero_fraction_heavy_tail_reproduces_page_band():
     # Laplace(b): E|W| = b and P(|W| <= b/2) = 1 - exp(-1/2) = 0.39347, inside the
     # page's 38-43% band for trained rows.
-    figs = {r[0]: float(r[1]) for r in _read_golden("page_figures.txt")}
+    figs = _figs()
     p = 1 - math.exp(-0.5)
     assert figs["zero_fraction_low"] < p < figs["zero_fraction_high"]
     g = np.random.default_rng(3)
@@ -264,7 +272,7 @@ def test_router_exact_path_resolves_float64_collision():
 
 # ------------------------------------------------------------------ LM head
 def test_lm_head_table_size_matches_page():
-    figs = {r[0]: float(r[1]) for r in _read_golden("page_figures.txt")}
+    figs = _figs()
     V, H = int(figs["vocab"]), int(figs["hidden"])
     table = V * H * 2  # one bf16 table
     assert table == 622329856
@@ -428,3 +436,112 @@ def test_max_normalized_error():
     ref = np.array([[1.0, -4.0], [0.0, 0.0]])
     got = np.array([[1.0, -4.0 + 4e-5], [1e-3, 0.0]])
     assert abs(O.max_normalized_error(got, ref) - 1e-3) < 1e-15
+
+
+# ----------------------------------------------------------- attention half (NEXT-3)
+from oracle import attention_oracle as AO  # noqa: E402
+
+
+def test_attention_census_and_pattern_match_pages():
+    figs = _figs()
+    H, I, E, L = int(figs["hidden"]), int(figs["moe_intermediate"]), int(figs["n_experts"]), int(figs["n_layers"])
+    experts = 3 * I * H * E * L
+    attn = L * (ti.ATTN_QKV_ROWS * H + H * AO.N_HEADS * AO.HEAD_DIM)
+    assert ti.ATTN_QKV_ROWS * H + H * H == 2 * H * H + 2 * 512 * H == 10_485_760
+    # the page's 19.58B ternary weights = experts + the attention projections
+    assert round((experts + attn) / 1e9, 2) == figs["ternary_params"] / 1e9
+    assert round(experts / 1e9, 2) == 19.33
+    assert [l for l in range(L) if AO.is_global_layer(l)] == figs["global_layers"]
+    assert AO.WINDOW == figs["sliding_window"] and AO.ROTARY_DIM == figs["partial_rotary_factor"] * AO.HEAD_DIM
+
+
+def test_rope_matches_library_rotate_half():
+    """Rotary on the first rot_dim dimensions with the rotate-half pairing, as the
+    transformers library applies it (llama rotate_half on the rotated part, the
+    rest passed through, inverse frequencies 1 / base^(2i / rot_dim))."""
+    import torch
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+
+    rng = np.random.default_rng(3)
+    P, hd, rot, base = 40, 128, 64, 10000.0
+    q = rng.standard_normal((2, P, hd))
+    k = rng.standard_normal((1, P, hd))
+    pos = np.arange(1000, 1000 + P)
+    inv = 1.0 / (base ** (torch.arange(0, rot, 2, dtype=torch.float64) / rot))
+    freqs = torch.outer(torch.tensor(pos, dtype=torch.float64), inv)
+    emb = torch.cat([freqs, freqs], dim=-1)
+    qt, kt = torch.tensor(q)[None], torch.tensor(k)[None]
+    q_rot, k_rot = apply_rotary_pos_emb(qt[..., :rot], kt[..., :rot], emb.cos()[None], emb.sin()[None])
+    want_q = torch.cat([q_rot, qt[..., rot:]], dim=-1)[0].numpy()
+    want_k = torch.cat([k_rot, kt[..., rot:]], dim=-1)[0].numpy()
+    assert np.allclose(AO.rope(q, pos), want_q, rtol=0, atol=1e-12)
+    assert np.allclose(AO.rope(k, pos), want_k, rtol=0, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal((1, 128)), rng.standard_normal((1, 128))
+    for m, n, shift in ((5, 3, 1000), (0, 0, 77), (130000, 129600, -129000)):
+        a = AO.rope(q, np.array([m]))[0] @ AO.rope(k, np.array([n]))[0]
+        b = AO.rope(q, np.array([m + shift]))[0] @ AO.rope(k, np.array([n + shift]))[0]
+        assert abs(a - b) < 1e-9 * (1 + abs(a))
+    r = AO.rope(q, np.array([12345]))
+    assert np.array_equal(r[0, 64:], q[0, 64:])  # only the first half of the head turns
+    assert abs(np.linalg.norm(r) - np.linalg.norm(q)) < 1e-12
+
+
+def _tiny_attention(seed, P, global_layer, window=8):
+    rng = np.random.default_rng(seed)
+    H, nh, nkv, hd = 64, 8, 2, 16
+    W = [rng.standard_normal(s) * 0.3 for s in ((nh * hd, H), (nkv * hd, H), (nkv * hd, H), (H, nh * hd))]
+    x = ti.f32_to_bf16_bits(rng.standard_normal((P, H)).astype(np.float32))
+    f = lambda xb: AO.attention_half(xb, *W, global_layer, n_heads=nh, n_kv=nkv, head_dim=hd, rot_dim=8,
+                                     window=window)
+    return x, W, f
+
+
+def test_attention_matches_library_sdpa_with_explicit_mask():
+    """Masking, scaling, softmax and the head-to-group map checked against
+    torch's scaled_dot_product_attention on the oracle's own q, k, v."""
+    import torch
+
+    for global_layer in (False, True):
+        x, W, f = _tiny_attention(5, 30, global_layer)
+        r = f(x)
+        q, k, v = (torch.tensor(r[n])[None] for n in ("q", "k", "v"))
+        k, v = k.repeat_interleave(4, dim=1), v.repeat_interleave(4, dim=1)  # query head h reads group h // 4
+        P = q.shape[2]
+        mask = torch.tensor([[AO.visible(p, j, 0 if global_layer else 8) for j in range(P)] for p in range(P)])
+        want = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+        got = r["attn"].reshape(P, 8, 16).transpose(1, 0, 2)
+        assert np.allclose(got, want[0].numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_window_locality():
+    """A sliding query at p ignores every input older than p - window + 1 and
+    depends on that one; a global query depends on position 0."""
+    x, W, f = _tiny_attention(6, 40, global_layer=False, window=8)
+    base = f(x)["o"][39]
+    y = x.copy()
+    y[:32] = ti.f32_to_bf16_bits(np.random.default_rng(7).standard_normal((32, 64)).astype(np.float32))
+    assert np.array_equal(f(y)["o"][39], base)
+    y[32] = y[33]
+    assert not np.allclose(f(y)["o"][39], base)
+    xg, Wg, fg = _tiny_attention(6, 40, global_layer=True)
+    yg = xg.copy()
+    yg[0] = yg[1]
+    assert not np.allclose(fg(yg)["o"][39], fg(xg)["o"][39])
+
+
+def test_attention_special_cases():
+    # one visible key: the output is its value vector, whatever the scores
+    x, W, f = _tiny_attention(8, 1, global_layer=False)
+    r = f(x)
+    for h in range(8):
+        assert np.allclose(r["attn"][0, 16 * h:16 * h + 16], r["v"][h // 4, 0], rtol=0, atol=1e-13)
+    # global layer, identical inputs at every position: every key scores the same, output = the common value
+    x, W, f = _tiny_attention(9, 12, global_layer=True)
+    x[:] = x[0]
+    r = f(x)
+    for h in range(8):
+        assert np.allclose(r["attn"][:, 16 * h:16 * h + 16], r["v"][h // 4, 0], rtol=0, atol=1e-12)

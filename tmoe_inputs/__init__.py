@@ -41,6 +41,9 @@ TOP_K = 8
 N_LAYERS = 24
 
 MAT_GATE, MAT_UP, MAT_DOWN, MAT_ROUTER = 0, 1, 2, 3
+MAT_ATTN_QKV, MAT_ATTN_O = 4, 5
+ATTN_STD = np.float32(0.02)
+ATTN_QKV_ROWS = 16 * 128 + 2 * 4 * 128  # query heads, then key and value heads (head_dim 128)
 MAT_LMHEAD = 6
 VOCAB = 151936
 LMHEAD_STD = np.float32(0.02)
@@ -95,6 +98,18 @@ def router_matrix(cfg: int, layer: int, experts: int = N_EXPERTS, hidden: int = 
     """fp32 router weights [E][H], fp32(0.02) * Irwin-Hall(12)."""
     w = ih12_normal(stream_id(cfg, layer, 1023, MAT_ROUTER), experts * hidden)
     return (w * ROUTER_STD).astype(np.float32).reshape(experts, hidden)
+
+
+def attn_qkv_matrix(cfg: int, layer: int, rows: int = ATTN_QKV_ROWS, hidden: int = HIDDEN) -> np.ndarray:
+    """Raw fp32 [q; k; v] projection rows [rows][hidden]: fp32(0.02) * Irwin-Hall(12)."""
+    w = ih12_normal(stream_id(cfg, layer, 0, MAT_ATTN_QKV), rows * hidden)
+    return (w * ATTN_STD).astype(np.float32).reshape(rows, hidden)
+
+
+def attn_o_matrix(cfg: int, layer: int, hidden: int = HIDDEN, width: int = HIDDEN) -> np.ndarray:
+    """Raw fp32 output projection [hidden][width]: fp32(0.02) * Irwin-Hall(12)."""
+    w = ih12_normal(stream_id(cfg, layer, 0, MAT_ATTN_O), hidden * width)
+    return (w * ATTN_STD).astype(np.float32).reshape(hidden, width)
 
 
 def lm_head_rows(cfg: int, v0: int, v1: int, hidden: int = HIDDEN) -> np.ndarray:
