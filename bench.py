@@ -42,6 +42,12 @@ WORKLOADS = {
     # config 6 with every layer's experts in pinned host memory, read over PCIe on demand
     8: dict(name="moe_stack24_decode_T1_host_experts", tokens=1, bias=None, layers=24, steps=40, warmup=2, stack=True,
             model_cfg=5, host_experts=True),
+    # one token through the 24 attention halves (18 sliding-window layers, 6 global) at context 4096
+    9: dict(name="attention24_decode_T1_ctx4096", tokens=1, bias=None, layers=24, steps=100, warmup=4, model_cfg=5,
+            attention=True, moe=False, context=4096),
+    # one token through the whole 24-layer stack, attention then MoE per layer, at context 4096
+    10: dict(name="model24_decode_T1_ctx4096", tokens=1, bias=None, layers=24, steps=100, warmup=4, model_cfg=5,
+             attention=True, moe=True, context=4096),
     # the model's untied bf16 output head (151,936 x 2048, 622 MB) and its top-16, one token per step
     7: dict(name="lm_head_topk16_T1", tokens=1, bias=None, layers=1, steps=400, warmup=10, model_cfg=5, lm_head=True),
 }
@@ -203,6 +209,125 @@ def cpu_baseline_lm_head(wl: dict, budget_s: float = 12.0):
             "kind": "oracle", "sample": sample}
 
 
+ATTN_KERNELS = ("linear", "attention")
+
+
+def main_attention(args, wl: dict):
+    """One-token decode through the 24 attention halves (config 9) or through
+    the whole stack, attention then MoE per layer (config 10), with key/value
+    caches prefilled to `context` positions by the library's own prefill
+    (one 4096-token call per layer, untimed). Step i is the token at position
+    context + i; the K timed steps are one captured graph."""
+    import numpy as np
+    import torch
+
+    ensure_built()
+    import ternary_weight_moe_base_amd as tm
+    from ternary_weight_moe_base_amd import synthetic
+
+    K = args.steps if args.steps is not None else wl["steps"]
+    W_ = args.warmup if args.warmup is not None else wl["warmup"]
+    L, ctx, mcfg = wl["layers"], wl["context"], wl["model_cfg"]
+    dev = torch.device("cuda")
+    torch.cuda.init()
+    t0 = time.perf_counter()
+    attn = [synthetic.build_attention(mcfg, l, synthetic.is_global_layer(l)) for l in range(L)]
+    moe = [synthetic.build_layer(mcfg, l, None) for l in range(L)] if wl["moe"] else None
+    caches = []
+    xp = synthetic.activations(mcfg, ctx)
+    wsp = torch.empty(tm.attention_workspace_bytes(ctx, attn[0]), dtype=torch.uint8, device=dev)
+    scratch = torch.empty((ctx, H), dtype=torch.int16, device=dev)
+    for l in range(L):
+        cap = ctx + W_ + K + 1 if attn[l].window == 0 else attn[l].window + ctx - 1
+        kc, vc = tm.kv_cache(attn[l], cap)
+        tm.attention_forward(attn[l], xp, 0, kc, vc, wsp, X_out=scratch)  # prefill: fills the cache
+        caches.append((kc, vc))
+    del wsp, scratch
+    torch.cuda.synchronize()
+    log(f"built and prefilled {L} layers in {time.perf_counter() - t0:.1f} s")
+    X = synthetic.activations(mcfg, W_ + K, layer=1).view(W_ + K, 1, H)
+    xw = torch.empty((1, H), dtype=torch.int16, device=dev)
+    wsa = torch.empty(tm.attention_workspace_bytes(1, attn[0]), dtype=torch.uint8, device=dev)
+    wsm = torch.empty(tm.moe_workspace_bytes(1, moe[0]) if moe else 16, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        for l in range(L):
+            tm.attention_forward(attn[l], X[i] if l == 0 else xw, ctx + i, *caches[l], wsa, X_out=xw)
+            if moe:
+                tm.moe_forward(moe[l], xw, None, wsm, resid_out=xw)
+
+    for i in range(W_):
+        step(i)
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph.capture_begin()
+            for i in range(W_, W_ + K):
+                step(i)
+            graph.capture_end()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(W_, W_ + K):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-kernel durations over the same steps launched again (eagerly, same positions)
+    kern = {}
+    names = ATTN_KERNELS + (DECODE_KERNELS if moe else ())
+    cap_n = K * L * 2
+    for name in names:
+        tm.profile_begin(name, cap_n)
+        for i in range(W_, W_ + K):
+            step(i)
+        ms = tm.profile_end(cap_n)
+        if len(ms):
+            kern[name] = ms
+    torch.cuda.synchronize()
+    per_token_us = {n: float(np.sum(v)) * 1e3 / K for n, v in kern.items()}
+    # algorithmic bytes per launch
+    n_glob = sum(1 for a in attn if a.window == 0)
+    keys_glob = ctx + W_ + (K - 1) / 2 + 1  # mean visible keys of a global layer over the timed steps
+    kv_bytes = 2 * 4 * 128 * 4  # key + value of one position, all 4 heads, fp32
+    att_b = (n_glob * keys_glob + (L - n_glob) * 512) / L * kv_bytes
+    lin_b = (tm.tiled_bytes(3072, H) + 4 * 3072 + tm.tiled_bytes(H, H) + 4 * H) / 2 + H * 2
+    dom = args.kernel if args.kernel else max(per_token_us, key=per_token_us.get)
+    if dom == "attention":
+        b = att_b
+    elif dom == "linear":
+        b = lin_b
+    elif dom == "gateup":
+        b = 8 * 2 * (PACKED_GU + 4 * I) + H * 2
+    elif dom == "down":
+        b = 8 * (PACKED_D + 4 * H)
+    else:
+        b = ROUTER_BYTES + H * 2
+    mean_s = float(np.mean(kern[dom])) * 1e-3
+    roof = {"bound": "hbm", "achieved": b / mean_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": b / mean_s / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": dom, "mean_launch_us": mean_s * 1e6,
+            "launches": int(len(kern[dom])), "algorithmic_bytes_per_launch": float(b),
+            "kernels_us_per_token": {n: round(v, 3) for n, v in per_token_us.items()}}
+    out = {
+        "metric": METRIC, "value": K / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W_,
+        "ms_per_step": 1e3 * elapsed / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["name"], "tokens_per_step": 1, "layers_per_step": L, "context": ctx,
+                   "global_layers": n_glob, "sliding_window": 512, "heads": "16 query, 4 key/value, 128 wide",
+                   "parts": "attention + MoE" if moe else "attention", "hip_graph": use_graph},
+        "token_latency_us": 1e6 * elapsed / K,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main_lm_head(args, wl: dict):
     import numpy as np
     import torch
@@ -308,6 +433,8 @@ def main():
     wl = dict(WORKLOADS[cfg])
     if wl.get("lm_head"):
         return main_lm_head(args, wl)
+    if wl.get("attention"):
+        return main_attention(args, wl)
     K = args.steps if args.steps is not None else wl["steps"]
     W_ = args.warmup if args.warmup is not None else wl["warmup"]
     L = args.layers if args.layers is not None else wl["layers"]

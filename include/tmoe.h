@@ -257,6 +257,58 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------- attention half
+ * The step before the MoE in every layer (ai.thesatyajit.com, "The
+ * architecture around the quantization"; jj-blog, architecture list): layers
+ * repeat three sliding-window layers (a query sees the last 512 positions,
+ * rotary embedding on half of each head: partial rotary factor 0.5) and one
+ * global layer (the whole prefix, no positional encoding). The projections
+ * are ternary like the experts; their sizes follow from the census (ai.
+ * thesatyajit.com, "The 5.31 GB claim reconciles": 19.58B ternary weights
+ * less the experts' 19.33B = 2 x 2048 x 2048 + 2 x 512 x 2048 per layer).
+ * Head shape, rotary base and pairing are not on the pages and are fields here.
+ * For tokens t = 0..T-1 at positions p = pos0 + t, with x = X[t]:
+ *   [q; k; v] = s (.) (T_qkv x)            (query heads, then key, value heads)
+ *   q, k rotated on sliding layers: pair (i, i + rotary_dim/2), i < rotary_dim/2,
+ *        turns by p * rope_base^(-2i / rotary_dim)
+ *   k, v of position p stored in cache slot p mod cache_cap
+ *   attn_h = sum_j softmax_j(q_h . k_j / sqrt(head_dim)) v_j over the visible
+ *        positions j of key/value head h / (n_heads / n_kv_heads): j <= p and,
+ *        if window > 0, p - j < window
+ *   O[t] = s_o (.) (T_o attn)               (attn fp32, split exactly into three bf16 parts)
+ *   X_out[t] = bf16_RNE(fp32(x) + O[t])    (if X_out is not NULL)
+ * Weights (device): qkv_p tiled [(n_heads + 2 n_kv_heads) head_dim][hidden],
+ * qkv_s fp32 per row; o_p tiled [hidden][n_heads head_dim], o_s per row.
+ * Cache (device, fp32, caller-owned): K and V [n_kv_heads][cache_cap][head_dim];
+ * positions < pos0 must hold the keys and
+ * values earlier calls stored. cache_cap >= pos0 + T (global layers) or
+ * >= window + T - 1 (sliding: no slot a query of this call still sees is
+ * overwritten). X bf16 [T][hidden], O fp32 [T][hidden] or NULL, X_out bf16
+ * [T][hidden] or NULL (may alias X). Limits: hidden 2048, head_dim 128,
+ * n_heads head_dim = hidden, n_heads = 4 n_kv_heads, rotary_dim even <= 128.
+ * ws: tmoe_attention_workspace_bytes(T, W) bytes, no zero-fill; calls sharing
+ * a workspace or a cache must not overlap. Errors: TMOE_E_ARG, TMOE_E_SHAPE
+ * (cache too small, bad head shape), TMOE_E_ALIGN, TMOE_E_WORKSPACE,
+ * TMOE_E_UNSUPPORTED. */
+typedef struct tmoe_attn_weights {
+  int64_t hidden;     /* 2048 */
+  int32_t n_heads;    /* query heads (16) */
+  int32_t n_kv_heads; /* key/value heads (4) */
+  int32_t head_dim;   /* 128 */
+  int32_t rotary_dim; /* rotated dimensions per head on sliding layers (64) */
+  int32_t window;     /* > 0: sliding window (512), rotary; 0: global layer, no positional encoding */
+  int32_t reserved;   /* must be 0 */
+  double rope_base;   /* 10000 */
+  const uint8_t *qkv_p;
+  const float *qkv_s;
+  const uint8_t *o_p;
+  const float *o_s;
+} tmoe_attn_weights;
+size_t tmoe_attention_workspace_bytes(int64_t T, const tmoe_attn_weights *W);
+int tmoe_attention_forward(void *stream, const tmoe_attn_weights *W, const uint16_t *X, int64_t T, int64_t pos0,
+                           float *k_cache, float *v_cache, int64_t cache_cap, float *O, uint16_t *X_out, void *ws,
+                           size_t ws_bytes);
+
 /* --------------------------------------------------- host-resident experts
  * Page-locked host memory the GPU reads in place over PCIe. Expert weights
  * placed here (packed matrices and row scales; the router stays in HBM) are
@@ -331,7 +383,8 @@ enum {
   TMOE_KERNEL_LINEAR = 11,
   TMOE_KERNEL_LMH_LOGITS = 12, /* LM head: the fp64 logit stream */
   TMOE_KERNEL_LMH_TOPK = 13,   /* LM head: per-chunk top-(k+1) */
-  TMOE_KERNEL_LMH_MERGE = 14   /* LM head: merge, certification, fallback */
+  TMOE_KERNEL_LMH_MERGE = 14,  /* LM head: merge, certification, fallback */
+  TMOE_KERNEL_ATTENTION = 15   /* attention half: the split softmax attention over the cache */
 };
 int tmoe_profile_begin(int kernel, int capacity);
 int tmoe_profile_end(float *ms, int capacity, int *count);

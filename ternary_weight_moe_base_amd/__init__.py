@@ -245,6 +245,55 @@ class MoEWeights:
         return ctypes.byref(self.struct)
 
 
+class AttnWeights:
+    """Device weights of one attention half plus the C struct that describes them.
+
+    qkv_p: uint8 tiled [(n_heads + 2 n_kv) head_dim][hidden]; qkv_s fp32 per
+    row; o_p: uint8 tiled [hidden][n_heads head_dim]; o_s fp32 per row.
+    window > 0: sliding layer with rotary on rotary_dim dimensions; 0: global
+    layer without positional encoding. Keeps references to the tensors."""
+
+    def __init__(self, qkv_p, qkv_s, o_p, o_s, window: int, hidden: int = 2048, n_heads: int = 16,
+                 n_kv_heads: int = 4, head_dim: int = 128, rotary_dim: int = 64, rope_base: float = 10000.0):
+        self.tensors = (qkv_p, qkv_s, o_p, o_s)
+        self.hidden, self.n_heads, self.n_kv_heads, self.head_dim = hidden, n_heads, n_kv_heads, head_dim
+        self.window, self.rotary_dim, self.rope_base = window, rotary_dim, rope_base
+        s = _abi.AttnWeightsStruct()
+        s.hidden, s.n_heads, s.n_kv_heads, s.head_dim = hidden, n_heads, n_kv_heads, head_dim
+        s.rotary_dim, s.window, s.reserved, s.rope_base = rotary_dim, window, 0, rope_base
+        s.qkv_p, s.qkv_s, s.o_p, s.o_s = _ptr(qkv_p), _ptr(qkv_s), _ptr(o_p), _ptr(o_s)
+        self.struct = s
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def attention_workspace_bytes(T: int, W: AttnWeights) -> int:
+    n = _load().tmoe_attention_workspace_bytes(T, W.ref)
+    if n == 0:
+        raise RuntimeError("attention_workspace_bytes: unsupported attention shape")
+    return n
+
+
+def kv_cache(W: AttnWeights, capacity: int):
+    """Zeroed fp32 key and value caches, each [n_kv][capacity][head_dim]."""
+    import torch
+
+    k = torch.zeros((W.n_kv_heads, capacity, W.head_dim), dtype=torch.float32, device="cuda")
+    v = torch.zeros((W.n_kv_heads, capacity, W.head_dim), dtype=torch.float32, device="cuda")
+    return k, v
+
+
+def attention_forward(W: AttnWeights, X, pos0: int, k_cache, v_cache, ws, O=None, X_out=None, stream=None) -> None:
+    """The attention half for T = X.shape[0] new tokens at positions pos0.. (X bf16 bit patterns)."""
+    T = X.shape[0]
+    cap = k_cache.shape[1]
+    _check(_load().tmoe_attention_forward(_stream(stream), W.ref, _ptr(X), T, pos0, _ptr(k_cache), _ptr(v_cache), cap,
+                                          _ptr(O), _ptr(X_out), _ptr(ws), ws.numel() * ws.element_size()),
+           "attention_forward")
+
+
 class HostBuffer:
     """Page-locked host memory that kernels read in place over PCIe
     (tmoe_host_alloc): `host` is its CPU address, `device` the address kernels

@@ -38,6 +38,14 @@ class MoEWeightsStruct(ctypes.Structure):
     ]
 
 
+class AttnWeightsStruct(ctypes.Structure):
+    _fields_ = [
+        ("hidden", c_int64), ("n_heads", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
+        ("rotary_dim", c_int32), ("window", c_int32), ("reserved", c_int32), ("rope_base", ctypes.c_double),
+        ("qkv_p", c_void_p), ("qkv_s", c_void_p), ("o_p", c_void_p), ("o_s", c_void_p),
+    ]
+
+
 class MoEOptionsStruct(ctypes.Structure):
     _fields_ = [
         ("clamp", c_float), ("reserved0", c_int32),
@@ -76,6 +84,9 @@ SIGNATURES = {
                              c_void_p]),
     "tmoe_moe_workspace_bytes": (c_int, [c_int64, c_void_p, POINTER(c_size_t)]),
     "tmoe_moe_forward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t]),
+    "tmoe_attention_workspace_bytes": (c_size_t, [c_int64, c_void_p]),
+    "tmoe_attention_forward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64,
+                                       c_void_p, c_void_p, c_void_p, c_size_t]),
     "tmoe_host_alloc": (c_int, [c_size_t, POINTER(c_void_p), POINTER(c_void_p)]),
     "tmoe_host_free": (c_int, [c_void_p]),
     "tmoe_lm_head_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
@@ -86,7 +97,7 @@ SIGNATURES = {
 }
 
 KERNELS = {"router_logits": 1, "router_topk": 2, "group": 4, "make_tiles": 5, "gateup": 7, "down": 9, "combine": 10,
-           "linear": 11, "lmh_logits": 12, "lmh_topk": 13, "lmh_merge": 14}
+           "linear": 11, "lmh_logits": 12, "lmh_topk": 13, "lmh_merge": 14, "attention": 15}
 
 
 def declare(lib) -> None:

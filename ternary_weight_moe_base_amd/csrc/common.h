@@ -232,6 +232,15 @@ size_t linear_ws_bytes(int64_t T, int64_t K);
 int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,
                   int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws);
 
+// Attention half (attention.hip): workspace bytes and the launch sequence
+// (q/k/v linear, rotary + cache append, split attention, merge, o linear + residual).
+int attn_nsplit(int64_t T, int nkv);
+size_t attn_ws_bytes(int64_t T, int nh, int nkv, int hd);
+int launch_attention(hipStream_t st, const tmoe_attn_weights &W, const uint16_t *X, int64_t T, int64_t pos0,
+                     float *kc, float *vc, int64_t cap, float *O, uint16_t *X_out, void *ws);
+// Ternary linear over fp32 inputs (three exact bf16 parts), K = 2048, optional bf16 residual.
+int launch_linear3(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const float *X, int64_t T,
+                   float *Y, const uint16_t *resid_in, uint16_t *resid_out);
 int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,
                    float *Y, const uint16_t *resid_in, uint16_t *resid_out);
 

@@ -1032,6 +1032,20 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   const int64_t tbytes = 64 * (int64_t)(8 * Fr + Rr);
   const uint8_t *wt = a.pt + (int64_t)(active ? rt : 0) * tbytes;
   char *xs = smem;
+  const int s0 = kp * Fr / KS, s1 = (kp + 1) * Fr / KS;
+  const bool tail_here = Rr > 0 && kp == KS - 1;
+  // fixed K: this wavefront's weights first, in flight while the activations are staged
+  constexpr int SMAXF = F >= 0 ? (F + KS - 1) / KS : 1;
+  uint2 dpre[SMAXF > 0 ? SMAXF : 1];
+  uint32_t dwpre = 0, shpre = 0;
+  if constexpr (F >= 0) {
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < SMAXF; ++i)
+        if (s0 + i < s1) dpre[i] = *reinterpret_cast<const uint2 *>(wt + (int64_t)(s0 + i) * 512 + lane * 8);
+      if (tail_here) load_tail<RT>(wt, F, lane, dwpre, shpre);
+    }
+  }
 
   if (a.contig) {
     const int vec = a.g.slots / 8, kv = (int)(a.g.K / 8);
@@ -1054,17 +1068,11 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const char *bp = xs + (n < cnt ? n : 16) * rs + g * M * 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int s0 = kp * Fr / KS, s1 = (kp + 1) * Fr / KS;
-  const bool tail_here = Rr > 0 && kp == KS - 1;
   if (active) {
     if constexpr (F >= 0) {
-      constexpr int SMAX = (F + KS - 1) / KS;
-      uint2 d[SMAX > 0 ? SMAX : 1];
-#pragma unroll
-      for (int i = 0; i < SMAX; ++i)
-        if (s0 + i < s1) d[i] = *reinterpret_cast<const uint2 *>(wt + (int64_t)(s0 + i) * 512 + lane * 8);
-      uint32_t dw = 0, sh = 0;
-      if (tail_here) load_tail<RT>(wt, F, lane, dw, sh);
+      constexpr int SMAX = SMAXF;
+      const uint2 *d = dpre;
+      const uint32_t dw = dwpre, sh = shpre;
 #pragma unroll
       for (int i = 0; i < SMAX; ++i) {
         const int s = s0 + i;
@@ -1130,6 +1138,115 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v)
     if (row0 + v < a.N) y[row0 + v] = (acc[v] * 0.5f) * a.s[row0 + v];
+}
+
+// ------------------------------------------- ternary linear, fp32 input
+// Y = s (.) (T x) with fp32 x: while staging, each input is split exactly into
+// three bf16 parts (hi + mid + lo, as h of the down projection), and every
+// decoded weight slice multiplies all three (fp32 accumulation). Optional
+// residual: resid_out = bf16(fp32(resid_in) + y). K = 2048 only (natural
+// operand order); eight tokens per workgroup (three planes of staged rows).
+struct Linear3Args {
+  const uint8_t *pt;
+  const float *s;
+  const float *X;  // [T][K] fp32
+  float *Y;        // [T][N] or null
+  const uint16_t *resid_in;
+  uint16_t *resid_out;  // [T][N] bf16 or null
+  int64_t T, N;
+  Geom g;
+};
+constexpr int kL3Tok = 8;
+
+template <int KS>
+__global__ __launch_bounds__(256) void linear3_kernel(Linear3Args a) {
+  extern __shared__ __align__(16) char smem[];
+  constexpr int F = 13, TT = kL3Tok, RTB = 4 / KS, M = 5 * F;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int cnt = (int)min<int64_t>(TT, a.T - t0);
+  const int nrt = (int)((a.N + 15) / 16);
+  const int rt = blockIdx.y * RTB + wave / KS;
+  const int kp = wave % KS;
+  const bool active = rt < nrt;
+  const int rs = lds_row_bytes(a.g.slots);
+  const int plane = (TT + 1) * rs;  // [3][TT + 1][rs]; row TT of each plane is zero
+  const uint8_t *wt = a.pt + (int64_t)(active ? rt : 0) * (64 * 8 * F);
+  // this wavefront's weights first: in flight while the activations are staged
+  constexpr int SMAX = (F + KS - 1) / KS;
+  const int s0 = kp * F / KS, s1 = (kp + 1) * F / KS;
+  uint2 d[SMAX];
+#pragma unroll
+  for (int i = 0; i < SMAX; ++i)
+    if (active && s0 + i < s1) d[i] = ldw8(wt + (int64_t)(s0 + i) * 512 + lane * 8);
+  const int vec = a.g.slots / 8, kv = (int)(a.g.K / 8);
+  for (int i = threadIdx.x; i < cnt * vec; i += 256) {
+    const int n = i / vec, c = i - n * vec;
+    uint32_t w3[3][4] = {};
+    if (c < kv) {
+      const float4 *src = reinterpret_cast<const float4 *>(a.X + (t0 + n) * a.g.K) + 2 * c;
+      const float4 f0 = src[0], f1 = src[1];
+      const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b0 = f32_to_bf16_rne(f[e]);
+        const float r1 = f[e] - __uint_as_float(b0 << 16);
+        const uint32_t b1 = f32_to_bf16_rne(r1);
+        const uint32_t b2 = f32_to_bf16_rne(r1 - __uint_as_float(b1 << 16));
+        const int sh = 16 * (e & 1);
+        w3[0][e >> 1] |= b0 << sh;
+        w3[1][e >> 1] |= b1 << sh;
+        w3[2][e >> 1] |= b2 << sh;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      *reinterpret_cast<uint4 *>(smem + q * plane + n * rs + c * 16) = make_uint4(w3[q][0], w3[q][1], w3[q][2], w3[q][3]);
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) zero_row(smem + q * plane + TT * rs, a.g.slots, threadIdx.x, 256);
+  __syncthreads();
+
+  const int n = lane & 15, g = lane >> 4;
+  const char *bp = smem + (n < cnt ? n : TT) * rs + g * M * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < SMAX; ++i) {
+      const int st = s0 + i;
+      if (st < s1) {
+        uint32_t pw[20];
+        unpack8(d[i], pw);
+#pragma unroll
+        for (int m = 0; m < 5; ++m)
+#pragma unroll
+          for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(bp + q * plane + (5 * st + m) * 16), acc);
+      }
+    }
+  }
+  if constexpr (KS > 1) {
+    float *red = reinterpret_cast<float *>(smem + 3 * plane);  // [4][64][4]
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wave * 64 + lane) * 4 + v] = acc[v];
+    __syncthreads();
+    if (kp != 0) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = 0.f;
+    for (int q = 0; q < KS; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += red[((wave + q) * 64 + lane) * 4 + v];
+  }
+  if (!active || n >= cnt) return;
+  const int64_t row0 = (int64_t)rt * 16 + 4 * g, t = t0 + n;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t row = row0 + v;
+    if (row >= a.N) continue;
+    const float y = (acc[v] * 0.5f) * a.s[row];
+    if (a.Y) a.Y[t * a.N + row] = y;
+    if (a.resid_out)
+      a.resid_out[t * a.N + row] = f32_to_bf16_rne(__uint_as_float((uint32_t)a.resid_in[t * a.N + row] << 16) + y);
+  }
 }
 
 // ------------------------------------------------------------------ combine
@@ -1418,6 +1535,37 @@ int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, 
   if (g.F == 13 && g.r == 0) return small ? run_linear<13, 0, 4>(st, a, ntt, nrt) : run_linear<13, 0, 1>(st, a, ntt, nrt);
   if (g.F == 3 && g.r == 2) return run_linear<3, 2, 1>(st, a, ntt, nrt);
   return run_linear<-1, 0, 1>(st, a, ntt, nrt);
+}
+
+int launch_linear3(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const float *X, int64_t T,
+                   float *Y, const uint16_t *resid_in, uint16_t *resid_out) {
+  const Geom g = make_geom(K);
+  if (!(g.F == 13 && g.r == 0 && g.QS == 5 * g.Q)) return fail(TMOE_E_UNSUPPORTED, "fp32-input linear needs K = 2048");
+  const int64_t nrt = cdiv(N, 16), ntt = cdiv(T, kL3Tok);
+  if (ntt > 0x7FFFFFFF || nrt > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too large");
+  Linear3Args a;
+  a.pt = Pt;
+  a.s = s;
+  a.X = X;
+  a.Y = Y;
+  a.resid_in = resid_in;
+  a.resid_out = resid_out;
+  a.T = T;
+  a.N = N;
+  a.g = g;
+  const size_t lds = (size_t)3 * (kL3Tok + 1) * lds_row_bytes(g.slots) + 4 * 64 * 4 * 4;
+  if (T <= 16) {
+    int rc = allow_lds<linear3_kernel<4>>(lds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_LINEAR, linear3_kernel<4>, dim3((unsigned)ntt, (unsigned)nrt), dim3(256), lds, st, a);
+  } else {
+    int rc = allow_lds<linear3_kernel<1>>(lds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_LINEAR, linear3_kernel<1>, dim3((unsigned)ntt, (unsigned)cdiv(nrt, 4)), dim3(256), lds, st,
+                a);
+  }
+  TMOE_LAUNCHED("ternary_linear3");
+  return TMOE_OK;
 }
 
 int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,

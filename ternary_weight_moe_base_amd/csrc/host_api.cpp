@@ -267,6 +267,49 @@ int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, cons
                        router_ws_carve(ws, T, E));
 }
 
+// ------------------------------------------------------------ attention half
+static int check_attn(const tmoe_attn_weights *W) {
+  REQUIRE(W, TMOE_E_ARG, "null weights");
+  REQUIRE(W->reserved == 0, TMOE_E_ARG, "reserved must be 0");
+  REQUIRE(W->hidden == 2048 && W->head_dim == 128 && (int64_t)W->n_heads * W->head_dim == W->hidden &&
+              W->n_kv_heads > 0 && W->n_heads == 4 * W->n_kv_heads,
+          TMOE_E_UNSUPPORTED, "attention: hidden 2048, head_dim 128, n_heads = hidden / 128 = 4 n_kv_heads");
+  REQUIRE(W->window >= 0 && W->rotary_dim >= 0 && W->rotary_dim <= W->head_dim && W->rotary_dim % 2 == 0,
+          TMOE_E_SHAPE, "bad window or rotary_dim");
+  REQUIRE(!(W->window > 0 && W->rotary_dim > 0) || W->rope_base > 1.0, TMOE_E_ARG, "rope_base must be > 1");
+  REQUIRE(W->qkv_p && W->qkv_s && W->o_p && W->o_s, TMOE_E_ARG, "null weight pointer");
+  REQUIRE(aligned16(W->qkv_p) && aligned16(W->o_p) && aligned16(W->qkv_s) && aligned16(W->o_s), TMOE_E_ALIGN,
+          "misaligned weights");
+  return TMOE_OK;
+}
+
+size_t tmoe_attention_workspace_bytes(int64_t T, const tmoe_attn_weights *W) {
+  if (T < 0 || check_attn(W) != TMOE_OK) return 0;
+  return attn_ws_bytes(T > 0 ? T : 1, W->n_heads, W->n_kv_heads, W->head_dim);
+}
+
+int tmoe_attention_forward(void *stream, const tmoe_attn_weights *W, const uint16_t *X, int64_t T, int64_t pos0,
+                           float *k_cache, float *v_cache, int64_t cache_cap, float *O, uint16_t *X_out, void *ws,
+                           size_t ws_bytes) {
+  clear_error();
+  int rc = check_attn(W);
+  if (rc) return rc;
+  REQUIRE(T >= 0 && pos0 >= 0 && cache_cap > 0, TMOE_E_ARG, "bad T, pos0 or cache_cap");
+  if (T == 0) return TMOE_OK;
+  REQUIRE(T <= (1 << 24) && pos0 <= ((int64_t)1 << 40), TMOE_E_UNSUPPORTED, "T or pos0 too large");
+  REQUIRE(X && k_cache && v_cache && (O || X_out), TMOE_E_ARG, "null X, cache, or neither O nor X_out");
+  REQUIRE(aligned16(X) && aligned16(k_cache) && aligned16(v_cache) && (!O || aligned16(O)) &&
+              (!X_out || aligned16(X_out)),
+          TMOE_E_ALIGN, "misaligned pointer");
+  if (W->window > 0)
+    REQUIRE(cache_cap >= W->window + T - 1, TMOE_E_SHAPE, "sliding cache needs capacity >= window + T - 1");
+  else
+    REQUIRE(cache_cap >= pos0 + T, TMOE_E_SHAPE, "global cache needs capacity >= pos0 + T");
+  const size_t need = attn_ws_bytes(T, W->n_heads, W->n_kv_heads, W->head_dim);
+  REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes", need);
+  return launch_attention((hipStream_t)stream, *W, X, T, pos0, k_cache, v_cache, cache_cap, O, X_out, ws);
+}
+
 // ------------------------------------------------------ host-resident experts
 int tmoe_host_alloc(size_t bytes, void **host, void **device) {
   clear_error();
@@ -495,7 +538,7 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
 
 int tmoe_profile_begin(int kernel, int capacity) {
   clear_error();
-  REQUIRE(kernel >= TMOE_KERNEL_ROUTER_LOGITS && kernel <= TMOE_KERNEL_LMH_MERGE, TMOE_E_ARG, "unknown kernel id %d",
+  REQUIRE(kernel >= TMOE_KERNEL_ROUTER_LOGITS && kernel <= TMOE_KERNEL_ATTENTION, TMOE_E_ARG, "unknown kernel id %d",
           kernel);
   REQUIRE(capacity > 0 && capacity <= (1 << 20), TMOE_E_ARG, "capacity out of range");
   REQUIRE(g_prof.kernel == 0, TMOE_E_ARG, "a profiling window is already open");

@@ -47,6 +47,37 @@ def build_layer(cfg: int, layer: int, bias_kind: str | None = None, experts: int
     return MoEWeights(router_w, router_bias, gate_p, up_p, down_p, gate_s, up_s, down_s, top_k=top_k)
 
 
+def is_global_layer(layer: int) -> bool:
+    """Layer pattern: three sliding-window layers, then one global layer
+    (global at 3, 7, 11, 15, 19, 23: ai.thesatyajit.com, "The architecture
+    around the quantization")."""
+    return layer % 4 == 3
+
+
+def build_attention(cfg: int, layer: int, global_layer: bool, window: int = 512, hidden: int = ti.HIDDEN):
+    """The attention half of one layer: [q; k; v] (16 + 2 x 4 heads of 128) and
+    output projections drawn as fp32(0.02) * IH12 (the streams of
+    tmoe_inputs.attn_qkv_matrix / attn_o_matrix), ternarized and packed on the
+    device. Global layers have no window and no rotary embedding."""
+    from . import AttnWeights
+
+    dev = torch.device("cuda")
+    rows = ti.ATTN_QKV_ROWS
+    qkv_p = torch.empty(tiled_bytes(rows, hidden), dtype=torch.uint8, device=dev)
+    o_p = torch.empty(tiled_bytes(hidden, hidden), dtype=torch.uint8, device=dev)
+    qkv_s = torch.empty(rows, dtype=torch.float32, device=dev)
+    o_s = torch.empty(hidden, dtype=torch.float32, device=dev)
+    w = torch.empty(rows * hidden, dtype=torch.float32, device=dev)
+    p = torch.empty(rows * ((hidden + 4) // 5), dtype=torch.uint8, device=dev)
+    for sid, R, out_p, out_s in ((ti.stream_id(cfg, layer, 0, ti.MAT_ATTN_QKV), rows, qkv_p, qkv_s),
+                                 (ti.stream_id(cfg, layer, 0, ti.MAT_ATTN_O), hidden, o_p, o_s)):
+        synth_ih12(w[: R * hidden], sid, mult=float(ti.ATTN_STD))
+        pv = p[: R * ((hidden + 4) // 5)].view(R, (hidden + 4) // 5)
+        ternarize_pack(w[: R * hidden].view(R, hidden), pv, out_s)
+        repack_tiled(pv, hidden, out_p)
+    return AttnWeights(qkv_p, qkv_s, o_p, o_s, window=0 if global_layer else window)
+
+
 def activations(cfg: int, tokens: int, hidden: int = ti.HIDDEN, layer: int = 0) -> torch.Tensor:
     """bf16 activations as an int16 device tensor of bit patterns [T][H]."""
     x = ti.activations(cfg, tokens, hidden, layer)

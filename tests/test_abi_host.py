@@ -186,3 +186,26 @@ def test_host_alloc_rejects_bad_arguments_without_gpu():
     assert lib.tmoe_host_alloc(64, None, ctypes.byref(d)) == -1
     assert lib.tmoe_host_alloc(64, ctypes.byref(h), None) == -1
     assert lib.tmoe_host_free(None) == 0
+
+
+def test_attention_rejects_bad_arguments_without_gpu():
+    """Shape and cache checks return status codes before anything touches HIP
+    (the pointers are aligned stand-ins that are never dereferenced)."""
+    W = tm._abi.AttnWeightsStruct()
+    W.hidden, W.n_heads, W.n_kv_heads, W.head_dim, W.rotary_dim, W.window, W.reserved = 2048, 16, 4, 128, 64, 512, 0
+    W.rope_base = 10000.0
+    W.qkv_p = W.qkv_s = W.o_p = W.o_s = 1 << 20
+    fake = ctypes.c_void_p(1 << 21)
+    ws_n = lib.tmoe_attention_workspace_bytes(1, ctypes.byref(W))
+    assert ws_n > 0
+    call = lambda W_, T, pos0, cap: lib.tmoe_attention_forward(None, ctypes.byref(W_), fake, T, pos0, fake, fake, cap,
+                                                               fake, None, fake, ws_n * 64)
+    assert call(W, 0, 0, 512) == 0  # nothing to do
+    assert call(W, 4, 0, 514) == -2  # sliding: capacity < window + T - 1
+    W.window = 0
+    assert call(W, 4, 100, 103) == -2  # global: capacity < pos0 + T
+    W.n_kv_heads = 8
+    assert call(W, 1, 0, 4096) == -6  # head shape outside the built kernels
+    assert lib.tmoe_attention_workspace_bytes(1, ctypes.byref(W)) == 0
+    W.n_kv_heads, W.reserved = 4, 1
+    assert call(W, 1, 0, 4096) == -1

@@ -663,6 +663,84 @@ def test_layer_experts_on_host(tm, layers, cfg, T, bias_kind):
             assert np.array_equal(host(Y), got["Y"]), rep
 
 
+# ------------------------------------------------------------ attention half
+_ATTN_DENSE = {}
+
+
+def _attn_dense(cfg, layer):
+    if (cfg, layer) not in _ATTN_DENSE:
+        dq = O.dequantize(*O.ternarize_absmean(ti.attn_qkv_matrix(cfg, layer)))
+        do = O.dequantize(*O.ternarize_absmean(ti.attn_o_matrix(cfg, layer)))
+        _ATTN_DENSE[(cfg, layer)] = (dq[:2048], dq[2048:2560], dq[2560:], do)
+    return _ATTN_DENSE[(cfg, layer)]
+
+
+@pytest.mark.parametrize("layer,P,chunk", [(0, 37, 37), (3, 37, 37), (1, 700, 50), (7, 700, 650), (2, 530, 1)])
+def test_attention_parity(tm, layer, P, chunk):
+    """The attention half over a P-token sequence, fed in chunks (prefill, then
+    one-token decode steps for chunk 1) through the cache, against the
+    oracle over the whole sequence: O per position within tolerance, the
+    residual bit for bit from O. Sliding caches take the smallest allowed
+    capacity (window + chunk - 1), so positions wrap around the ring."""
+    from oracle import attention_oracle as AO
+    from ternary_weight_moe_base_amd import synthetic
+
+    cfg = 5
+    glob = AO.is_global_layer(layer)
+    say(f"attention layer={layer} ({'global' if glob else 'sliding'}) P={P} chunk={chunk}")
+    W = synthetic.build_attention(cfg, layer, glob)
+    cap = P if glob else 512 + chunk - 1
+    kc, vc = tm.kv_cache(W, cap)
+    xb = ti.activations(cfg, P + 3)[3:]
+    X = bf16_dev(xb)
+    Ob = torch.empty((P, 2048), dtype=torch.float32, device="cuda")
+    Xo = torch.empty((P, 2048), dtype=torch.int16, device="cuda")
+    ws = ws_bytes(tm.attention_workspace_bytes(chunk, W))
+    for p0 in range(0, P, chunk):
+        T = min(chunk, P - p0)
+        tm.attention_forward(W, X[p0:p0 + T], p0, kc, vc, ws, O=Ob[p0:p0 + T], X_out=Xo[p0:p0 + T])
+    got_o, got_x = host(Ob), host(Xo).view(np.uint16)
+    ref = AO.attention_half(xb, *_attn_dense(cfg, layer), glob)
+    err = O.max_normalized_error(got_o, ref["o"])
+    say(f"  O max normalized error {err:.2e}")
+    assert err <= TOL
+    assert np.array_equal(got_x, O.residual_bf16(xb, got_o))
+
+
+def test_attention_decode_graph_replay(tm):
+    """One-token attention steps captured in a HIP graph (positions advance
+    through the cache between replays) equal the eager steps bit for bit."""
+    from ternary_weight_moe_base_amd import synthetic
+
+    W = synthetic.build_attention(5, 0, False)
+    xb = ti.activations(5, 12)
+    X = bf16_dev(xb)
+    outs = []
+    for graph in (False, True):
+        kc, vc = tm.kv_cache(W, 519)  # window + 8 - 1: the 8-token prefill below
+        ws = ws_bytes(tm.attention_workspace_bytes(1, W))
+        O_ = torch.zeros((1, 2048), dtype=torch.float32, device="cuda")
+        tm.attention_forward(W, X[:8], 0, kc, vc, ws_bytes(tm.attention_workspace_bytes(8, W)), O=torch.empty((8, 2048), dtype=torch.float32, device="cuda"))
+        res = []
+        for p in range(8, 12):
+            if graph:
+                g = torch.cuda.CUDAGraph()
+                s_ = torch.cuda.Stream()
+                s_.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s_):
+                    g.capture_begin()
+                    tm.attention_forward(W, X[p:p + 1], p, kc, vc, ws, O=O_)
+                    g.capture_end()
+                torch.cuda.synchronize()
+                g.replay()
+            else:
+                tm.attention_forward(W, X[p:p + 1], p, kc, vc, ws, O=O_)
+            res.append(host(O_).copy())
+        outs.append(res)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
 # -------------------------------------------------------------------- LM head
 def _lm_head(tm, xb, Wd, k, with_logits=True):
     T = xb.shape[0]
