@@ -1392,8 +1392,8 @@ static int run_down(hipStream_t st, const tmoe_moe_weights *W, const FfnWs &fw, 
   da.gd = gi;
   da.stream_w = P < 32 * W->n_experts;  // with many tiles per expert the caches serve the re-reads
   const bool walk = P < 4 * W->n_experts;
-  if (P < 1024) return run_down_r<2>(st, da, max_tiles, W->hidden, walk);
-  return run_down_r<4>(st, da, max_tiles, W->hidden, walk);
+  if (P < 1024) return run_down_r<4>(st, da, max_tiles, W->hidden, walk);
+  return run_down_r<8>(st, da, max_tiles, W->hidden, walk);  // 512 rows per item: h staged once for them
 }
 
 int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float clamp,

@@ -260,7 +260,7 @@ def test_router_near_ties_certified_in_fp64(tm, T):
 
 
 @pytest.mark.parametrize("k,E,H,T", [(1, 256, 2048, 33), (16, 256, 2048, 9), (8, 64, 256, 100), (4, 1000, 512, 7),
-                                     (64 // 8, 8, 256, 5)])
+                                     (64 // 8, 8, 256, 5), (8, 200, 512, 1100), (4, 72, 256, 1031)])
 def test_router_shapes(tm, k, E, H, T):
     say(f"router k={k} E={E} H={H} T={T}")
     g = np.random.default_rng(k + E + H + T)
