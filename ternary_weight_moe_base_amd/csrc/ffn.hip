@@ -698,29 +698,42 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
     accg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // the decode of step s + 1 is interleaved with the products of step s (VALU
+  // beside the matrix cores); the four token tiles run unconditionally
+  // (columns past the block hold a clamped pair and are not stored)
+  uint32_t pg[20], pu[20];
+  unpack8(gd[0], pg);
+  unpack8(ud[0], pu);
 #pragma unroll
   for (int s = 0; s < F; ++s) {
     if (s + kTbDepth - 1 < F) issue(s + kTbDepth - 1);
-    uint32_t pg[20], pu[20];
-    unpack8(gd[s], pg);
-    unpack8(ud[s], pu);
     // wait for this wavefront's loads of step s, then for everyone's
     static_assert(kTbDepth == 4, "wait_steps covers three steps in flight");
     wait_steps((F - 1 - s) < (kTbDepth - 1) ? (F - 1 - s) : (kTbDepth - 1), nj);
     __builtin_amdgcn_s_barrier();
     const char *buf = xs + (s % kTbDepth) * kTbStepBytes + (g * 16 + n) * 16;
+    uint32_t ng[20], nu[20];
+    if (s + 1 < F) {
+      unpack8(gd[s + 1], ng);
+      unpack8(ud[s + 1], nu);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (t < ntt) {
 #pragma unroll
-        for (int m = 0; m < 5; ++m) {
-          const u32x4 bx = lds16(buf + (t * 5 + m) * 1024);
-          accg[t] = mfma_bf16(pg + 4 * m, bx, accg[t]);
-          accu[t] = mfma_bf16(pu + 4 * m, bx, accu[t]);
-        }
+      for (int m = 0; m < 5; ++m) {
+        const u32x4 bx = lds16(buf + (t * 5 + m) * 1024);
+        accg[t] = mfma_bf16(pg + 4 * m, bx, accg[t]);
+        accu[t] = mfma_bf16(pu + 4 * m, bx, accu[t]);
       }
     }
     lds_barrier();  // the buffer of step s is refilled by the next issue
+    if (s + 1 < F) {
+#pragma unroll
+      for (int i = 0; i < 20; ++i) {
+        pg[i] = ng[i];
+        pu[i] = nu[i];
+      }
+    }
   }
 
 #pragma unroll
