@@ -104,12 +104,18 @@ __global__ __launch_bounds__(64) void rope_append_kernel(const float *qkv, int n
 }
 
 struct AttnArgs {
-  const float *qr;  // [T][nh][hd]
-  const float *kc, *vc;
+  const float *qr;  // [T][nh][hd] (fused one-token path: the raw q/k/v row instead)
+  float *kc, *vc;  // written by the fused one-token path (its own position)
   float *part;  // [T][nh][nsplit][hd + 2]: acc[hd], running max, sum
   int64_t cap, pos0;
   int T, nh, nkv, window, nsplit;
   float scale;
+  int rot;  // fused one-token path: rotated dimensions
+};
+// The one token's rotary cosines and sines (angles formed and reduced on the
+// host in fp64), a kernel argument of its own so it is read in place.
+struct RopeCS {
+  float cs[kAttnHeadDim / 2][2];
 };
 
 // grid (T * nkv, nsplit), block 256: wavefront w is query head g*4 + w of
@@ -119,13 +125,23 @@ struct AttnArgs {
 // the wavefront updates its running max and sum and rescales its
 // accumulator, and each lane adds the probability-weighted values of its two
 // dimensions.
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+//
+// FUSED (one token): the rotary and the cache append happen here instead of
+// in rope_append_kernel. Every workgroup rotates its four query heads from
+// the raw q/k/v row; the one workgroup whose range holds the token's own
+// position rotates the new key, stores key and value in the cache, and stages
+// them from LDS in place of that (not yet written) cache slot. No other
+// workgroup reads that slot: on sliding layers it held a position outside the
+// window, on global layers it was empty.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, RopeCS rcs) {
   constexpr int hd = kAttnHeadDim, HD4 = hd / 4;
   extern __shared__ __align__(16) float lds[];
   float(*ks)[kAttnKRow] = reinterpret_cast<float(*)[kAttnKRow]>(lds);
   float(*vs)[hd] = reinterpret_cast<float(*)[hd]>(lds + kAttnKeys * kAttnKRow);
   __shared__ float4 qs[kAttnGroup][HD4];
   __shared__ float ps[kAttnGroup][kAttnKeys];
+  __shared__ float4 knew[HD4], vnew[HD4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x / a.nkv, g = blockIdx.x - t * a.nkv;
   const int h = g * kAttnGroup + wave;
@@ -138,6 +154,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int64_t k1 = k0 + chunk < p + 1 ? k0 + chunk : p + 1;
   const float4 *kg = reinterpret_cast<const float4 *>(a.kc + (int64_t)g * a.cap * hd);
   const float4 *vg = reinterpret_cast<const float4 *>(a.vc + (int64_t)g * a.cap * hd);
+  const bool own = FUSED && k0 <= p && p < k1;  // this workgroup's range holds the new position
   if (threadIdx.x < kAttnGroup * HD4) {
     float4 q = reinterpret_cast<const float4 *>(a.qr + ((int64_t)t * a.nh + g * kAttnGroup) * hd)[threadIdx.x];
     q.x *= a.scale;
@@ -145,6 +162,36 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     q.z *= a.scale;
     q.w *= a.scale;
     qs[threadIdx.x / HD4][threadIdx.x % HD4] = q;
+  }
+  if (own && threadIdx.x < 2 * HD4) {
+    const float *row = a.qr + (int64_t)(a.nh + (threadIdx.x < HD4 ? 0 : a.nkv) + g) * hd;
+    const float4 v = reinterpret_cast<const float4 *>(row)[threadIdx.x % HD4];
+    if (threadIdx.x < HD4) knew[threadIdx.x] = v;
+    else vnew[threadIdx.x - HD4] = v;
+  }
+  if (FUSED && a.rot > 0) {
+    __syncthreads();
+    // pairs (i, i + rot/2) of the four query heads and of the new key
+    const int half = a.rot / 2;
+    float *qf = reinterpret_cast<float *>(qs), *kf = reinterpret_cast<float *>(knew);
+    for (int idx = threadIdx.x; idx < (kAttnGroup + 1) * half; idx += 256) {
+      const int hh = idx / half, i = idx - hh * half;
+      if (hh == kAttnGroup && !own) continue;
+      float *x = hh < kAttnGroup ? qf + hh * hd : kf;
+      const float c = rcs.cs[i][0], sn = rcs.cs[i][1];
+      const float x1 = x[i], x2 = x[i + half];
+      x[i] = fmaf(x1, c, -x2 * sn);
+      x[i + half] = fmaf(x2, c, x1 * sn);
+    }
+  }
+  if (own) {
+    __syncthreads();
+    const int64_t slot = p % a.cap;
+    if (threadIdx.x < HD4)
+      reinterpret_cast<float4 *>(a.kc)[((int64_t)g * a.cap + slot) * HD4 + threadIdx.x] = knew[threadIdx.x];
+    else if (threadIdx.x < 2 * HD4)
+      reinterpret_cast<float4 *>(a.vc)[((int64_t)g * a.cap + slot) * HD4 + threadIdx.x - HD4] =
+          vnew[threadIdx.x - HD4];
   }
   float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int64_t base = k0; base < k1; base += kAttnKeys) {
@@ -161,8 +208,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int c = threadIdx.x + 256 * r, j = c / HD4, d4 = c - j * HD4;
-      *reinterpret_cast<float4 *>(&ks[j][4 * d4]) = kv[r];
-      *reinterpret_cast<float4 *>(&vs[j][4 * d4]) = vv[r];
+      // the new position comes from LDS (its cache slot is being written by this workgroup)
+      float4 kx = kv[r], vx = vv[r];
+      if (own && base + j == p) {  // value selects (a select of the two sources' addresses spills kv, vv)
+        const float4 kn = knew[d4], vn = vnew[d4];
+        kx = make_float4(kn.x, kn.y, kn.z, kn.w);
+        vx = make_float4(vn.x, vn.y, vn.z, vn.w);
+      }
+      *reinterpret_cast<float4 *>(&ks[j][4 * d4]) = kx;
+      *reinterpret_cast<float4 *>(&vs[j][4 * d4]) = vx;
     }
     __syncthreads();
     float dot = 0.f;
@@ -270,13 +324,25 @@ int launch_attention(hipStream_t st, const tmoe_attn_weights &sh, const uint16_t
   if (rc) return rc;
   if (T > 0x7FFFFFFF / nkv) return fail(TMOE_E_UNSUPPORTED, "T too large");
   const int rot = sh.window > 0 ? sh.rotary_dim : 0;
-  RopeFreq fr{};
-  for (int i = 0; i < rot / 2; ++i) fr.inv[i] = std::pow(sh.rope_base, -2.0 * i / rot);
-  hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)T, (unsigned)(nh + 2 * nkv)), dim3(64), 0, st, qkv, nh, nkv,
-                     rot, fr, pos0, qr, kc, vc, cap);
-  TMOE_LAUNCHED("rope_append");
+  const bool fused = T == 1;
   AttnArgs a;
-  a.qr = qr;
+  a.rot = rot;
+  RopeCS rcs{};
+  if (fused) {
+    // one token: its angles here in fp64 (reduced, then fp32); rotary and append in the attention kernel
+    for (int i = 0; i < rot / 2; ++i) {
+      const double ang = (double)pos0 * std::pow(sh.rope_base, -2.0 * i / rot);
+      rcs.cs[i][0] = (float)std::cos(ang);
+      rcs.cs[i][1] = (float)std::sin(ang);
+    }
+  } else {
+    RopeFreq fr{};
+    for (int i = 0; i < rot / 2; ++i) fr.inv[i] = std::pow(sh.rope_base, -2.0 * i / rot);
+    hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)T, (unsigned)(nh + 2 * nkv)), dim3(64), 0, st, qkv, nh, nkv,
+                       rot, fr, pos0, qr, kc, vc, cap);
+    TMOE_LAUNCHED("rope_append");
+  }
+  a.qr = fused ? qkv : qr;
   a.kc = kc;
   a.vc = vc;
   a.part = part;
@@ -288,10 +354,17 @@ int launch_attention(hipStream_t st, const tmoe_attn_weights &sh, const uint16_t
   a.window = sh.window;
   a.nsplit = nsplit;
   a.scale = 1.0f / sqrtf((float)hd);
-  rc = allow_lds<attn_kernel>(kAttnLds);
-  if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_ATTENTION, attn_kernel, dim3((unsigned)(T * nkv), (unsigned)nsplit), dim3(256), kAttnLds, st,
-              a);
+  if (fused) {
+    rc = allow_lds<attn_kernel<true>>(kAttnLds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_ATTENTION, attn_kernel<true>, dim3((unsigned)nkv, (unsigned)nsplit), dim3(256), kAttnLds,
+                st, a, rcs);
+  } else {
+    rc = allow_lds<attn_kernel<false>>(kAttnLds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_ATTENTION, attn_kernel<false>, dim3((unsigned)(T * nkv), (unsigned)nsplit), dim3(256),
+                kAttnLds, st, a, rcs);
+  }
   TMOE_LAUNCHED("attention");
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(T * nh)), dim3(hd), 0, st, part, nsplit, attn);
   TMOE_LAUNCHED("attention_merge");
