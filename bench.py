@@ -48,6 +48,9 @@ WORKLOADS = {
     # one token through the whole 24-layer stack, attention then MoE per layer, at context 4096
     10: dict(name="model24_decode_T1_ctx4096", tokens=1, bias=None, layers=24, steps=100, warmup=4, model_cfg=5,
              attention=True, moe=True, context=4096),
+    # config 10 plus the output head: the next token's top-16 over the 151,936-token vocabulary
+    11: dict(name="model24_lmhead_decode_T1_ctx4096", tokens=1, bias=None, layers=24, steps=100, warmup=4, model_cfg=5,
+             attention=True, moe=True, context=4096, head=True),
     # the model's untied bf16 output head (151,936 x 2048, 622 MB) and its top-16, one token per step
     7: dict(name="lm_head_topk16_T1", tokens=1, bias=None, layers=1, steps=400, warmup=10, model_cfg=5, lm_head=True),
 }
@@ -249,12 +252,21 @@ def main_attention(args, wl: dict):
     xw = torch.empty((1, H), dtype=torch.int16, device=dev)
     wsa = torch.empty(tm.attention_workspace_bytes(1, attn[0]), dtype=torch.uint8, device=dev)
     wsm = torch.empty(tm.moe_workspace_bytes(1, moe[0]) if moe else 16, dtype=torch.uint8, device=dev)
+    head = wl.get("head", False)
+    if head:
+        from tmoe_inputs import VOCAB
+        table = synthetic.lm_head_table(mcfg)
+        wsh = torch.empty(tm.lm_head_workspace_bytes(1, VOCAB, LMH_K), dtype=torch.uint8, device=dev)
+        nxt = torch.empty((W_ + K, 1, LMH_K), dtype=torch.int32, device=dev)
+        nval = torch.empty((1, LMH_K), dtype=torch.float32, device=dev)
 
     def step(i):
         for l in range(L):
             tm.attention_forward(attn[l], X[i] if l == 0 else xw, ctx + i, *caches[l], wsa, X_out=xw)
             if moe:
                 tm.moe_forward(moe[l], xw, None, wsm, resid_out=xw)
+        if head:
+            tm.lm_head_topk(xw, table, LMH_K, nxt[i], nval, wsh)
 
     for i in range(W_):
         step(i)
@@ -281,7 +293,7 @@ def main_attention(args, wl: dict):
 
     # per-kernel durations over the same steps launched again (eagerly, same positions)
     kern = {}
-    names = ATTN_KERNELS + (DECODE_KERNELS if moe else ())
+    names = ATTN_KERNELS + (DECODE_KERNELS if moe else ()) + (("lmh_logits",) if head else ())
     cap_n = K * L * 2
     for name in names:
         tm.profile_begin(name, cap_n)
@@ -307,6 +319,8 @@ def main_attention(args, wl: dict):
         b = 8 * 2 * (PACKED_GU + 4 * I) + H * 2
     elif dom == "down":
         b = 8 * (PACKED_D + 4 * H)
+    elif dom == "lmh_logits":
+        b = 151936 * H * 2 + H * 2
     else:
         b = ROUTER_BYTES + H * 2
     mean_s = float(np.mean(kern[dom])) * 1e-3
@@ -320,7 +334,8 @@ def main_attention(args, wl: dict):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "tokens_per_step": 1, "layers_per_step": L, "context": ctx,
                    "global_layers": n_glob, "sliding_window": 512, "heads": "16 query, 4 key/value, 128 wide",
-                   "parts": "attention + MoE" if moe else "attention", "hip_graph": use_graph},
+                   "parts": ("attention + MoE" if moe else "attention") + (" + LM head top-16" if head else ""),
+                   "hip_graph": use_graph},
         "token_latency_us": 1e6 * elapsed / K,
         "roofline": roof,
         "cpu_baseline": None,
