@@ -75,6 +75,48 @@ __device__ inline void scatter_block(const uint32_t *bits, const int *base, cons
   }
 }
 
+// k <= KM (the layer's top-k): a thread reads its token's k choices once, all
+// loads in flight together, and builds the bitmask and scatters from
+// registers (the generic loops above reload idx after every store, since the
+// stores may alias it).
+template <int KM>
+__device__ inline void load_choices(const int32_t *idx, int64_t T, int k, int64_t t0, int (&ch)[KM]) {
+  const int64_t t = t0 + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) ch[j] = (t < T && j < k) ? idx[t * k + j] : -1;
+}
+
+template <int KM>
+__device__ inline void build_bitmask_r(uint32_t *bits, const int (&ch)[KM], int E) {
+  for (int i = threadIdx.x; i < E * 8; i += kBlockTok) bits[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int e = ch[j];
+    if (e >= 0 && e < E) atomicOr(&bits[e * 8 + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+  }
+  __syncthreads();
+}
+
+template <int KM>
+__device__ inline void scatter_block_r(const uint32_t *bits, const int *base, const int (&ch)[KM], int64_t T, int k,
+                                       int E, int64_t t0, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos) {
+  const int64_t t = t0 + threadIdx.x;
+  if (t >= T) return;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j >= k) break;
+    const int e = ch[j];
+    int p = -1;
+    if (e >= 0 && e < E) {
+      p = base[e] + block_rank(bits, e, threadIdx.x);
+      sorted_token[p] = (int32_t)t;
+      sorted_slot[p] = j;
+    }
+    pos[t * k + j] = p;
+  }
+}
+
 // Work tiles of up to 16 grouped pairs of one expert, in expert order, from
 // the per-expert counts c[] and offsets off[] (tc[], tmp[]: LDS scratch).
 __device__ inline void write_tiles(const int *c, const int *off, int E, int *tc, int *tmp, int32_t *tiles,
@@ -88,7 +130,8 @@ __device__ inline void write_tiles(const int *c, const int *off, int E, int *tc,
   if (threadIdx.x == 0) *ntiles = total;
 }
 
-// Whole grouping in one workgroup (T <= 256).
+// Whole grouping in one workgroup (T <= 256). KM > 0: k <= KM, choices in registers.
+template <int KM>
 __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *idx, int64_t T, int k, int E,
                                                                 int32_t *counts, int32_t *offsets,
                                                                 int32_t *sorted_token, int32_t *sorted_slot,
@@ -96,7 +139,13 @@ __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *i
   __shared__ uint32_t bits[1024 * 8];
   __shared__ int cnt[1024], c0[1024], tc[1024];
   __shared__ int tmp[kBlockTok];
-  build_bitmask(bits, idx, T, k, E, 0);
+  int ch[KM > 0 ? KM : 1];
+  if constexpr (KM > 0) {
+    load_choices<KM>(idx, T, k, 0, ch);
+    build_bitmask_r<KM>(bits, ch, E);
+  } else {
+    build_bitmask(bits, idx, T, k, E, 0);
+  }
   for (int e = threadIdx.x; e < E; e += kBlockTok) {
     int c = block_count(bits, e);
     cnt[e] = c;
@@ -107,14 +156,24 @@ __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *i
   int total = block_exclusive_scan<kBlockTok>(cnt, E, tmp);
   for (int e = threadIdx.x; e < E; e += kBlockTok) offsets[e] = cnt[e];
   if (threadIdx.x == 0) offsets[E] = total;
-  scatter_block(bits, cnt, idx, T, k, E, 0, sorted_token, sorted_slot, pos);
+  if constexpr (KM > 0)
+    scatter_block_r<KM>(bits, cnt, ch, T, k, E, 0, sorted_token, sorted_slot, pos);
+  else
+    scatter_block(bits, cnt, idx, T, k, E, 0, sorted_token, sorted_slot, pos);
   if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles);
 }
 
+template <int KM>
 __global__ __launch_bounds__(kBlockTok) void group_count_kernel(const int32_t *idx, int64_t T, int k, int E,
                                                                 int32_t *bcount) {
   __shared__ uint32_t bits[1024 * 8];
-  build_bitmask(bits, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok);
+  if constexpr (KM > 0) {
+    int ch[KM];
+    load_choices<KM>(idx, T, k, (int64_t)blockIdx.x * kBlockTok, ch);
+    build_bitmask_r<KM>(bits, ch, E);
+  } else {
+    build_bitmask(bits, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok);
+  }
   for (int e = threadIdx.x; e < E; e += kBlockTok) bcount[(int64_t)blockIdx.x * E + e] = block_count(bits, e);
 }
 
@@ -140,6 +199,7 @@ __global__ __launch_bounds__(kBlockTok) void group_scan_kernel(const int32_t *bc
   if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles);
 }
 
+template <int KM>
 __global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t *idx, int64_t T, int k, int E,
                                                                   const int32_t *offsets, const int32_t *bbase,
                                                                   int32_t *sorted_token, int32_t *sorted_slot,
@@ -147,30 +207,50 @@ __global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t 
   __shared__ uint32_t bits[1024 * 8];
   __shared__ int base[1024];
   for (int e = threadIdx.x; e < E; e += kBlockTok) base[e] = offsets[e] + bbase[(int64_t)blockIdx.x * E + e];
-  build_bitmask(bits, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok);
-  scatter_block(bits, base, idx, T, k, E, (int64_t)blockIdx.x * kBlockTok, sorted_token, sorted_slot, pos);
+  const int64_t t0 = (int64_t)blockIdx.x * kBlockTok;
+  if constexpr (KM > 0) {
+    int ch[KM];
+    load_choices<KM>(idx, T, k, t0, ch);
+    build_bitmask_r<KM>(bits, ch, E);
+    scatter_block_r<KM>(bits, base, ch, T, k, E, t0, sorted_token, sorted_slot, pos);
+  } else {
+    build_bitmask(bits, idx, T, k, E, t0);
+    scatter_block(bits, base, idx, T, k, E, t0, sorted_token, sorted_slot, pos);
+  }
 }
 
-int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
-                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw, int32_t *tiles,
-                 int32_t *ntiles) {
+template <int KM>
+static int launch_group_k(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts,
+                          int32_t *offsets, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos,
+                          const GroupWs &gw, int32_t *tiles, int32_t *ntiles) {
   const int64_t nb = cdiv(T, kBlockTok);
   if (nb <= 1) {
-    TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_fused_kernel, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts,
+    TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_fused_kernel<KM>, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts,
                 offsets, sorted_token, sorted_slot, pos, tiles, ntiles);
     TMOE_LAUNCHED("group_fused");
     return TMOE_OK;
   }
   if (nb > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
-  TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_count_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, gw.bcount);
+  TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_count_kernel<KM>, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E,
+              gw.bcount);
   TMOE_LAUNCHED("group_count");
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kBlockTok), 0, st, gw.bcount, (int)nb, (int)E, gw.bbase, counts,
                      offsets, tiles, ntiles);
   TMOE_LAUNCHED("group_scan");
-  hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, offsets,
+  hipLaunchKernelGGL(group_scatter_kernel<KM>, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, offsets,
                      gw.bbase, sorted_token, sorted_slot, pos);
   TMOE_LAUNCHED("group_scatter");
   return TMOE_OK;
+}
+
+int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
+                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw, int32_t *tiles,
+                 int32_t *ntiles) {
+  if (k <= 8)
+    return launch_group_k<8>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles);
+  if (k <= 16)
+    return launch_group_k<16>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles);
+  return launch_group_k<0>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles);
 }
 
 }  // namespace tmoe

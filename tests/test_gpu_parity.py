@@ -284,7 +284,8 @@ def _group(tm, idx, E):
 
 @pytest.mark.parametrize("T,k,E,mode", [(1, 8, 256, "rand"), (7, 8, 256, "rand"), (64, 8, 256, "zipf"),
                                         (256, 8, 256, "rand"), (257, 8, 256, "rand"), (1000, 1, 64, "rand"),
-                                        (4096, 8, 256, "rand"), (300, 16, 1000, "rand"), (600, 8, 256, "one")])
+                                        (4096, 8, 256, "rand"), (300, 16, 1000, "rand"), (600, 8, 256, "one"),
+                                        (50, 40, 128, "rand"), (700, 12, 64, "rand")])
 def test_grouping_parity(tm, T, k, E, mode):
     say(f"group T={T} k={k} E={E} {mode}")
     g = np.random.default_rng(T * 31 + k + E)
