@@ -2,6 +2,7 @@
 inputs. Integer and index results must match bit for bit; floating-point
 results within a max normalized error (per row) of 2e-5."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -817,3 +818,22 @@ def test_lm_head_full_vocabulary(tm):
     assert O.max_normalized_error(val, rval) <= TOL
     assert O.max_normalized_error(lg, rL) <= TOL
     say(f"  top-{k} ids {idx[0].tolist()}")
+
+
+# ------------------------------------------------------------- native driver
+@pytest.mark.parametrize("args", [["layer", "--tokens", "1", "--layers", "2", "--steps", "20", "--warmup", "2"],
+                                  ["layer", "--tokens", "64", "--layers", "1", "--steps", "5", "--warmup", "1"],
+                                  ["layer", "--tokens", "1", "--layers", "1", "--steps", "5", "--warmup", "1",
+                                   "--host-experts", "1"],
+                                  ["lmhead", "--vocab", "20000", "--steps", "5", "--warmup", "1"],
+                                  ["copy", "--mib", "64", "--steps", "3"]])
+def test_native_driver_runs(args):
+    """The C-ABI driven with no Python in the process: the native driver builds
+    its synthetic model through the library and runs each workload."""
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.dirname(__file__)), "ternary_weight_moe_base_amd", "tmoe_run")
+    say(f"tmoe_run {' '.join(args)}")
+    r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr
+    assert ("us/step" in r.stdout) or ("GB/s" in r.stdout), r.stdout
