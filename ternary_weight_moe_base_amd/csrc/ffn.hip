@@ -718,13 +718,14 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
       unpack8(ud[s + 1], nu);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int m = 0; m < 5; ++m) {
+      u32x4 bx[4];
 #pragma unroll
-      for (int m = 0; m < 5; ++m) {
-        const u32x4 bx = lds16(buf + (t * 5 + m) * 1024);
-        accg[t] = mfma_bf16(pg + 4 * m, bx, accg[t]);
-        accu[t] = mfma_bf16(pu + 4 * m, bx, accu[t]);
-      }
+      for (int t = 0; t < 4; ++t) bx[t] = lds16(buf + (t * 5 + m) * 1024);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) accg[t] = mfma_bf16(pg + 4 * m, bx[t], accg[t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) accu[t] = mfma_bf16(pu + 4 * m, bx[t], accu[t]);
     }
     lds_barrier();  // the buffer of step s is refilled by the next issue
     if (s + 1 < F) {
