@@ -1265,6 +1265,8 @@ __global__ __launch_bounds__(256) void linear3_kernel(Linear3Args a) {
 
 // ------------------------------------------------------------------ combine
 // grid (T, H / 512), 128 threads x one float4 each; fixed slot order j = 0..k-1.
+// NT: the expert outputs are far larger than the caches and read once, non-temporally.
+template <bool NT>
 __global__ __launch_bounds__(128) void combine_kernel(const float *O, const float *w, const int32_t *pos, int k,
                                                        int H, float *Y, const uint16_t *resid_in,
                                                        uint16_t *resid_out) {
@@ -1277,7 +1279,13 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *O, const floa
     const int p = pos[t * k + j];
     if (p < 0) continue;
     const float wj = w[t * k + j];
-    const float4 o = reinterpret_cast<const float4 *>(O + (int64_t)p * H)[c];
+    float4 o;
+    if constexpr (NT) {
+      const f32x4 o4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(O + (int64_t)p * H) + c);
+      o = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    } else {
+      o = reinterpret_cast<const float4 *>(O + (int64_t)p * H)[c];
+    }
     acc.x = fmaf(wj, o.x, acc.x);
     acc.y = fmaf(wj, o.y, acc.y);
     acc.z = fmaf(wj, o.z, acc.z);
@@ -1585,8 +1593,13 @@ int launch_linear3(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N,
 int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,
                    float *Y, const uint16_t *resid_in, uint16_t *resid_out) {
   if (T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
-  TMOE_LAUNCH(TMOE_KERNEL_COMBINE, combine_kernel, dim3((unsigned)T, (unsigned)cdiv(H, 512)), dim3(128), 0, st, O, w,
-              pos, k, (int)H, Y, resid_in, resid_out);
+  const dim3 grid((unsigned)T, (unsigned)cdiv(H, 512));
+  if ((double)T * k * H * 4 > 64.0 * (1 << 20))  // expert outputs beyond 64 MB: stream them
+    TMOE_LAUNCH(TMOE_KERNEL_COMBINE, combine_kernel<true>, grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y, resid_in,
+                resid_out);
+  else
+    TMOE_LAUNCH(TMOE_KERNEL_COMBINE, combine_kernel<false>, grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y, resid_in,
+                resid_out);
   TMOE_LAUNCHED("combine");
   return TMOE_OK;
 }
