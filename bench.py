@@ -77,7 +77,7 @@ def roofline(name, ms, n_hit, T, cfg, bias):
     x_b, y_b = T * H * 2, T * H * (2 if stack else 4)
     flops = None
     if name == "router_logits":
-        b = np.full(len(n_hit), ROUTER_BYTES + x_b + (E * 4 if bias else 0) + (T * K_TOP * 8 if T <= 16 else 0))
+        b = np.full(len(n_hit), ROUTER_BYTES + x_b + (E * 4 if bias else 0))
         flops, fpeak = 2.0 * T * E * H, FP64_PEAK_TFLOPS
     elif name == "gateup":
         b = n_hit * 2 * (PACKED_GU + 4 * I) + x_b

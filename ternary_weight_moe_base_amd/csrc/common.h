@@ -164,11 +164,11 @@ struct RouterWs {
 };
 size_t router_ws_bytes(int64_t T, int64_t E);
 RouterWs router_ws_carve(void *ws, int64_t T, int64_t E);
-// Logits (fp64 VALU for T <= 16, fp64 matrix cores above) and the certified
+// Logits (fp64 VALU for T <= 64, fp64 matrix cores above) and the certified
 // top-k with its double-double fall-back (two kernels).
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                   int64_t E, int k, int32_t *idx, float *w, float *logits_out, int32_t *n_fixup, const RouterWs &rw);
-// Logits and per-token bound slots only, T <= 16 (the decode layer path certifies
+// Logits and per-token bound slots only (the decode layer path, T <= 3, certifies
 // the top-k in the gate/up kernel's prologue). Returns the error-bound depth in
 // *depth and the bound slots per token in *nb.
 int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
