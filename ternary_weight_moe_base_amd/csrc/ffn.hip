@@ -24,6 +24,11 @@
 
 namespace tmoe {
 
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt not waited)
+#define TMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family parts
+constexpr int kBufWord3 = 0x00020000;
+
 // ---------------------------------------------------------- trit decoding
 __device__ __forceinline__ uint32_t fma16x2(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, a),
@@ -414,9 +419,10 @@ __device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const 
 // them (and for both matrices). blockIdx.x = work tile (expert, <= 16 pairs),
 // blockIdx.y = group of (4 / KS) * R row tiles.
 // RNPL > 0: decode path with the routing prologue (experts per lane of its top-k).
-template <int F, int RT, int KS, int RNPL, int R>
+template <int F, int RT, int KS, int RNPL, int R, int NW>
 __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id, int ry) {
   static_assert(KS == 1 || R == 1, "row tiles per wavefront need the full K range");
+  static_assert(NW == 4 || (KS == 1 && RNPL == 0), "eight wavefronts only on the batched full-K path");
   int e, start, cnt;
   const int32_t *toks;
   const int rs0 = lds_row_bytes(a.gx.slots);
@@ -431,13 +437,13 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
   } else {
     const int tile = tile_id;
     const int4 td = reinterpret_cast<const int4 *>(a.tiles)[tile];
-    e = td.x;
-    start = td.y;
-    cnt = td.z;
+    e = __builtin_amdgcn_readfirstlane(td.x);
+    start = __builtin_amdgcn_readfirstlane(td.y);
+    cnt = __builtin_amdgcn_readfirstlane(td.z);
     toks = a.sorted_token + start;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int RTB = 4 / KS;
+  constexpr int RTB = NW / KS;
   constexpr int M = 5 * F + tail_mfmas(RT);
   constexpr int SMAX = (F + KS - 1) / KS;
   const int rtb = ry * RTB * R + wave / KS;  // row tiles rtb + RTB r
@@ -445,25 +451,62 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
   const int rs = lds_row_bytes(a.gx.slots);
   char *xs = smem;  // [17][rs]; row 16 = zeros
 
-  // weights first: all loads of this wavefront are in flight while x is staged
+  if constexpr (RNPL == 0) {
+    // Activations of the tile's pairs (natural order = operand order for
+    // H = 2048), by buffer loads straight into LDS issued before the weights:
+    // loads complete in issue order, so the wait for these leaves the weights
+    // in flight, and each K step below waits only for its own weights. (The
+    // flat-encoded global form would make the compiler wait for every load
+    // before the first product.) Wavefront w copies rows w, w + NW, ...; each
+    // row is four 1 KB slices (the padding inputs 2048..2079 were cleared at
+    // launch). The buffer resource's 4096-byte range bounds every read.
+    static_assert(16 % NW == 0, "rows per wavefront");
+    const int tokv = (lane & 15) < cnt ? toks[lane & 15] : 0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int tks[16 / NW];
+#pragma unroll
+    for (int j = 0; j < 16 / NW; ++j) tks[j] = __builtin_amdgcn_readlane(tokv, wv + NW * j);
+#pragma unroll
+    for (int j = 0; j < 16 / NW; ++j) {
+      const int nrow = wv + NW * j;
+      if (nrow < cnt) {
+        const int tk = tks[j];
+        const __amdgpu_buffer_rsrc_t row =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(a.X + (int64_t)tk * 2048), (short)0, 4096, kBufWord3);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              row, (__attribute__((address_space(3))) void *)(xs + nrow * rs + c * 1024), 16, lane * 16 + c * 1024, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the weight loads stay behind these
+  }
+
+  // then the weights: all loads of this wavefront are in flight while x lands
   const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
   const int s0 = kp * F / KS, s1 = (kp + 1) * F / KS;
   const bool tail_here = RT > 0 && kp == KS - 1;
   uint2 gd[R][SMAX], ud[R][SMAX];
   uint32_t gdw[R], gsh[R], udw[R], ush[R];
   float4 sg[R], su[R];
+  // issued in the order the K steps consume them, so step 0 can start while
+  // later steps are still arriving
+#pragma unroll
+  for (int i = 0; i < SMAX; ++i) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t off = (int64_t)e * a.stride_gu + (int64_t)(rtb + RTB * r) * tbytes + (int64_t)(s0 + i) * 512;
+      if (s0 + i < s1) {
+        gd[r][i] = ldw8(a.gate_p + off + lane * 8);
+        ud[r][i] = ldw8(a.up_p + off + lane * 8);
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int rt = rtb + RTB * r;
     const uint8_t *gt = a.gate_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
     const uint8_t *ut = a.up_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
-#pragma unroll
-    for (int i = 0; i < SMAX; ++i) {
-      if (s0 + i < s1) {
-        gd[r][i] = ldw8(gt + (int64_t)(s0 + i) * 512 + lane * 8);
-        ud[r][i] = ldw8(ut + (int64_t)(s0 + i) * 512 + lane * 8);
-      }
-    }
     gdw[r] = gsh[r] = udw[r] = ush[r] = 0;
     if (tail_here) {
       load_tail<RT>(gt, F, lane, gdw[r], gsh[r]);
@@ -476,22 +519,10 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
   }
 
   if constexpr (RNPL == 0) {
-    // activations of the tile's pairs (natural order = operand order for H = 2048)
-    constexpr int vec = 4 * M;
-    const int kv = (int)(a.gx.K / 8);
-    copy16<256>(
-        cnt * vec,
-        [&](int i) {
-          const int n = i / vec, c = i - n * vec;
-          return c < kv ? reinterpret_cast<const uint4 *>(a.X + (int64_t)toks[n] * a.gx.K)[c]
-                        : make_uint4(0, 0, 0, 0);
-        },
-        [&](int i) {
-          const int n = i / vec, c = i - n * vec;
-          return reinterpret_cast<uint4 *>(xs + n * rs + c * 16);
-        });
-    zero_row(xs + 16 * rs, a.gx.slots, threadIdx.x, 256);
-    __syncthreads();
+    // every wavefront has at least 2 (F / KS) R weight loads behind its copies
+    __builtin_amdgcn_sched_barrier(0);
+    TMOE_WAIT_VM(2 * (F / KS) * R);
+    __builtin_amdgcn_s_barrier();
   }
   // (with the routing prologue the activations were staged before its last barrier)
 
@@ -590,17 +621,26 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
 // Decode (RNPL > 0): the grid is (hit experts, row-tile groups). Otherwise the
 // grid is a fixed number of workgroups that walk the (work tile, row-tile
 // group) items, so no workgroup is launched for a tile that does not exist.
-template <int F, int RT, int KS, int RNPL, int R>
-__global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
+template <int F, int RT, int KS, int RNPL, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void gateup_kernel(GateUpArgs a) {
   extern __shared__ __align__(16) char smem[];
   if constexpr (RNPL > 0) {
-    gateup_work<F, RT, KS, RNPL, R>(a, smem, blockIdx.x, blockIdx.y);
+    gateup_work<F, RT, KS, RNPL, R, NW>(a, smem, blockIdx.x, blockIdx.y);
   } else {
-    const int groups = a.I / 16 / (4 / KS) / R;
+    static_assert(F == 13 && RT == 0, "activation rows are copied as 2048 inputs");
+    // padding inputs 2048..2079 of the 16 token rows, and the zero row 16
+    const int rs = lds_row_bytes(a.gx.slots), nc = a.gx.slots / 8;
+    for (int i = threadIdx.x; i < 16 * (nc - 256) + nc; i += 64 * NW) {
+      const int row = i < 16 * (nc - 256) ? i / (nc - 256) : 16;
+      const int c = row < 16 ? 256 + i % (nc - 256) : i - 16 * (nc - 256);
+      *reinterpret_cast<uint4 *>(smem + row * rs + c * 16) = make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    const int groups = a.I / 16 / (NW / KS) / R;
     const int nitems = *a.ntiles * groups;
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
       const int tile = item / groups;
-      gateup_work<F, RT, KS, RNPL, R>(a, smem, tile, item - tile * groups);
+      gateup_work<F, RT, KS, RNPL, R, NW>(a, smem, tile, item - tile * groups);
       __syncthreads();  // the staged activations are reused by the next item
     }
   }
@@ -618,8 +658,6 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
 // K are read from a valid address (their trits are zero).
 constexpr int kTbWaves = 8, kTbDepth = 4, kTbStepBytes = 4 * 5 * 64 * 16;
 
-// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt not waited)
-#define TMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 // Waits until at most `later` steps of this wavefront's loads (nj per step) are in flight.
 __device__ __forceinline__ void wait_steps(int later, int nj) {
   switch (later * 4 + nj) {
@@ -1341,16 +1379,16 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   return f;
 }
 
-template <int F, int RT, int KS, int RNPL, int R = 1>
+template <int F, int RT, int KS, int RNPL, int R = 1, int NW = 4>
 static int run_gateup(hipStream_t st, const GateUpArgs &a, int64_t max_tiles, int I, bool walk = true) {
   const int rs = lds_row_bytes(a.gx.slots);
   size_t lds = (size_t)17 * rs + (KS > 1 ? 4 * 64 * 8 * 4 : 0);
-  const int64_t groups = I / 16 / (4 / KS) / R;
+  const int64_t groups = I / 16 / (NW / KS) / R;
   dim3 grid((unsigned)max_tiles, (unsigned)groups);
   if (RNPL == 0) grid = dim3(walk_grid(max_tiles * groups, walk), 1);
-  int rc = allow_lds<gateup_kernel<F, RT, KS, RNPL, R>>(lds);
+  int rc = allow_lds<gateup_kernel<F, RT, KS, RNPL, R, NW>>(lds);
   if (rc) return rc;
-  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS, RNPL, R>), grid, dim3(256), lds, st, a);
+  TMOE_LAUNCH(TMOE_KERNEL_GATEUP, (gateup_kernel<F, RT, KS, RNPL, R, NW>), grid, dim3(64 * NW), lds, st, a);
   TMOE_LAUNCHED("gateup");
   return TMOE_OK;
 }
@@ -1511,7 +1549,7 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   else if (P < 1024)
     rc = run_gateup<13, 0, 1, 0, 1>(st, ga, max_tiles, (int)I, P < 4 * E);
   else
-    rc = run_gateup<13, 0, 1, 0, 2>(st, ga, max_tiles, (int)I, P < 4 * E);
+    rc = run_gateup<13, 0, 1, 0, 1, 8>(st, ga, max_tiles, (int)I, P < 4 * E);
   if (rc) return rc;
 
   return run_down(st, W, fw, P, max_tiles, O);

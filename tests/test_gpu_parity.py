@@ -345,7 +345,8 @@ def _run_layer(tm, W, xb, clamp=7.0):
 
 
 @pytest.mark.parametrize("cfg,T,bias_kind,clamp", [(2, 1, None, 7.0), (2, 1, None, math.inf), (3, 64, "zipf", 7.0),
-                                                   (2, 5, None, 7.0), (2, 4, None, 7.0), (3, 16, "zipf", 7.0)])
+                                                   (2, 5, None, 7.0), (2, 4, None, 7.0), (3, 16, "zipf", 7.0),
+                                                   (5, 256, None, 7.0)])
 def test_layer_parity(tm, layers, cfg, T, bias_kind, clamp):
     say(f"layer cfg={cfg} T={T} clamp={clamp}")
     W = layers(cfg, 0, bias_kind)
@@ -379,11 +380,12 @@ def test_layer_parity(tm, layers, cfg, T, bias_kind, clamp):
 
 
 @pytest.mark.parametrize("E,k,T", [(8, 8, 3), (8, 8, 6), (8, 2, 16), (16, 4, 9), (16, 4, 17), (16, 12, 3),
-                                   (32, 16, 2)])
+                                   (32, 16, 2), (64, 8, 200), (128, 8, 130)])
 def test_layer_few_experts(tm, E, k, T):
     """Edge cases of both paths: more (token, slot) pairs than experts, every
     expert hit, up to 16 pairs per tile; on the decode path (T <= 3) the fused
-    combine (T k <= 32) and the separate one (T k > 32)."""
+    combine (T k <= 32) and the separate one (T k > 32); batches of 1024 or
+    more pairs (eight-wavefront gate/up workgroups, several tiles per expert)."""
     from ternary_weight_moe_base_amd import synthetic
     say(f"layer E={E} k={k} T={T}")
     cfg = 2
