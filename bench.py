@@ -32,6 +32,10 @@ EXPERT_BYTES = 2 * PACKED_GU + PACKED_D + 4 * (2 * I + H)  # 643,072
 ROUTER_BYTES = E * H * 4
 
 WORKLOADS = {
+    # the 2048 -> 512 ternary linear, streamed: 2048 distinct 512 x 2048 matrices stacked into one
+    # 1,048,576 x 2048 operand (436 MB packed, past the 256 MB last-level cache), 4 tokens per launch
+    1: dict(name="ternary_linear_T4_streamed_2048x512x2048", tokens=4, bias=None, layers=1, steps=50, warmup=5,
+            linear=True, mats=2048),
     2: dict(name="moe_layer_decode_T1", tokens=1, bias=None, layers=24, steps=2400, warmup=48),
     3: dict(name="moe_layer_decode_T64_zipf1.1", tokens=64, bias="zipf", layers=24, steps=480, warmup=48),
     4: dict(name="moe_layer_prefill_T4096_uniform", tokens=4096, bias="uniform", layers=4, steps=40, warmup=4),
@@ -210,6 +214,120 @@ def cpu_baseline_lm_head(wl: dict, budget_s: float = 12.0):
               f"151,936-token table; {timed:.1f} s of oracle time; the table drawn beforehand, untimed")
     return {"value": tokens / timed, "unit": "tokens/s", "cores": blas if blas > 1 else 1, "host_cpus": threads,
             "kind": "oracle", "sample": sample}
+
+
+def cpu_baseline_linear(wl: dict, budget_s: float = 12.0):
+    """The oracle's ternary_linear on this host, matrix by matrix of the
+    streamed operand, until budget_s seconds of oracle time; each matrix is
+    drawn and ternarized before its timed call (untimed)."""
+    import numpy as np
+
+    import oracle as O
+    import tmoe_inputs as ti
+
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    x = O.bf16_to_f64(ti.activations(1, wl["tokens"]))
+    done, timed = 0, 0.0
+    for q in range(wl["mats"]):
+        t, sc = O.ternarize_absmean(ti.expert_matrix(1, q // 1024, q % 1024, ti.MAT_GATE))
+        t0 = time.perf_counter()
+        O.ternary_linear(t, sc, x)
+        timed += time.perf_counter() - t0
+        done += 1
+        if timed >= budget_s:
+            break
+    per_operand = timed / done * wl["mats"]
+    sample = (f"{done} of the {wl['mats']} matrices of the {wl['name']} operand through the oracle's ternary_linear "
+              f"({wl['tokens']} tokens), {timed:.1f} s of oracle time, scaled to the whole operand; weights drawn "
+              f"and ternarized beforehand, untimed")
+    return {"value": wl["tokens"] / per_operand, "unit": "tokens/s", "cores": blas if blas > 1 else 1,
+            "host_cpus": threads, "kind": "oracle", "sample": sample}
+
+
+def main_linear(args, wl: dict):
+    import numpy as np
+    import torch
+
+    ensure_built()
+    import ternary_weight_moe_base_amd as tm
+    from ternary_weight_moe_base_amd import synthetic
+
+    K = args.steps if args.steps is not None else wl["steps"]
+    W_ = args.warmup if args.warmup is not None else wl["warmup"]
+    T, mats = wl["tokens"], wl["mats"]
+    N = mats * 512
+    dev = torch.device("cuda")
+    torch.cuda.init()
+    t0 = time.perf_counter()
+    Pt, sc = synthetic.streamed_linear(1, mats)
+    torch.cuda.synchronize()
+    log(f"built {mats} matrices in {time.perf_counter() - t0:.1f} s")
+    X = synthetic.activations(1, 64 * T).view(64, T, H)
+    Y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(tm.linear_workspace_bytes(T, H), 16), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        tm.ternary_linear(Pt, sc, N, H, X[i % 64], Y, ws)
+
+    for i in range(W_):
+        step(i)
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph.capture_begin()
+            for i in range(W_, W_ + K):
+                step(i)
+            graph.capture_end()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(W_, W_ + K):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    tm.profile_begin("linear", K)
+    for i in range(W_, W_ + K):
+        step(i)
+    ms = tm.profile_end(K)
+    torch.cuda.synchronize()
+    mean_s = float(np.mean(ms)) * 1e-3
+    launch_bytes = Pt.numel() + 4 * N + T * H * 2 + T * N * 4  # packed weights, row scales, X, Y
+    achieved = launch_bytes / mean_s / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None, "kernel": "ternary_linear", "mean_launch_us": mean_s * 1e6, "launches": int(len(ms)),
+            "algorithmic_bytes_per_launch": float(launch_bytes),
+            "packed_weight_gbs": Pt.numel() / mean_s / 1e9}
+    out = {
+        "metric": METRIC, "value": T * K / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W_,
+        "ms_per_step": 1e3 * elapsed / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["name"], "tokens_per_step": T, "rows": N, "cols": H, "matrices": mats,
+                   "weights": "ternary, 5 trits/byte, fp32 row scales", "hip_graph": use_graph},
+        "achieved_hbm_gbs": launch_bytes * K / elapsed / 1e9,
+        "hbm_frac": launch_bytes * K / elapsed / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": float(launch_bytes),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline_linear(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
 
 
 ATTN_KERNELS = ("linear", "attention")
@@ -448,6 +566,8 @@ def main():
     wl = dict(WORKLOADS[cfg])
     if wl.get("lm_head"):
         return main_lm_head(args, wl)
+    if wl.get("linear"):
+        return main_linear(args, wl)
     if wl.get("attention"):
         return main_attention(args, wl)
     K = args.steps if args.steps is not None else wl["steps"]

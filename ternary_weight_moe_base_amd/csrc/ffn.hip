@@ -1062,19 +1062,22 @@ struct LinearArgs {
   int64_t T, N, ldx, ldy;
   Geom g;
   bool contig;
+  bool rows_x;  // grid x walks the row-tile groups (one token tile), else the token tiles
+  int zrow;     // staged rows per token tile (min(16, T)); this LDS row holds zeros
 };
 
-// blockIdx.x = 16-token tile, blockIdx.y = group of 4/KS row tiles. F < 0:
-// generic K (runtime steps, one step in flight).
+// blockIdx.x = 16-token tile, blockIdx.y = group of 4/KS row tiles (swapped
+// when rows_x: one token tile and up to 2^31 row groups). F < 0: generic K
+// (runtime steps, one step in flight). LDS holds zrow + 1 rows.
 template <int F, int RT, int KS>
 __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int RTB = 4 / KS;
-  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int64_t t0 = (int64_t)(a.rows_x ? blockIdx.y : blockIdx.x) * 16;
   const int cnt = (int)min<int64_t>(16, a.T - t0);
   const int nrt = (int)((a.N + 15) / 16);
-  const int rt = blockIdx.y * RTB + wave / KS;
+  const int rt = (int)(a.rows_x ? blockIdx.x : blockIdx.y) * RTB + wave / KS;
   const int kp = wave % KS;
   const bool active = rt < nrt;
   const int rs = lds_row_bytes(a.g.slots);
@@ -1114,11 +1117,11 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
   } else {
     for (int n = 0; n < cnt; ++n) stage_row(xs + n * rs, a.X + (t0 + n) * a.ldx, a.g, threadIdx.x, 256);
   }
-  zero_row(xs + 16 * rs, a.g.slots, threadIdx.x, 256);
+  zero_row(xs + a.zrow * rs, a.g.slots, threadIdx.x, 256);
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
-  const char *bp = xs + (n < cnt ? n : 16) * rs + g * M * 16;
+  const char *bp = xs + (n < cnt ? n : a.zrow) * rs + g * M * 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     if constexpr (F >= 0) {
@@ -1173,7 +1176,7 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
     }
   }
   if constexpr (KS > 1) {
-    float *red = reinterpret_cast<float *>(smem + 17 * rs);  // [4][64][4]
+    float *red = reinterpret_cast<float *>(smem + (a.zrow + 1) * rs);  // [4][64][4]
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[(wave * 64 + lane) * 4 + v] = acc[v];
     __syncthreads();
@@ -1190,6 +1193,90 @@ __global__ __launch_bounds__(256) void linear_kernel(LinearArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v)
     if (row0 + v < a.N) y[row0 + v] = (acc[v] * 0.5f) * a.s[row0 + v];
+}
+
+// ------------------------------------------- ternary linear, streamed
+// Few tokens over very many rows (K = 2048): each workgroup stages the tokens
+// once, then every wavefront walks its own row tiles (wavefront g of G takes
+// tiles g, g + G, ...), the next tile's weights and row scales in flight while
+// the current one is decoded and multiplied. Nothing synchronizes the
+// wavefronts after the staging, so loads from many tiles per CU overlap.
+constexpr int kStreamWgs = 1024;  // four workgroups of four wavefronts per CU (about 110 VGPRs each)
+
+struct StreamW {
+  uint2 d[13];
+  float4 sc;
+};
+
+__device__ __forceinline__ void stream_issue(const LinearArgs &a, int rt, int nrt, int lane, StreamW &w) {
+  const bool live = rt < nrt;  // otherwise every lane reads the first bytes (counts stay path-independent)
+  const int64_t base = live ? (int64_t)rt * (64 * 8 * 13) + lane * 8 : 0;
+  const int64_t step = live ? 512 : 0;
+#pragma unroll
+  for (int s = 0; s < 13; ++s) w.d[s] = ldw8(a.pt + base + s * step);
+  const int64_t row0 = (int64_t)rt * 16 + 4 * (lane >> 4);
+  w.sc = live && row0 + 3 < a.N ? *reinterpret_cast<const float4 *>(a.s + row0) : make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live && row0 + 3 >= a.N) {  // the last, partial row tile
+    w.sc.x = row0 < a.N ? a.s[row0] : 0.f;
+    w.sc.y = row0 + 1 < a.N ? a.s[row0 + 1] : 0.f;
+    w.sc.z = row0 + 2 < a.N ? a.s[row0 + 2] : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256) void linear_stream_kernel(LinearArgs a) {
+  extern __shared__ __align__(16) char smem[];  // [zrow + 1][rs]
+  constexpr int M = 65;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cnt = (int)a.T;  // <= 16, one token tile
+  const int nrt = (int)((a.N + 15) / 16);
+  const int rs = lds_row_bytes(a.g.slots);
+  const int G = gridDim.x * 4;
+  int rt = blockIdx.x * 4 + wave;
+  StreamW cur, nxt;
+  stream_issue(a, rt, nrt, lane, cur);
+  {
+    const int vec = a.g.slots / 8, kv = 256;  // natural operand order, K = 2048
+    copy16<256>(
+        cnt * vec,
+        [&](int i) {
+          const int n = i / vec, c = i - n * vec;
+          return c < kv ? reinterpret_cast<const uint4 *>(a.X + n * a.ldx)[c] : make_uint4(0, 0, 0, 0);
+        },
+        [&](int i) {
+          const int n = i / vec, c = i - n * vec;
+          return reinterpret_cast<uint4 *>(smem + n * rs + c * 16);
+        });
+    zero_row(smem + a.zrow * rs, a.g.slots, threadIdx.x, 256);
+  }
+  __syncthreads();
+  const int n = lane & 15, g = lane >> 4;
+  int boff = (n < cnt ? n : a.zrow) * rs + g * M * 16;
+#pragma nounroll
+  for (; rt < nrt; rt += G) {
+    // the activation slices are re-read from LDS every tile (an opaque offset
+    // keeps the compiler from hoisting all 65 of them into 260 registers,
+    // which would leave one wavefront per SIMD)
+    asm volatile("" : "+v"(boff));
+    const char *bp = smem + boff;
+    stream_issue(a, rt + G, nrt, lane, nxt);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 13; ++s) {
+      uint32_t pw[20];
+      unpack8(cur.d[s], pw);
+#pragma unroll
+      for (int m = 0; m < 5; ++m) acc = mfma_bf16(pw + 4 * m, lds16(bp + (5 * s + m) * 16), acc);
+    }
+    if (n < cnt) {
+      const int64_t row0 = (int64_t)rt * 16 + 4 * g;
+      float *y = a.Y + n * a.ldy;
+      const float sv[4] = {cur.sc.x, cur.sc.y, cur.sc.z, cur.sc.w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (row0 + v < a.N) y[row0 + v] = (acc[v] * 0.5f) * sv[v];
+    }
+    cur = nxt;
+  }
 }
 
 // ------------------------------------------- ternary linear, fp32 input
@@ -1564,8 +1651,10 @@ size_t linear_ws_bytes(int64_t T, int64_t K) {
 template <int F, int RT, int KS>
 static int run_linear(hipStream_t st, const LinearArgs &a, int64_t ntok_tiles, int64_t nrt) {
   const int rs = lds_row_bytes(a.g.slots);
-  size_t lds = (size_t)17 * rs + (KS > 1 ? 4 * 64 * 4 * 4 : 0);
+  size_t lds = (size_t)(a.zrow + 1) * rs + (KS > 1 ? 4 * 64 * 4 * 4 : 0);
   dim3 grid((unsigned)ntok_tiles, (unsigned)cdiv(nrt, 4 / KS));
+  if (a.rows_x) grid = dim3((unsigned)cdiv(nrt, 4 / KS), (unsigned)ntok_tiles);
+  if (grid.y > 65535) return fail(TMOE_E_UNSUPPORTED, "too many row tiles for one token tile grid");
   int rc = allow_lds<linear_kernel<F, RT, KS>>(lds);
   if (rc) return rc;
   TMOE_LAUNCH(TMOE_KERNEL_LINEAR, (linear_kernel<F, RT, KS>), grid, dim3(256), lds, st, a);
@@ -1591,6 +1680,20 @@ int launch_linear(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N, 
   a.ldy = ldy;
   a.g = g;
   a.contig = g.QS == 5 * g.Q && K % 8 == 0 && ldx % 8 == 0 && ((uintptr_t)X & 15) == 0;
+  a.rows_x = ntt == 1;
+  a.zrow = (int)(T < 16 ? T : 16);
+  if (g.F == 13 && g.r == 0 && T <= 16 && nrt >= 8192 && a.contig) {
+    // a streamed matrix: the rows alone fill the chip many times over
+    const size_t lds = (size_t)(a.zrow + 1) * lds_row_bytes(g.slots);
+    int rc = allow_lds<linear_stream_kernel>(lds);
+    if (rc) return rc;
+    const int64_t wgs = cdiv(nrt, 4) < kStreamWgs ? cdiv(nrt, 4) : kStreamWgs;
+    TMOE_LAUNCH(TMOE_KERNEL_LINEAR, linear_stream_kernel, dim3((unsigned)wgs), dim3(256), lds, st, a);
+    TMOE_LAUNCHED("ternary_linear_stream");
+    return TMOE_OK;
+  }
+  // few tokens: K split over the four wavefronts (more workgroups for a few
+  // thousand rows)
   const bool small = T <= 16;
   if (g.F == 13 && g.r == 0) return small ? run_linear<13, 0, 4>(st, a, ntt, nrt) : run_linear<13, 0, 1>(st, a, ntt, nrt);
   if (g.F == 3 && g.r == 2) return run_linear<3, 2, 1>(st, a, ntt, nrt);

@@ -47,6 +47,22 @@ def build_layer(cfg: int, layer: int, bias_kind: str | None = None, experts: int
     return MoEWeights(router_w, router_bias, gate_p, up_p, down_p, gate_s, up_s, down_s, top_k=top_k)
 
 
+def streamed_linear(cfg: int = 1, mats: int = 2048, rows: int = ti.INTER, cols: int = ti.HIDDEN):
+    """`mats` distinct [rows][cols] ternary matrices stacked into one tiled
+    [mats * rows][cols] matrix (tiled bytes and fp32 row scales on the device);
+    matrix q takes the Philox stream (cfg, layer q // 1024, expert q % 1024,
+    gate), so matrix 0 is the config's single linear matrix; each is
+    ternarized and packed like every expert matrix."""
+    dev = torch.device("cuda")
+    Pt = torch.empty((mats, tiled_bytes(rows, cols)), dtype=torch.uint8, device=dev)
+    s = torch.empty((mats, rows), dtype=torch.float32, device=dev)
+    wbuf = torch.empty(rows * cols, dtype=torch.float32, device=dev)
+    pbuf = torch.empty(rows * ((cols + 4) // 5), dtype=torch.uint8, device=dev)
+    for q in range(mats):
+        _mat(cfg, q // 1024, q % 1024, ti.MAT_GATE, rows, cols, wbuf, pbuf, Pt[q], s[q])
+    return Pt.view(-1), s.view(-1)
+
+
 def is_global_layer(layer: int) -> bool:
     """Layer pattern: three sliding-window layers, then one global layer
     (global at 3, 7, 11, 15, 19, 23: ai.thesatyajit.com, "The architecture
