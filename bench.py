@@ -10,6 +10,11 @@ top-8, moe_intermediate_size 512); successive steps rotate over 24 distinct
 layers (3.9 GB of packed experts, far above the 256 MB last-level cache) and
 fresh tokens, so expert weights stream from HBM. The K timed steps run as one
 captured HIP graph, replayed once after the warm-up. Prints one JSON line.
+Other workloads (--config): 1 the streamed 2048 -> 512 ternary linear, 3 a
+64-token batch with Zipf routing, 4 4096-token prefill, 5 the 24-layer stack
+at 256 tokens, 6 one token through the 24-layer stack, 7 the LM head top-16,
+8 config 6 with experts in pinned host memory, 9/10/11 one token through the
+attention halves / the whole model / the model and its LM head at context 4096.
 """
 from __future__ import annotations
 
