@@ -145,7 +145,12 @@ int tmoe_synth_ih12(void *stream, uint64_t key0, uint64_t key1, uint64_t stream_
  *   X: bf16 [T][ldx] (ldx >= K, element stride; 2-byte alignment suffices);
  *   Y: fp32 [T][ldy] (ldy >= N).
  * ws: workspace of tmoe_linear_workspace_bytes(T, K) bytes; the current
- *   kernels need none (0 bytes, ws may be NULL). */
+ *   kernels need none (0 bytes, ws may be NULL).
+ * Very tall operands with few tokens (K = 2048, T <= 16, N >= 131,072 rows,
+ * contiguous 16-byte-aligned X) take a streaming kernel whose wavefronts walk
+ * row tiles with the next tile's weights in flight; the result is the same
+ * up to fp32 summation order. Errors: TMOE_E_UNSUPPORTED when T > 16 and
+ * N > 4,194,240 rows (more than 65,535 groups of four row tiles). */
 size_t tmoe_linear_workspace_bytes(int64_t T, int64_t K);
 int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,
                         int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws, size_t ws_bytes);
