@@ -213,9 +213,10 @@ typedef struct tmoe_moe_weights {
  * For every grouped pair p (expert e, token t = sorted_token[p]):
  *   g = gate_e x_t, u = up_e x_t            (ternary linear, fp32)
  *   h = SiLU(min(g, c)) * clamp(u, -c, c)   (c = clamp; INFINITY disables)
- *   O[p] = down_e h                          (h kept fp32: split exactly into
- *                                             three bf16 parts, each multiplied
- *                                             exactly, fp32 accumulation)
+ *   O[p] = down_e h                          (h fp32, entering as two fp16
+ *                                             parts hi = fp16(h), lo = fp16(h -
+ *                                             hi), each multiplied exactly, fp32
+ *                                             accumulation)
  * (ai.thesatyajit.com, "The shipped code does no quantization").
  *   X bf16 [T][H]; offsets [E+1], sorted_token [T*k] from the grouping;
  *   O fp32 [T*k][H] in grouped order; Hout fp32 [T*k][I] or NULL (h, for

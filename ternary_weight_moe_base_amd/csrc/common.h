@@ -192,7 +192,7 @@ int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E
 struct FfnWs {
   int32_t *tiles;    // [max_tiles][4]: expert, start, count, 0
   int32_t *ntiles;   // [1]
-  uint16_t *hp;      // [3][T*k][slots_I] bf16 parts hi + mid + lo = h of each grouped pair,
+  uint16_t *hp;      // [2][T*k][slots_I] fp16 parts hi, lo of h of each grouped pair,
                      // in the down projection's operand layout
   float *pw;         // [T*k] routing weight of each grouped pair (decode path)
   int32_t *blocks;   // [max_blocks][4]: expert, start, count (<= 64), 0 (token-blocked gate/up)

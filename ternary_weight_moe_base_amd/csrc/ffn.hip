@@ -17,9 +17,10 @@
 //    floor), another 1027 + R + floor(R / 3), whose two low bits are
 //    (d - 1) mod 4 because d = R - 3 floor(R / 3) == R + floor(R / 3) (mod 4).
 //  - gate/up take the bf16 activations directly. The down projection's input h
-//    is fp32: it is split exactly into three bf16 parts h = hi + mid + lo (each
-//    rounding keeps the next 8 of the 24 significant bits), each multiplied
-//    exactly.
+//    is fp32: it enters as two fp16 parts h ~ hi + lo (hi = fp16(h), lo =
+//    fp16(h - hi); 22 of the 24 significant bits, |h - hi - lo| <= 2^-23 |h|
+//    above the fp16 normal range), each multiplied exactly on the fp16 matrix
+//    cores, whose trit operand is the same bit pattern.
 #include "route_util.h"
 
 namespace tmoe {
@@ -202,7 +203,7 @@ struct GateUpArgs {
   const uint16_t *X;  // [T][H] bf16, natural order
   const int32_t *tiles, *ntiles, *sorted_token;
   float *h;            // [pairs][I] fp32 (grouped order) or null
-  uint16_t *hp;        // [3][pairs][gd.slots] bf16 parts of h in the down operand layout (pads not written)
+  uint16_t *hp;        // [2][pairs][gd.slots] fp16 parts of h in the down operand layout (pads not written)
   int64_t hp_plane;    // pairs * gd.slots
   Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
   int I;
@@ -213,29 +214,33 @@ struct GateUpArgs {
   int T, E, k;
 };
 
+// h -> two fp16 parts (bit patterns): hi = fp16(h), lo = fp16(h - hi); the
+// difference h - hi is exact in fp32.
+__device__ inline void split_h2(float h, uint32_t &hi, uint32_t &lo) {
+  const _Float16 a = (_Float16)h;
+  const _Float16 b = (_Float16)(h - (float)a);
+  hi = __builtin_bit_cast(uint16_t, a);
+  lo = __builtin_bit_cast(uint16_t, b);
+}
+
 __device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
                                 const float4 &sg, const float4 &su) {
   const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
   const float c = a.clamp;
   float hv[4];
-  uint32_t part[3][2];
+  uint32_t part[2][2];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float gg = (gs[v] * 0.5f) * sgv[v];
     const float uu = (us[v] * 0.5f) * suv[v];
     const float z = fminf(gg, c);
     hv[v] = __fdividef(z, 1.f + __expf(-z)) * fminf(fmaxf(uu, -c), c);
-    // h = hi + mid + lo exactly (each bf16 rounding keeps the next 8 bits)
-    const uint32_t b0 = f32_to_bf16_rne(hv[v]);
-    const float r1 = hv[v] - __uint_as_float(b0 << 16);
-    const uint32_t b1 = f32_to_bf16_rne(r1);
-    const float r2 = r1 - __uint_as_float(b1 << 16);
-    const uint32_t b2 = f32_to_bf16_rne(r2);
+    uint32_t b0, b1;
+    split_h2(hv[v], b0, b1);
     const int sh = (v & 1) * 16;
-    if ((v & 1) == 0) part[0][v >> 1] = part[1][v >> 1] = part[2][v >> 1] = 0u;
+    if ((v & 1) == 0) part[0][v >> 1] = part[1][v >> 1] = 0u;
     part[0][v >> 1] |= b0 << sh;
     part[1][v >> 1] |= b1 << sh;
-    part[2][v >> 1] |= b2 << sh;
   }
   const int q5 = 5 * a.gd.Q;
 #pragma unroll
@@ -243,7 +248,7 @@ __device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const 
     const int nn = row0 + 2 * hpair;
     const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) *reinterpret_cast<uint32_t *>(a.hp + q * a.hp_plane + o) = part[q][hpair];
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<uint32_t *>(a.hp + q * a.hp_plane + o) = part[q][hpair];
   }
   if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
 }
@@ -405,7 +410,7 @@ __device__ __forceinline__ float silu(float z) { return __fdividef(z, 1.f + __ex
 
 // h = SiLU(min(g, c)) * clip(u, -c, c) of four consecutive intermediate rows
 // row0 .. row0+3 of grouped pair p, from the gate / up sums (trits entered as
-// 2t) and the row scales; stored as three exact bf16 parts in the down
+// 2t) and the row scales; stored as two fp16 parts (split_h2) in the down
 // operand layout, two rows per 32-bit store (row0 is a multiple of 4 and a
 // quarter holds an even number of inputs, so a row pair never straddles two
 // quarters), and as fp32 if requested.
@@ -597,18 +602,14 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
     const float gg = (gs * 0.5f) * sgv[v];
     const float uu = (us * 0.5f) * suv[v];
     const float hv = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
-    const uint16_t b0 = f32_to_bf16_rne(hv);
-    const float r1 = hv - __uint_as_float((uint32_t)b0 << 16);
-    const uint16_t b1 = f32_to_bf16_rne(r1);
-    const float r2 = r1 - __uint_as_float((uint32_t)b1 << 16);
-    const uint16_t b2 = f32_to_bf16_rne(r2);
+    uint32_t b0, b1;
+    split_h2(hv, b0, b1);
     const int nn = rtb * 16 + 4 * g + v;
     const int q5 = 5 * a.gd.Q;
     const int64_t p = start + n;
     const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
-    a.hp[o] = b0;
-    a.hp[a.hp_plane + o] = b1;
-    a.hp[2 * a.hp_plane + o] = b2;
+    a.hp[o] = (uint16_t)b0;
+    a.hp[a.hp_plane + o] = (uint16_t)b1;
     if (a.h) a.h[p * a.I + nn] = hv;
     return;
   }
@@ -788,7 +789,7 @@ struct DownArgs {
   const uint8_t *down_p;
   int64_t stride_d;
   const float *down_s;
-  const uint16_t *hp;  // [3][pairs][slots] bf16 parts of h (operand layout)
+  const uint16_t *hp;  // [2][pairs][slots] fp16 parts of h (operand layout)
   int64_t hp_plane;
   const int32_t *tiles, *ntiles;
   float *O;  // [pairs][H]
@@ -808,7 +809,7 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
   constexpr int M = 5 * F + tail_mfmas(RT);
   const int rtb = ry * 4 * R + wave;  // row tiles rtb + 4 r
   const int rs = lds_row_bytes(a.slots);
-  char *xb[3] = {smem, smem + 17 * rs, smem + 34 * rs};  // [3][17][rs]
+  char *xb[2] = {smem, smem + 17 * rs};  // [2][17][rs]
   const int g = lane >> 4;
 
   const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
@@ -829,20 +830,20 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
 
   constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
   copy16<256>(
-      3 * cnt * VPR,
+      2 * cnt * VPR,
       [&](int i) {
         const int row = i / VPR, c = i - row * VPR;
-        const int q = row >= 2 * cnt ? 2 : (row >= cnt ? 1 : 0), n = row - q * cnt;
+        const int q = row >= cnt ? 1 : 0, n = row - q * cnt;
         return reinterpret_cast<const uint4 *>(a.hp + q * a.hp_plane + (int64_t)(start + n) * a.slots)[c];
       },
       [&](int i) {
         const int row = i / VPR, c = i - row * VPR;
-        const int q = row >= 2 * cnt ? 2 : (row >= cnt ? 1 : 0), n = row - q * cnt;
+        const int q = row >= cnt ? 1 : 0, n = row - q * cnt;
         return reinterpret_cast<uint4 *>(xb[q] + n * rs + c * 16);
       },
       [&](int i, uint4 v) { return keep_live(v, live_in_chunk<F, RT>(a.gd.K, i % VPR)); });
 #pragma unroll
-  for (int q = 0; q < 3; ++q) zero_row(xb[q] + 16 * rs, a.slots, threadIdx.x, 256);
+  for (int q = 0; q < 2; ++q) zero_row(xb[q] + 16 * rs, a.slots, threadIdx.x, 256);
   __syncthreads();
 
   const int n = lane & 15;
@@ -852,11 +853,11 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
   for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < F; ++s) {
-    u32x4 bx[5][3];
+    u32x4 bx[5][2];
 #pragma unroll
     for (int m = 0; m < 5; ++m)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) bx[m][q] = lds16(xb[q] + boff + (5 * s + m) * 16);
+      for (int q = 0; q < 2; ++q) bx[m][q] = lds16(xb[q] + boff + (5 * s + m) * 16);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       uint32_t pw[20];
@@ -864,15 +865,15 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
 #pragma unroll
       for (int m = 0; m < 5; ++m)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) acc[r] = mfma_bf16(pw + 4 * m, bx[m][q], acc[r]);
+        for (int q = 0; q < 2; ++q) acc[r] = mfma_f16(pw + 4 * m, bx[m][q], acc[r]);
     }
   }
   if constexpr (RT > 0) {
-    u32x4 bx[tail_mfmas(RT)][3];
+    u32x4 bx[tail_mfmas(RT)][2];
 #pragma unroll
     for (int m = 0; m < tail_mfmas(RT); ++m)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) bx[m][q] = lds16(xb[q] + boff + (5 * F + m) * 16);
+      for (int q = 0; q < 2; ++q) bx[m][q] = lds16(xb[q] + boff + (5 * F + m) * 16);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       uint32_t pw[16];
@@ -880,7 +881,7 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
 #pragma unroll
       for (int m = 0; m < tail_mfmas(RT); ++m)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) acc[r] = mfma_bf16(pw + 4 * m, bx[m][q], acc[r]);
+        for (int q = 0; q < 2; ++q) acc[r] = mfma_f16(pw + 4 * m, bx[m][q], acc[r]);
     }
   }
   if (n >= cnt) return;
@@ -915,7 +916,7 @@ struct DownCombineArgs {
   const uint8_t *down_p;
   int64_t stride_d;
   const float *down_s;
-  const uint16_t *hp;  // [3][pairs][slots] bf16 parts of h (operand layout), contiguous
+  const uint16_t *hp;  // [2][pairs][slots] fp16 parts of h (operand layout), contiguous
   int slots;
   const int32_t *tiles, *ntiles, *sorted_token;
   const float *pair_w;  // [pairs] routing weight of each grouped pair
@@ -929,7 +930,7 @@ struct DownCombineArgs {
 constexpr int kDcWaves = 8;
 
 // Decode path with few pairs (T*k <= 32): workgroup = one 16-row block of the
-// H outputs for all work tiles. The three bf16 parts of h of every pair are
+// H outputs for all work tiles. The two fp16 parts of h of every pair are
 // staged in LDS together with the first tile descriptors; wavefront w then takes
 // tiles w, w + 8, ... in order and adds pair_w * o (o = sd * (Td h)) into its
 // own LDS accumulator of the pair's token; the accumulators are summed in fixed
@@ -937,7 +938,7 @@ constexpr int kDcWaves = 8;
 // the tile's pairs repeat its last pair and are discarded.
 template <int F, int RT>
 __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombineArgs a) {
-  extern __shared__ __align__(16) char hps[];  // [3][P][slots] bf16
+  extern __shared__ __align__(16) char hps[];  // [2][P][slots] fp16
   __shared__ float yacc[kDcWaves][kDecodeMaxT][16];
   __shared__ int32_t s_tok[kDcMaxPairs];
   __shared__ float s_pw[kDcMaxPairs];
@@ -952,7 +953,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   // first staging batch in flight, then the first tile's weights, then the stores
   constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
   constexpr int NT = 64 * kDcWaves, NB = 8;
-  const int nchunk = 3 * a.P * VPR;
+  const int nchunk = 2 * a.P * VPR;
   uint4 sv[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -1021,7 +1022,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
 #pragma unroll
       for (int m = 0; m < 5; ++m)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(hb + q * plane + 16 * (5 * s + m)), acc);
+        for (int q = 0; q < 2; ++q) acc = mfma_f16(pw + 4 * m, lds16(hb + q * plane + 16 * (5 * s + m)), acc);
     }
     if constexpr (RT > 0) {
       uint32_t pw[16];
@@ -1029,7 +1030,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
 #pragma unroll
       for (int m = 0; m < tail_mfmas(RT); ++m)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) acc = mfma_bf16(pw + 4 * m, lds16(hb + q * plane + 16 * (5 * F + m)), acc);
+        for (int q = 0; q < 2; ++q) acc = mfma_f16(pw + 4 * m, lds16(hb + q * plane + 16 * (5 * F + m)), acc);
     }
     if (live) {
       const int tok = s_tok[p];
@@ -1281,7 +1282,8 @@ __global__ __launch_bounds__(256) void linear_stream_kernel(LinearArgs a) {
 
 // ------------------------------------------- ternary linear, fp32 input
 // Y = s (.) (T x) with fp32 x: while staging, each input is split exactly into
-// three bf16 parts (hi + mid + lo, as h of the down projection), and every
+// three bf16 parts (hi + mid + lo, exact: each rounding keeps the next 8 of
+// the 24 significant bits), and every
 // decoded weight slice multiplies all three (fp32 accumulation). Optional
 // residual: resid_out = bf16(fp32(resid_in) + y). K = 2048 only (natural
 // operand order); eight tokens per workgroup (three planes of staged rows).
@@ -1439,7 +1441,7 @@ size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   size_t o = 0;
   o = align_up(o + ffn_max_tiles(P, E) * 16, 256);
   o = align_up(o + 16, 256);
-  o = align_up(o + (size_t)3 * P * gi.slots * 2, 256);
+  o = align_up(o + (size_t)2 * P * gi.slots * 2, 256);
   o = align_up(o + (size_t)P * 4, 256);
   o = align_up(o + ffn_max_blocks(P, E) * 16, 256);
   o = align_up(o + 16, 256);
@@ -1457,7 +1459,7 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   f.ntiles = (int32_t *)(b + o);
   o = align_up(o + 16, 256);
   f.hp = (uint16_t *)(b + o);
-  o = align_up(o + (size_t)3 * P * make_geom(I).slots * 2, 256);
+  o = align_up(o + (size_t)2 * P * make_geom(I).slots * 2, 256);
   f.pw = (float *)(b + o);
   o = align_up(o + (size_t)P * 4, 256);
   f.blocks = (int32_t *)(b + o);
@@ -1513,7 +1515,7 @@ static int check_ffn_shapes(const tmoe_moe_weights *W) {
 
 template <int R>
 static int run_down_r(hipStream_t st, const DownArgs &da, int64_t max_tiles, int64_t H, bool walk) {
-  const size_t lds = (size_t)3 * 17 * lds_row_bytes(da.slots);
+  const size_t lds = (size_t)2 * 17 * lds_row_bytes(da.slots);
   int rc = allow_lds<down_kernel<3, 2, R>>(lds);
   if (rc) return rc;
   TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_kernel<3, 2, R>),
@@ -1587,7 +1589,7 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
     da.Y = Y;
     da.resid_in = resid_in;
     da.resid_out = resid_out;
-    const size_t lds = (size_t)3 * P * gi.slots * 2;
+    const size_t lds = (size_t)2 * P * gi.slots * 2;
     rc = allow_lds<down_combine_kernel<3, 2>>(lds);
     if (rc) return rc;
     TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_combine_kernel<3, 2>), dim3((unsigned)(H / 16)), dim3(64 * kDcWaves), lds,
