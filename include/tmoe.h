@@ -213,11 +213,17 @@ typedef struct tmoe_moe_weights {
  * For every grouped pair p (expert e, token t = sorted_token[p]):
  *   g = gate_e x_t, u = up_e x_t            (ternary linear, fp32)
  *   h = SiLU(min(g, c)) * clamp(u, -c, c)   (c = clamp; INFINITY disables)
- *   O[p] = down_e h                          (h fp32, entering as two fp16
- *                                             parts hi = fp16(h), lo = fp16(h -
- *                                             hi), each multiplied exactly, fp32
- *                                             accumulation)
+ *   O[p] = down_e h                          (ternary linear over fp32 h)
  * (ai.thesatyajit.com, "The shipped code does no quantization").
+ * Precision: fp32 accumulation throughout. h enters the down projection
+ * scaled per pair by a power of two 2^sig that puts the pair's largest |h| in
+ * [2^14, 2^15), as two fp16 parts hi = fp16(2^sig h), lo = fp16(2^sig h - hi)
+ * (22 of h's 24 significant bits; values under 2^-28 of the pair's largest
+ * lose only bits below 2^-39 of it), multiplied exactly; the sums are
+ * rescaled by 2^-sig exactly. This holds for every finite h, in both clamp
+ * modes and at any input scale; results are finite whenever g, u, h and O
+ * themselves are representable in fp32 (with the clamp on, |h| <= c SiLU(c)
+ * for c >= 1.3, e.g. 49 for c = 7).
  *   X bf16 [T][H]; offsets [E+1], sorted_token [T*k] from the grouping;
  *   O fp32 [T*k][H] in grouped order; Hout fp32 [T*k][I] or NULL (h, for
  *   checking). ws: tmoe_ffn_workspace_bytes(T, W). */

@@ -318,9 +318,10 @@ def silu(z: np.ndarray) -> np.ndarray:
 def expert_ffn(x: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray, clamp: float = 7.0):
     """One expert on float64 rows x [n][H] with dense float64 weights.
 
-    ai.thesatyajit.com, "The shipped code does no quantization":
-    out = linear(act(clamp(linear(x, Wg), max=c)) * clamp(linear(x, Wu), -c, c), Wd),
-    act = SiLU, c = 7 (clamp = inf gives the unclamped textbook form).
+    The expert forward of ai.thesatyajit.com, "The shipped code does no
+    quantization": with g = Wg x and u = Wu x (weights in [out][in] order),
+    h = SiLU(min(g, c)) * min(max(u, -c), c) elementwise and o = Wd h; the
+    activation is SiLU and c = 7 (c = inf leaves g and u unclamped).
     Returns (g, u, h, o), all float64.
     """
     g = x @ gate.T
@@ -347,7 +348,6 @@ def moe_layer(x_bits: np.ndarray, Wr: np.ndarray, bias, get_expert, k: int = 8, 
     counts, offsets, sorted_token, sorted_slot, pos = group_by_expert(idx, E)
     I = None
     G = U = Hh = O = None
-    Y = np.zeros((T, H), dtype=np.float64)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -363,9 +363,7 @@ def moe_layer(x_bits: np.ndarray, Wr: np.ndarray, bias, get_expert, k: int = 8, 
             G = np.zeros((T * k, I)); U = np.zeros((T * k, I)); Hh = np.zeros((T * k, I))
             O = np.zeros((T * k, H))
         G[lo:hi], U[lo:hi], Hh[lo:hi], O[lo:hi] = g, u, h, o
-    for t in range(T):
-        for j in range(k):
-            Y[t] += w[t, j] * O[pos[t * k + j]]
+    Y = combine(O, w, pos)
     return dict(idx=idx, w=w, logits=L, n_exact=n_exact, counts=counts, offsets=offsets,
                 sorted_token=sorted_token, sorted_slot=sorted_slot, pos=pos,
                 G=G, U=U, H=Hh, O=O, Y=Y)

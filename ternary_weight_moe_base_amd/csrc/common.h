@@ -192,8 +192,8 @@ int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E
 struct FfnWs {
   int32_t *tiles;    // [max_tiles][4]: expert, start, count, 0
   int32_t *ntiles;   // [1]
-  uint16_t *hp;      // [2][T*k][slots_I] fp16 parts hi, lo of h of each grouped pair,
-                     // in the down projection's operand layout
+  float *hf;         // [T*k][I] fp32 h of each grouped pair (gate/up writes it; the down
+                     // kernels split it into scaled fp16 parts while staging)
   float *pw;         // [T*k] routing weight of each grouped pair (decode path)
   int32_t *blocks;   // [max_blocks][4]: expert, start, count (<= 64), 0 (token-blocked gate/up)
   int32_t *nblocks;  // [1]

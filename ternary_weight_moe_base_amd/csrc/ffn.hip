@@ -17,10 +17,15 @@
 //    floor), another 1027 + R + floor(R / 3), whose two low bits are
 //    (d - 1) mod 4 because d = R - 3 floor(R / 3) == R + floor(R / 3) (mod 4).
 //  - gate/up take the bf16 activations directly. The down projection's input h
-//    is fp32: it enters as two fp16 parts h ~ hi + lo (hi = fp16(h), lo =
-//    fp16(h - hi); 22 of the 24 significant bits, |h - hi - lo| <= 2^-23 |h|
-//    above the fp16 normal range), each multiplied exactly on the fp16 matrix
-//    cores, whose trit operand is the same bit pattern.
+//    is fp32 (written to the workspace by gate/up). While a down kernel stages
+//    a pair's h row it scales the row by a power of two 2^sig that puts the
+//    row's largest |h| in [2^14, 2^15), and splits each value into two fp16
+//    parts hi = fp16(2^sig h), lo = fp16(2^sig h - hi) (the difference is
+//    exact in fp32): hi never overflows, and every value the row's result can
+//    feel keeps 22 of its 24 significant bits, for any finite h. Both parts
+//    are multiplied exactly on the fp16 matrix cores (the trit operand is the
+//    same bit pattern), and the epilogue multiplies the pair's sums by
+//    2^-(sig + 1), exactly.
 #include "route_util.h"
 
 namespace tmoe {
@@ -154,27 +159,6 @@ __device__ inline void zero_row(char *dst, int slots, int tid, int nthreads) {
   for (int c = tid; c < slots / 8; c += nthreads) *reinterpret_cast<uint4 *>(dst + c * 16) = make_uint4(0, 0, 0, 0);
 }
 
-// Positions of an operand row that hold no input (j >= 5Q in a quarter, or
-// input index >= K) must be zero where they meet activations: number of live
-// 16-bit values in 16-byte chunk c of a staged row, and the chunk with the
-// others cleared.
-template <int F, int RT>
-__device__ inline int live_in_chunk(int K, int c) {
-  constexpr int QS = 8 * (5 * F + (RT == 0 ? 0 : (5 * (RT / 2) + 3) / 4)), Q5 = 5 * (8 * F + RT);
-  const int pos = c * 8, quarter = pos / QS, j0 = pos - quarter * QS;
-  const int live = K - Q5 * quarter;
-  const int lq = live < 0 ? 0 : (live < Q5 ? live : Q5);
-  const int n = lq - j0;
-  return n < 0 ? 0 : (n > 8 ? 8 : n);
-}
-__device__ inline uint4 keep_live(uint4 v, int nlive) {
-  if (nlive >= 8) return v;
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] &= (2 * i + 1 < nlive) ? 0xFFFFFFFFu : (2 * i < nlive ? 0x0000FFFFu : 0u);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // ---------------------------------------------------------------- tiles
 // Work tiles of up to TILE grouped pairs of one expert, in expert order.
 template <int TILE>
@@ -202,9 +186,8 @@ struct GateUpArgs {
   const float *gate_s, *up_s;
   const uint16_t *X;  // [T][H] bf16, natural order
   const int32_t *tiles, *ntiles, *sorted_token;
-  float *h;            // [pairs][I] fp32 (grouped order) or null
-  uint16_t *hp;        // [2][pairs][gd.slots] fp16 parts of h in the down operand layout (pads not written)
-  int64_t hp_plane;    // pairs * gd.slots
+  float *h;            // [pairs][I] fp32 (grouped order) or null: a copy of h for the caller
+  float *hf;           // [pairs][I] fp32 h in grouped order (the down projection's input)
   Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
   int I;
   float clamp;
@@ -214,43 +197,92 @@ struct GateUpArgs {
   int T, E, k;
 };
 
-// h -> two fp16 parts (bit patterns): hi = fp16(h), lo = fp16(h - hi); the
-// difference h - hi is exact in fp32.
-__device__ inline void split_h2(float h, uint32_t &hi, uint32_t &lo) {
-  const _Float16 a = (_Float16)h;
-  const _Float16 b = (_Float16)(h - (float)a);
-  hi = __builtin_bit_cast(uint16_t, a);
-  lo = __builtin_bit_cast(uint16_t, b);
-}
-
 __device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
                                 const float4 &sg, const float4 &su) {
   const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
   const float c = a.clamp;
   float hv[4];
-  uint32_t part[2][2];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float gg = (gs[v] * 0.5f) * sgv[v];
     const float uu = (us[v] * 0.5f) * suv[v];
     const float z = fminf(gg, c);
     hv[v] = __fdividef(z, 1.f + __expf(-z)) * fminf(fmaxf(uu, -c), c);
-    uint32_t b0, b1;
-    split_h2(hv[v], b0, b1);
-    const int sh = (v & 1) * 16;
-    if ((v & 1) == 0) part[0][v >> 1] = part[1][v >> 1] = 0u;
-    part[0][v >> 1] |= b0 << sh;
-    part[1][v >> 1] |= b1 << sh;
   }
-  const int q5 = 5 * a.gd.Q;
+  const float4 h4 = make_float4(hv[0], hv[1], hv[2], hv[3]);
+  *reinterpret_cast<float4 *>(a.hf + p * a.I + row0) = h4;
+  if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = h4;
+}
+
+// ------------------------------------------------ down operand staging
+// The h rows of `cnt` grouped pairs (fp32, row n at h + n * I) become the down
+// projection's operand in LDS: two fp16 planes (row n of plane q at
+// pl[q] + n * rs) in the operand layout (position g * 8M + j holds input
+// 5Qg + j, zero where no input is held). Row n is scaled by 2^sig[n], sig
+// chosen so that the row's largest |h| lies in [2^14, 2^15) (sig = 0 for an
+// all-zero or non-finite row): hi = fp16(2^sig h) then never overflows, and
+// lo = fp16(2^sig h - hi) keeps the next 11 bits; values below 2^-28 of the
+// row's largest only lose bits under 2^-39 of it. Wavefront w of NW takes rows
+// w, w + NW, ... (at most RPW each); all loads of a wavefront are issued before
+// its first row is reduced.
+template <int NW, int RPW, int M>
+__device__ inline void stage_h_parts(const float *h, int cnt, int I, int q5, char *pl0, char *pl1, int rs, int *sig) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NCH = 4 * M;            // 16-byte chunks (8 positions) per staged row
+  constexpr int NPL = (NCH + 63) / 64;  // chunks per lane
+  float v[RPW][NPL][8];
 #pragma unroll
-  for (int hpair = 0; hpair < 2; ++hpair) {
-    const int nn = row0 + 2 * hpair;
-    const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
+  for (int i = 0; i < RPW; ++i) {
+    const int n = wave + NW * i;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<uint32_t *>(a.hp + q * a.hp_plane + o) = part[q][hpair];
+    for (int u = 0; u < NPL; ++u) {
+      const int c = lane + 64 * u;
+      const int quarter = c / M, j0 = 8 * (c - quarter * M), k0 = q5 * quarter + j0;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // q5, I and k0 are even, so both values of a pair are inputs or neither is
+        float2 f = make_float2(0.f, 0.f);
+        if (n < cnt && c < NCH && j0 + e < q5 && k0 + e < I)
+          f = *reinterpret_cast<const float2 *>(h + (int64_t)n * I + k0 + e);
+        v[i][u][e] = f.x;
+        v[i][u][e + 1] = f.y;
+      }
+    }
   }
-  if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int n = wave + NW * i;
+    if (n >= cnt) break;
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < NPL; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = max(mx, __float_as_uint(v[i][u][e]) & 0x7FFFFFFFu);
+    mx = wave_max_u32(mx);
+    int s = 0;
+    if (mx != 0 && mx < 0x7F800000u) {
+      int ex;
+      (void)frexpf(__uint_as_float(mx), &ex);  // largest |h| = f 2^ex, f in [1/2, 1)
+      s = 15 - ex;
+    }
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) {
+      const int c = lane + 64 * u;
+      if (c >= NCH) continue;
+      uint32_t w[2][4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float a0 = ldexpf(v[i][u][e], s), a1 = ldexpf(v[i][u][e + 1], s);
+        const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+        const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
+        w[0][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        w[1][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      *reinterpret_cast<uint4 *>(pl0 + n * rs + c * 16) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+      *reinterpret_cast<uint4 *>(pl1 + n * rs + c * 16) = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+    }
+    if (lane == 0) sig[n] = s;
+  }
 }
 
 // ------------------------------------------------------ routing prologue
@@ -410,10 +442,8 @@ __device__ __forceinline__ float silu(float z) { return __fdividef(z, 1.f + __ex
 
 // h = SiLU(min(g, c)) * clip(u, -c, c) of four consecutive intermediate rows
 // row0 .. row0+3 of grouped pair p, from the gate / up sums (trits entered as
-// 2t) and the row scales; stored as two fp16 parts (split_h2) in the down
-// operand layout, two rows per 32-bit store (row0 is a multiple of 4 and a
-// quarter holds an even number of inputs, so a row pair never straddles two
-// quarters), and as fp32 if requested.
+// 2t) and the row scales; stored as fp32 in grouped order (one 16-byte store),
+// and into the caller's copy if requested.
 struct GateUpArgs;
 __device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
                                 const float4 &sg, const float4 &su);
@@ -602,14 +632,9 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
     const float gg = (gs * 0.5f) * sgv[v];
     const float uu = (us * 0.5f) * suv[v];
     const float hv = silu(fminf(gg, c)) * fminf(fmaxf(uu, -c), c);
-    uint32_t b0, b1;
-    split_h2(hv, b0, b1);
     const int nn = rtb * 16 + 4 * g + v;
-    const int q5 = 5 * a.gd.Q;
     const int64_t p = start + n;
-    const int64_t o = p * a.gd.slots + (nn / q5) * a.gd.QS + nn % q5;
-    a.hp[o] = (uint16_t)b0;
-    a.hp[a.hp_plane + o] = (uint16_t)b1;
+    a.hf[p * a.I + nn] = hv;
     if (a.h) a.h[p * a.I + nn] = hv;
     return;
   }
@@ -789,18 +814,17 @@ struct DownArgs {
   const uint8_t *down_p;
   int64_t stride_d;
   const float *down_s;
-  const uint16_t *hp;  // [2][pairs][slots] fp16 parts of h (operand layout)
-  int64_t hp_plane;
+  const float *hf;  // [pairs][I] fp32 h in grouped order
   const int32_t *tiles, *ntiles;
   float *O;  // [pairs][H]
-  int H, slots;
+  int H, I, slots;
   Geom gd;       // operand geometry of the down projection (K = I)
   int stream_w;  // few pairs per expert: each weight tile is read once, non-temporally
 };
 
-// Workgroup = 4 wavefronts x R 16-row tiles each (64 R output rows); three
-// bf16 passes (hi, mid, lo parts of h) per operand slice, each slice read from
-// LDS once per wavefront for its R row tiles.
+// Workgroup = 4 wavefronts x R 16-row tiles each (64 R output rows); two fp16
+// passes (the hi and lo parts of the scaled h) per operand slice, each slice
+// read from LDS once per wavefront for its R row tiles.
 template <int F, int RT, int R>
 __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry) {
   const int4 td = reinterpret_cast<const int4 *>(a.tiles)[tile];
@@ -828,20 +852,8 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
     sd[r] = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + (rtb + 4 * r) * 16 + 4 * g);
   }
 
-  constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
-  copy16<256>(
-      2 * cnt * VPR,
-      [&](int i) {
-        const int row = i / VPR, c = i - row * VPR;
-        const int q = row >= cnt ? 1 : 0, n = row - q * cnt;
-        return reinterpret_cast<const uint4 *>(a.hp + q * a.hp_plane + (int64_t)(start + n) * a.slots)[c];
-      },
-      [&](int i) {
-        const int row = i / VPR, c = i - row * VPR;
-        const int q = row >= cnt ? 1 : 0, n = row - q * cnt;
-        return reinterpret_cast<uint4 *>(xb[q] + n * rs + c * 16);
-      },
-      [&](int i, uint4 v) { return keep_live(v, live_in_chunk<F, RT>(a.gd.K, i % VPR)); });
+  __shared__ int sig[16];
+  stage_h_parts<4, 4, M>(a.hf + (int64_t)start * a.I, cnt, a.I, 5 * a.gd.Q, xb[0], xb[1], rs, sig);
 #pragma unroll
   for (int q = 0; q < 2; ++q) zero_row(xb[q] + 16 * rs, a.slots, threadIdx.x, 256);
   __syncthreads();
@@ -886,14 +898,15 @@ __device__ inline void down_work(const DownArgs &a, char *smem, int tile, int ry
   }
   if (n >= cnt) return;
   const int64_t p = start + n;
+  const int us = -1 - sig[n];  // the trits entered as 2t, h as 2^sig h
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row0 = (rtb + 4 * r) * 16 + 4 * g;
-    float4 o;  // the trits entered as 2t
-    o.x = (acc[r][0] * 0.5f) * sd[r].x;
-    o.y = (acc[r][1] * 0.5f) * sd[r].y;
-    o.z = (acc[r][2] * 0.5f) * sd[r].z;
-    o.w = (acc[r][3] * 0.5f) * sd[r].w;
+    float4 o;
+    o.x = ldexpf(acc[r][0], us) * sd[r].x;
+    o.y = ldexpf(acc[r][1], us) * sd[r].y;
+    o.z = ldexpf(acc[r][2], us) * sd[r].z;
+    o.w = ldexpf(acc[r][3], us) * sd[r].w;
     *reinterpret_cast<float4 *>(a.O + p * a.H + row0) = o;
   }
 }
@@ -916,8 +929,8 @@ struct DownCombineArgs {
   const uint8_t *down_p;
   int64_t stride_d;
   const float *down_s;
-  const uint16_t *hp;  // [2][pairs][slots] fp16 parts of h (operand layout), contiguous
-  int slots;
+  const float *hf;  // [pairs][I] fp32 h in grouped order
+  int slots, I;
   const int32_t *tiles, *ntiles, *sorted_token;
   const float *pair_w;  // [pairs] routing weight of each grouped pair
   int P, T, H, max_tiles;
@@ -930,8 +943,9 @@ struct DownCombineArgs {
 constexpr int kDcWaves = 8;
 
 // Decode path with few pairs (T*k <= 32): workgroup = one 16-row block of the
-// H outputs for all work tiles. The two fp16 parts of h of every pair are
-// staged in LDS together with the first tile descriptors; wavefront w then takes
+// H outputs for all work tiles. The two fp16 parts of the scaled h of every
+// pair are staged in LDS (the first tile's weights in flight meanwhile);
+// wavefront w then takes
 // tiles w, w + 8, ... in order and adds pair_w * o (o = sd * (Td h)) into its
 // own LDS accumulator of the pair's token; the accumulators are summed in fixed
 // order, then Y and/or the residual bf16(x + y) are written. MFMA columns past
@@ -942,6 +956,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   __shared__ float yacc[kDcWaves][kDecodeMaxT][16];
   __shared__ int32_t s_tok[kDcMaxPairs];
   __shared__ float s_pw[kDcMaxPairs];
+  __shared__ int s_sig[kDcMaxPairs];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rt = blockIdx.x;
   constexpr int M = 5 * F + tail_mfmas(RT);
@@ -950,16 +965,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   const int nt = *a.ntiles;
   int4 td0 = make_int4(0, 0, 1, 0);
   if (wave < a.max_tiles) td0 = reinterpret_cast<const int4 *>(a.tiles)[wave];  // first tile, before nt is known
-  // first staging batch in flight, then the first tile's weights, then the stores
-  constexpr int VPR = 4 * M;  // 16-byte chunks per staged row
-  constexpr int NT = 64 * kDcWaves, NB = 8;
-  const int nchunk = 2 * a.P * VPR;
-  uint4 sv[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int c = threadIdx.x + j * NT;
-    if (c < nchunk) sv[j] = reinterpret_cast<const uint4 *>(a.hp)[c];
-  }
+  // the first tile's weights in flight while h is staged
   uint2 dd0[F];
   uint32_t ddw0 = 0, dsh0 = 0;
   float4 sd0 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -970,30 +976,15 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
     if constexpr (RT > 0) load_tail<RT>(dt, F, lane, ddw0, dsh0);
     sd0 = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)td0.x * a.H + rt * 16 + 4 * g);
   }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int c = threadIdx.x + j * NT;
-    if (c < nchunk) reinterpret_cast<uint4 *>(hps)[c] = keep_live(sv[j], live_in_chunk<F, RT>(a.gd.K, c % VPR));
-  }
-  for (int base = threadIdx.x + NB * NT; base < nchunk; base += NT * NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int c = base + j * NT;
-      if (c < nchunk) sv[j] = reinterpret_cast<const uint4 *>(a.hp)[c];
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int c = base + j * NT;
-      if (c < nchunk) reinterpret_cast<uint4 *>(hps)[c] = keep_live(sv[j], live_in_chunk<F, RT>(a.gd.K, c % VPR));
-    }
-  }
+  const int plane = a.P * a.slots * 2;
+  stage_h_parts<kDcWaves, kDcMaxPairs / kDcWaves, M>(a.hf, a.P, a.I, 5 * a.gd.Q, hps, hps + plane, a.slots * 2,
+                                                     s_sig);
   if ((int)threadIdx.x < a.P) {
     s_tok[threadIdx.x] = a.sorted_token[threadIdx.x];
     s_pw[threadIdx.x] = a.pair_w[threadIdx.x];
   }
   for (int i = lane; i < kDecodeMaxT * 16; i += 64) (&yacc[wave][0][0])[i] = 0.f;
   lds_barrier();  // the first tile's weights may still be in flight
-  const int plane = a.P * a.slots * 2;
   for (int tile = wave; tile < nt; tile += kDcWaves) {
     const bool first = tile == wave;
     const int4 td = first ? td0 : reinterpret_cast<const int4 *>(a.tiles)[tile];
@@ -1035,10 +1026,11 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
     if (live) {
       const int tok = s_tok[p];
       const float wt = s_pw[p];
+      const int us = -1 - s_sig[p];  // the trits entered as 2t, h as 2^sig h
       const float sdv[4] = {sd.x, sd.y, sd.z, sd.w};
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        yacc[wave][tok][4 * g + v] = fmaf(wt, (acc[v] * 0.5f) * sdv[v], yacc[wave][tok][4 * g + v]);
+        yacc[wave][tok][4 * g + v] = fmaf(wt, ldexpf(acc[v], us) * sdv[v], yacc[wave][tok][4 * g + v]);
     }
   }
   __syncthreads();
@@ -1437,11 +1429,10 @@ static int64_t ffn_max_blocks(int64_t pairs, int64_t E) { return cdiv(pairs, 64)
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   (void)H;
   const int64_t P = T * k;
-  const Geom gi = make_geom(I);
   size_t o = 0;
   o = align_up(o + ffn_max_tiles(P, E) * 16, 256);
   o = align_up(o + 16, 256);
-  o = align_up(o + (size_t)2 * P * gi.slots * 2, 256);
+  o = align_up(o + (size_t)P * I * 4, 256);
   o = align_up(o + (size_t)P * 4, 256);
   o = align_up(o + ffn_max_blocks(P, E) * 16, 256);
   o = align_up(o + 16, 256);
@@ -1458,8 +1449,8 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   o = align_up(o + ffn_max_tiles(P, E) * 16, 256);
   f.ntiles = (int32_t *)(b + o);
   o = align_up(o + 16, 256);
-  f.hp = (uint16_t *)(b + o);
-  o = align_up(o + (size_t)2 * P * make_geom(I).slots * 2, 256);
+  f.hf = (float *)(b + o);
+  o = align_up(o + (size_t)P * I * 4, 256);
   f.pw = (float *)(b + o);
   o = align_up(o + (size_t)P * 4, 256);
   f.blocks = (int32_t *)(b + o);
@@ -1496,8 +1487,7 @@ static GateUpArgs gateup_args(const tmoe_moe_weights *W, const uint16_t *X, int6
   ga.ntiles = fw.ntiles;
   ga.sorted_token = sorted_token;
   ga.h = Hout;
-  ga.hp = fw.hp;
-  ga.hp_plane = P * gi.slots;
+  ga.hf = fw.hf;
   ga.gx = gh;
   ga.gd = gi;
   ga.I = (int)W->inter;
@@ -1531,12 +1521,12 @@ static int run_down(hipStream_t st, const tmoe_moe_weights *W, const FfnWs &fw, 
   da.down_p = W->down_p;
   da.stride_d = W->stride_d;
   da.down_s = W->down_s;
-  da.hp = fw.hp;
-  da.hp_plane = P * gi.slots;
+  da.hf = fw.hf;
   da.tiles = fw.tiles;
   da.ntiles = fw.ntiles;
   da.O = O;
   da.H = (int)W->hidden;
+  da.I = (int)W->inter;
   da.slots = gi.slots;
   da.gd = gi;
   da.stream_w = P < 32 * W->n_experts;  // with many tiles per expert the caches serve the re-reads
@@ -1575,8 +1565,9 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
     da.down_p = W->down_p;
     da.stride_d = W->stride_d;
     da.down_s = W->down_s;
-    da.hp = fw.hp;
+    da.hf = fw.hf;
     da.slots = gi.slots;
+    da.I = (int)I;
     da.tiles = fw.tiles;
     da.ntiles = fw.ntiles;
     da.sorted_token = r.sorted_token;

@@ -340,6 +340,22 @@ def _raw_expert(cfg, layer, e):
     return _EXPERT_CACHE[key]
 
 
+def _prefetch_experts(cfg, layer, experts):
+    """Draws the raw fp32 matrices of `experts` on the host, in parallel (the
+    generator releases the interpreter lock)."""
+    import concurrent.futures
+    todo = [int(e) for e in experts if (cfg, layer, int(e)) not in _EXPERT_CACHE]
+    with concurrent.futures.ThreadPoolExecutor(16) as ex:
+        list(ex.map(lambda e: _raw_expert(cfg, layer, e), todo))
+
+
+def _scaled(xb, scale):
+    """bf16 bit patterns of scale * x (scale a power of two: exact)."""
+    if scale == 1:
+        return xb
+    return ti.f32_to_bf16_bits(ti.bf16_bits_to_f32(xb) * np.float32(scale))
+
+
 @pytest.fixture(scope="module")
 def layers():
     from ternary_weight_moe_base_amd import synthetic
@@ -367,16 +383,23 @@ def _run_layer(tm, W, xb, clamp=7.0):
     return dict(Y=host(Y), idx=host(idx), w=host(w), pos=host(pos), nfix=int(host(nf)[0]))
 
 
-@pytest.mark.parametrize("cfg,T,bias_kind,clamp", [(2, 1, None, 7.0), (2, 1, None, math.inf), (3, 64, "zipf", 7.0),
-                                                   (2, 5, None, 7.0), (2, 4, None, 7.0), (3, 16, "zipf", 7.0),
-                                                   (5, 256, None, 7.0)])
-def test_layer_parity(tm, layers, cfg, T, bias_kind, clamp):
-    say(f"layer cfg={cfg} T={T} clamp={clamp}")
+# (cfg, T, bias, clamp, input scale): both clamp modes; without the clamp,
+# inputs x4 drive |h| past the fp16 range (up to ~1e5), and inputs x2^-10 make
+# every h tiny (~1e-6): the down projection's per-pair scaling must hold both.
+@pytest.mark.parametrize("cfg,T,bias_kind,clamp,scale", [
+    (2, 1, None, 7.0, 1), (2, 1, None, math.inf, 1), (3, 64, "zipf", 7.0, 1), (3, 64, "zipf", math.inf, 1),
+    (2, 5, None, 7.0, 1), (2, 4, None, 7.0, 1), (3, 16, "zipf", 7.0, 1), (5, 256, None, 7.0, 1),
+    (2, 1, None, math.inf, 4), (3, 64, "zipf", math.inf, 4), (2, 1, None, 7.0, 2.0 ** -10),
+    (5, 256, None, 7.0, 2.0 ** -10), (2, 3, None, math.inf, 16)])
+def test_layer_parity(tm, layers, cfg, T, bias_kind, clamp, scale):
+    say(f"layer cfg={cfg} T={T} clamp={clamp} input scale={scale}")
     W = layers(cfg, 0, bias_kind)
-    xb = ti.activations(cfg, T)
+    xb = _scaled(ti.activations(cfg, T), scale)
     got = _run_layer(tm, W, xb, clamp)
-    ref = O.moe_layer(xb, ti.router_matrix(cfg, 0), ti.router_bias(cfg, bias_kind),
-                      lambda e: _raw_expert(cfg, 0, e), k=8, clamp=clamp)
+    Wr, bias = ti.router_matrix(cfg, 0), ti.router_bias(cfg, bias_kind)
+    _prefetch_experts(cfg, 0, np.unique(O.router_topk(O.bf16_to_f64(xb), Wr, bias, 8)[0]))
+    ref = O.moe_layer(xb, Wr, bias, lambda e: _raw_expert(cfg, 0, e), k=8, clamp=clamp)
+    say(f"  max |h| {np.abs(ref['H']).max():.3e}, min |h| {np.abs(ref['H']).min():.3e}")
     assert np.array_equal(got["idx"], ref["idx"])
     assert np.array_equal(got["pos"], ref["pos"])
     err = O.max_normalized_error(got["Y"], ref["Y"])
@@ -449,30 +472,62 @@ def test_layer_token_blocked(tm, E, k, T):
     assert O.max_normalized_error(host(O_), ref["O"]) <= TOL
 
 
-def test_layer_prefill_sampled(tm, layers):
-    # prefill of 4096 tokens: router and grouping checked on every token, the
-    # expert outputs on a sample of tokens (their experts computed by the oracle)
-    cfg, T = 4, 4096
+def _grouped_ffn_reference(cfg, layer, x, sorted_token, offsets, clamps):
+    """Oracle expert FFN of every grouped pair, expert by expert in parallel
+    threads: {clamp: (H, O)} in grouped order (the same per-expert steps as the
+    oracle's moe_layer: absmean ternarization, dense dequantized weights,
+    expert_ffn)."""
+    import concurrent.futures
+    P = len(sorted_token)
+    out = {c: (np.zeros((P, 512)), np.zeros((P, 2048))) for c in clamps}
+
+    def one(e):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            return
+        deq = [O.dequantize(*O.ternarize_absmean(m)) for m in _raw_expert(cfg, layer, e)]
+        xe = x[sorted_token[lo:hi]]
+        for c in clamps:
+            _, _, h, o = O.expert_ffn(xe, *deq, c)
+            out[c][0][lo:hi], out[c][1][lo:hi] = h, o
+    with concurrent.futures.ThreadPoolExecutor(16) as ex:
+        list(ex.map(one, range(len(offsets) - 1)))
+    return out
+
+
+def test_layer_prefill_every_row(tm, layers):
+    """Prefill of 4096 tokens (uniform routing bias), in both clamp modes:
+    router and grouping on every token; Y of the layer on every one of the 4096
+    rows; h and the expert outputs of all 32,768 pairs through the step-by-step
+    ABI (tmoe_expert_ffn), all against the oracle."""
+    cfg, T, k, E = 4, 4096, 8, 256
     W = layers(cfg, 0, "uniform")
     xb = ti.activations(cfg, T)
-    say("layer prefill T=4096")
-    got = _run_layer(tm, W, xb)
     Wr, b = ti.router_matrix(cfg, 0), ti.router_bias(cfg, "uniform")
     ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, 8)
-    assert np.array_equal(got["idx"], ridx)
-    counts, offsets, st, ss, pos = O.group_by_expert(ridx, 256)
-    assert np.array_equal(got["pos"], pos)
-    say(f"  expert counts: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}")
-    x = O.bf16_to_f64(xb)
-    for t in (0, 1234, 4095):
-        y = np.zeros(2048)
-        for j in range(8):
-            Wg, Wu, Wd = _raw_expert(cfg, 0, int(ridx[t, j]))
-            deq = [O.dequantize(*O.ternarize_absmean(m)) for m in (Wg, Wu, Wd)]
-            y += rw[t, j] * O.expert_ffn(x[t:t + 1], *deq)[3][0]
-        err = O.max_normalized_error(got["Y"][t:t + 1], y[None])
-        say(f"  token {t}: max normalized error {err:.2e}")
+    counts, offsets, st, ss, pos = O.group_by_expert(ridx, E)
+    say(f"layer prefill T=4096: expert counts min {counts.min()} max {counts.max()} mean {counts.mean():.1f}")
+    _prefetch_experts(cfg, 0, range(E))
+    ref = _grouped_ffn_reference(cfg, 0, O.bf16_to_f64(xb), st, offsets, (7.0, math.inf))
+    g = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k, T * k)]
+    tm.group_by_expert(dev(ridx.astype(np.int32)), E, *g, ws=ws_bytes(tm.group_workspace_bytes(T, k, E)))
+    assert np.array_equal(host(g[1]), offsets) and np.array_equal(host(g[2]), st)
+    for clamp in (7.0, math.inf):
+        got = _run_layer(tm, W, xb, clamp)
+        assert np.array_equal(got["idx"], ridx)
+        assert np.array_equal(got["pos"], pos)
+        Href, Oref = ref[clamp]
+        Yref = O.combine(Oref, rw, pos)
+        err = O.max_normalized_error(got["Y"], Yref)
+        say(f"  clamp={clamp}: Y max normalized error over all {T} rows {err:.2e}")
         assert err <= TOL
+        O_ = torch.empty((T * k, 2048), dtype=torch.float32, device="cuda")
+        Hh = torch.empty((T * k, 512), dtype=torch.float32, device="cuda")
+        tm.expert_ffn(W, bf16_dev(xb), g[1], g[2], O_, ws_bytes(tm.ffn_workspace_bytes(T, W)), clamp=clamp, Hout=Hh)
+        eh, eo = O.max_normalized_error(host(Hh), Href), O.max_normalized_error(host(O_), Oref)
+        say(f"  clamp={clamp}: h error {eh:.2e}, expert outputs error {eo:.2e} over all {T * k} pairs")
+        assert eh <= TOL and eo <= TOL
+        del O_, Hh
 
 
 def test_layer_is_deterministic(tm, layers):

@@ -406,6 +406,49 @@ def test_moe_layer_identical_experts_and_k1():
         assert np.allclose(r1["Y"][t], O.expert_ffn(x[t:t + 1], *d)[3][0], rtol=1e-12)
 
 
+def test_moe_layer_distinct_experts_dense_form():
+    """The layer written densely over all experts, without grouping or slot
+    positions: Y[t] = sum over the k selected experts e of
+    softmax-over-the-selected(l)[e] * FFN_e(x_t), each FFN evaluated with
+    torch's own linear / clamp / silu on the dequantized weights (codeinsider.com.br,
+    "256 experts, 8 ativos": a weighted sum of the chosen experts' outputs).
+    Distinct experts, k = 3 and unequal weights make any slot / weight / expert
+    mix-up visible, as the swapped-weight check shows."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    g = np.random.default_rng(13)
+    H, I, E, k, T = 24, 8, 6, 3, 7
+    x_bits = ti.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
+    Wr = (g.standard_normal((E, H)) * 0.5).astype(np.float32)
+    experts = [[g.standard_normal(sh).astype(np.float32) for sh in ((I, H), (I, H), (H, I))] for _ in range(E)]
+    res = O.moe_layer(x_bits, Wr, None, lambda e: experts[e], k=k)
+    x = O.bf16_to_f64(x_bits)
+    logits = x @ Wr.astype(np.float64).T
+    Y = np.zeros((T, H))
+    Y_swapped = np.zeros((T, H))
+    for t in range(T):
+        order = np.argsort(-logits[t], kind="stable")
+        chosen = order[:k]
+        gaps = -np.diff(logits[t][order[:k + 1]])
+        assert gaps.min() > 1e-6  # well separated: the selection is unambiguous
+        p = np.exp(logits[t] - logits[t].max())
+        w = p[chosen] / p[chosen].sum()
+        assert np.ptp(w) > 0.05  # unequal weights
+        outs = []
+        for e in chosen:
+            deq = [torch.from_numpy(O.dequantize(*O.ternarize_absmean(m))) for m in experts[e]]
+            tx = torch.from_numpy(x[t:t + 1])
+            o = F.linear(F.silu(torch.clamp(F.linear(tx, deq[0]), max=7.0))
+                         * torch.clamp(F.linear(tx, deq[1]), min=-7.0, max=7.0), deq[2])
+            outs.append(o.numpy()[0])
+        Y[t] = sum(wj * oj for wj, oj in zip(w, outs))
+        Y_swapped[t] = w[1] * outs[0] + w[0] * outs[1] + sum(wj * oj for wj, oj in zip(w[2:], outs[2:]))
+        assert np.array_equal(np.sort(res["idx"][t]), np.sort(chosen))
+    assert np.allclose(res["Y"], Y, rtol=1e-12, atol=1e-12)
+    # a weight paired with another slot's output would be caught
+    assert O.max_normalized_error(Y_swapped, Y) > 1e-2
+
+
 def test_combine_hand_example():
     Ob = np.array([[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]])
     w = np.array([[0.25, 0.75], [1.0, 0.0]])
