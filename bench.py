@@ -43,7 +43,8 @@ WORKLOADS = {
             linear=True, mats=2048),
     2: dict(name="moe_layer_decode_T1", tokens=1, bias=None, layers=24, steps=2400, warmup=48),
     3: dict(name="moe_layer_decode_T64_zipf1.1", tokens=64, bias="zipf", layers=24, steps=480, warmup=48),
-    4: dict(name="moe_layer_prefill_T4096_uniform", tokens=4096, bias="uniform", layers=4, steps=40, warmup=4),
+    4: dict(name="moe_layer_prefill_T4096_uniform", tokens=4096, bias="uniform", layers=4, steps=40, warmup=4,
+            prof_steps=40, cpu_tokens=256),
     5: dict(name="moe_stack24_T256_residual", tokens=256, bias=None, layers=24, steps=20, warmup=2, stack=True),
     # one token at a time through the same 24-layer stack: per-token decode latency
     6: dict(name="moe_stack24_decode_T1_residual", tokens=1, bias=None, layers=24, steps=100, warmup=4, stack=True,
@@ -126,6 +127,7 @@ def parse():
     ap.add_argument("--kernel", default=None, help="kernel whose roofline is reported (default: the dominant one)")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill record of the default workload")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
     return ap.parse_args()
 
@@ -142,48 +144,80 @@ def ensure_built():
 
 
 # -------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg: int, wl: dict, n_tok: int | None, budget_s: float = 12.0):
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(cfg: int, wl: dict, n_tok: int | None, budget_s: float = 12.0, one_core_budget_s: float = 8.0):
     """The CPU oracle, untuned, timed on this host on a bounded sample of the
-    workload: successive token batches of the workload (for one-token decode,
-    token i through layer i mod 24) until `budget_s` seconds of oracle time or
-    n_tok tokens. The inputs a batch reads (router, raw fp32 experts it routes
-    to) are drawn before its timed call; only the oracle's moe_layer is timed."""
+    workload, twice: with every host core (the reported value) and with one
+    core (BLAS limited to one thread; the oracle's other steps are
+    single-threaded NumPy anyway). One-token decode: token i through layer
+    i mod 24 until the time budget or n_tok tokens. Batched workloads: the
+    first `cpu_tokens` tokens of the workload's batch (for the 4096-token
+    prefill, 256 tokens, which route to nearly every expert) as one batch
+    through layer 0. The inputs a call reads (router, raw fp32 experts it
+    routes to) are drawn before the call; only the oracle's moe_layer (which
+    ternarizes the routed experts itself) is timed."""
     import numpy as np
 
     import oracle as O
     import tmoe_inputs as ti
 
     threads = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        blas = 1
-    cfg = wl.get("model_cfg", cfg)
+    blas = _blas_threads()
+    mcfg = wl.get("model_cfg", cfg)
     one = wl["tokens"] == 1
-    if one:
-        batches = ((i % wl["layers"], ti.activations(cfg, i + 1)[i:i + 1]) for i in range(n_tok or 1000))
-    else:
-        x = ti.activations(cfg, wl["tokens"])
-        batches = ((0, x[j:j + 8]) for j in range(0, min(n_tok or len(x), len(x)), 8))
-    tokens, timed = 0, 0.0
-    with concurrent.futures.ThreadPoolExecutor(min(16, threads)) as ex:
+    pool = concurrent.futures.ThreadPoolExecutor(min(16, threads))
+
+    def prepare(layer, xb):
+        Wr, b = ti.router_matrix(mcfg, layer), ti.router_bias(mcfg, wl["bias"])
+        idx, _, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, K_TOP)
+        es = sorted(set(idx.ravel().tolist()))
+        mats = dict(zip(es, pool.map(lambda e: tuple(ti.expert_matrix(mcfg, layer, e, m) for m in range(3)), es)))
+        return Wr, b, mats
+
+    def timed_run(batches, budget):
+        tokens, timed = 0, 0.0
         for layer, xb in batches:
-            Wr, b = ti.router_matrix(cfg, layer), ti.router_bias(cfg, wl["bias"])
-            idx, _, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, K_TOP)
-            es = sorted(set(idx.ravel().tolist()))
-            mats = dict(zip(es, ex.map(lambda e: tuple(ti.expert_matrix(cfg, layer, e, m) for m in range(3)), es)))
+            Wr, b, mats = prepare(layer, xb)
             t0 = time.perf_counter()
             O.moe_layer(xb, Wr, b, lambda e: mats[e], k=K_TOP)
             timed += time.perf_counter() - t0
             tokens += xb.shape[0]
-            if timed >= budget_s:
+            if timed >= budget:
                 break
-    what = "token i through layer i mod 24" if one else "batches of 8 tokens through layer 0"
+        return tokens, timed
+
+    if one:
+        def batches():
+            return ((i % wl["layers"], ti.activations(mcfg, i + 1)[i:i + 1]) for i in range(n_tok or 1000))
+        what = "token i through layer i mod 24"
+    else:
+        n = n_tok or wl.get("cpu_tokens", 8)
+        xs = ti.activations(mcfg, wl["tokens"])[:n]
+
+        def batches():
+            return iter([(0, xs)])
+        what = f"the first {n} tokens of the batch as one call through layer 0"
+    tokens, timed = timed_run(batches(), budget_s)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            tokens1, timed1 = timed_run(batches(), one_core_budget_s)
+        one_core = {"value": tokens1 / timed1, "unit": "tokens/s", "cores": 1,
+                    "sample": f"{tokens1} token(s), {timed1:.1f} s of oracle time"}
+    except ImportError:  # pragma: no cover
+        one_core = None
+    pool.shutdown()
     sample = (f"{tokens} token(s) of the {wl['name']} workload ({what}) through the oracle's moe_layer; "
               f"{timed:.1f} s of oracle time; router and raw fp32 experts drawn beforehand, untimed")
     return {"value": tokens / timed, "unit": "tokens/s", "cores": blas if blas > 1 else 1,
-            "host_cpus": threads, "kind": "oracle", "sample": sample}
+            "host_cpus": threads, "kind": "oracle", "sample": sample, "one_core": one_core}
 
 
 # ------------------------------------------------------------------ LM head
@@ -552,37 +586,35 @@ def main_lm_head(args, wl: dict):
 
 
 # ------------------------------------------------------------------ workload
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures a single GPU only: the layer is data-parallel, and this benchmark "
-              "runs and reports one MI355X (--gpus 1). Multi-GPU runs are not supported.", file=sys.stderr)
-        sys.exit(2)
+EVICT_BYTES = 1 << 30  # streamed between the untimed and the timed replay (4x the 256 MB last-level cache)
+
+
+def evict_caches(buf) -> None:
+    """Reads and writes `buf` (EVICT_BYTES) so that nothing the timed steps read
+    is still in the L2 or last-level caches when they start."""
+    import torch
+
+    buf.add_(1)
+    torch.cuda.synchronize()
+
+
+def run_layer(args, cfg: int, K: int, W_: int, L: int, evict) -> dict:
+    """One MoE-layer workload (configs 2-6, 8): builds its layers, runs W_
+    warm-up steps, captures the K timed steps in one HIP graph, replays it
+    once untimed, evicts the caches, replays it timed; then times each kernel
+    over the same steps launched eagerly (at most `prof_steps` of them).
+    Returns the JSON record of the run (no CPU baseline)."""
     import numpy as np
     import torch
 
-    ensure_built()
     import ternary_weight_moe_base_amd as tm
-    import tmoe_inputs as ti
     from ternary_weight_moe_base_amd import synthetic
 
-    cfg = args.config
     wl = dict(WORKLOADS[cfg])
-    if wl.get("lm_head"):
-        return main_lm_head(args, wl)
-    if wl.get("linear"):
-        return main_linear(args, wl)
-    if wl.get("attention"):
-        return main_attention(args, wl)
-    K = args.steps if args.steps is not None else wl["steps"]
-    W_ = args.warmup if args.warmup is not None else wl["warmup"]
-    L = args.layers if args.layers is not None else wl["layers"]
     T = wl["tokens"]
     stack = wl.get("stack", False)
     mcfg = wl.get("model_cfg", cfg)  # seeds of the model's weights and activations
     dev = torch.device("cuda")
-    torch.cuda.init()
 
     t0 = time.perf_counter()
     layers = [synthetic.build_layer(mcfg, l, wl["bias"]) for l in range(L)]
@@ -591,7 +623,7 @@ def main():
         for l in range(L):
             layers[l] = tm.experts_on_host(layers[l])
         torch.cuda.empty_cache()
-    log(f"built {L} layers in {time.perf_counter() - t0:.1f} s")
+    log(f"{wl['name']}: built {L} layers in {time.perf_counter() - t0:.1f} s")
 
     ws = torch.zeros(tm.moe_workspace_bytes(T, layers[0]), dtype=torch.uint8, device=dev)
     Y = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -604,7 +636,7 @@ def main():
         Xw = torch.empty((1, H), dtype=X.dtype, device=dev)  # the token's residual stream
         idx_buf = torch.empty((n_steps * L, T, K_TOP), dtype=torch.int32, device=dev)
     else:
-        n_batches = n_steps if cfg == 2 else min(n_steps, 64)
+        n_batches = n_steps if cfg == 2 else min(n_steps, 64 if T < 4096 else 16)
         X = synthetic.activations(cfg, n_batches * T).view(n_batches, T, H)
         idx_buf = torch.empty((n_steps, T, K_TOP), dtype=torch.int32, device=dev)
 
@@ -623,7 +655,6 @@ def main():
     torch.cuda.synchronize()
 
     use_graph = not args.no_graph
-    prof_cap = K * (L if stack else 1)
     graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
@@ -637,6 +668,7 @@ def main():
         torch.cuda.synchronize()
         graph.replay()  # first replay of a fresh graph: untimed
         torch.cuda.synchronize()
+    evict()  # the timed steps start with cold caches, whatever K is
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -648,13 +680,16 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Per-kernel durations: the same K steps launched again (eagerly), one
-    # kernel at a time carrying start/stop events recorded by its own dispatch
-    # on the stream it runs on.
+    # Per-kernel durations: the same steps launched again (eagerly), one kernel
+    # at a time carrying start/stop events recorded by its own dispatch on the
+    # stream it runs on.
+    prof_steps = min(K, wl.get("prof_steps", K))
+    prof_cap = prof_steps * (L if stack else 1)
     kern = {}
     for name in (DECODE_KERNELS if T <= 3 else BATCH_KERNELS):
+        evict()
         tm.profile_begin(name, prof_cap)
-        for i in range(W_, W_ + K):
+        for i in range(W_, W_ + prof_steps):
             step(i)
         ms = tm.profile_end(prof_cap)
         if len(ms):
@@ -667,24 +702,24 @@ def main():
 
     # algorithmic bytes: packed experts (+ scales) with >= 1 routed token, router, X, Y
     idx_h = idx_buf.cpu().numpy()
-    if stack:
-        sel = idx_h[W_ * L:(W_ + K) * L]
-    else:
-        sel = idx_h[W_:W_ + K]
+    sel = idx_h[W_ * L:(W_ + K) * L] if stack else idx_h[W_:W_ + K]
     n_hit = np.array([len(np.unique(s)) for s in sel])
     step_bytes = ROUTER_BYTES + n_hit * EXPERT_BYTES + T * H * 2 + T * H * (2 if stack else 4)
     hbm_gbs = float(step_bytes.sum()) / elapsed / 1e9
 
     # roofline of the dominant kernel (largest total time per step)
-    per_step_us = {n: float(np.sum(v)) * 1e3 / layer_passes for n, v in kern.items()}
+    prof_passes = prof_steps * (L if stack else 1)
+    per_step_us = {n: float(np.sum(v)) * 1e3 / prof_passes for n, v in kern.items()}
     dom = args.kernel if args.kernel else max(per_step_us, key=per_step_us.get)
-    roof = roofline(dom, kern[dom], n_hit, T, cfg, bias=wl["bias"] is not None)
+    sel_prof = sel[:prof_passes]
+    n_hit_prof = np.array([len(np.unique(s)) for s in sel_prof])
+    roof = roofline(dom, kern[dom], n_hit_prof, T, cfg, bias=wl["bias"] is not None)
     roof["kernels_us_per_layer"] = {n: round(v, 3) for n, v in per_step_us.items()}
 
     extra = {}
     if stack and T == 1:  # one token through the whole stack per step: its latency
         extra = {"token_latency_us": 1e6 * elapsed / K, "stack_tokens_per_s": K / elapsed}
-    out = {
+    return {
         "metric": METRIC,
         "value": tokens_per_layer_s,
         "unit": "tokens/s",
@@ -700,18 +735,65 @@ def main():
         "config": {"workload": wl["name"], "tokens_per_step": T, "layers_per_step": L if stack else 1,
                    "distinct_layers": L, "hidden": H, "experts": E, "top_k": K_TOP, "moe_intermediate": I,
                    "weights": "ternary, 5 trits/byte, fp32 row scales", "hip_graph": use_graph,
-                   "expert_memory": "pinned host, read over PCIe" if wl.get("host_experts") else "hbm"},
+                   "expert_memory": "pinned host, read over PCIe" if wl.get("host_experts") else "hbm",
+                   "timed_replay": f"cold: {EVICT_BYTES >> 20} MiB streamed after the untimed replay",
+                   "kernel_timing_steps": prof_steps},
         "achieved_hbm_gbs": hbm_gbs,
         "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": float(np.mean(step_bytes)) * (L if stack else 1),
         "roofline": roof,
         **extra,
     }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU only: the layer is data-parallel, and this benchmark "
+              "runs and reports one MI355X (--gpus 1). Multi-GPU runs are not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    ensure_built()
+
+    cfg = args.config
+    wl = dict(WORKLOADS[cfg])
+    if wl.get("lm_head"):
+        return main_lm_head(args, wl)
+    if wl.get("linear"):
+        return main_linear(args, wl)
+    if wl.get("attention"):
+        return main_attention(args, wl)
+    K = args.steps if args.steps is not None else wl["steps"]
+    W_ = args.warmup if args.warmup is not None else wl["warmup"]
+    L = args.layers if args.layers is not None else wl["layers"]
+    torch.cuda.init()
+    evict_buf = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = run_layer(args, cfg, K, W_, L, lambda: evict_caches(evict_buf))
+    # the metric's other half: the 4096-token prefill, with the same step counts
+    prefill = None
+    if cfg == 2 and not args.no_prefill:
+        torch.cuda.empty_cache()
+        wp = WORKLOADS[4]
+        Kp = args.steps if args.steps is not None else wp["steps"]
+        Wp = args.warmup if args.warmup is not None else wp["warmup"]
+        pf = run_layer(args, 4, Kp, Wp, wp["layers"], lambda: evict_caches(evict_buf))
+        prefill = {key: pf[key] for key in ("value", "unit", "steps", "warmup", "ms_per_step", "config", "roofline",
+                                            "achieved_hbm_gbs", "hbm_frac", "algorithmic_bytes_per_step")}
+        prefill["workload"] = pf["config"]["workload"]
+    del evict_buf
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_tokens)
+        if prefill is not None:
+            prefill["cpu_baseline"] = cpu_baseline(4, WORKLOADS[4], None)
     else:
         out["cpu_baseline"] = None
+        if prefill is not None:
+            prefill["cpu_baseline"] = None
+    if prefill is not None:
+        out["prefill"] = prefill
     print(json.dumps(out), flush=True)
 
 
