@@ -269,6 +269,25 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out);
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
 
+/* Layer call for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels as tmoe_moe_forward, with the workspace taken
+ * from a fixed array of TMOE_NOALLOC_SCRATCH_BYTES in the library's own device
+ * memory (one per GPU, reserved when the library's code is loaded on that
+ * GPU and held until the process ends). Allocates nothing. The first call on a
+ * device looks up that device's array (the calling thread's current device,
+ * which must be the stream's). Requests whose workspace
+ * (tmoe_moe_workspace_bytes) exceeds the array fail with TMOE_E_WORKSPACE
+ * before anything is enqueued: at the model's shape (hidden 2048, 256 experts,
+ * top 8, inter 512) up to 384 tokens fit. All calls on one GPU share its
+ * array, so calls that may overlap on one GPU (different streams, or
+ * different threads) race and must be serialized by the caller; each call
+ * writes every byte of it that it reads, so nothing needs clearing between
+ * calls. Arguments and errors otherwise as tmoe_moe_forward. */
+#define TMOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int tmoe_moe_forward_noalloc(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
+                             const tmoe_moe_options *opt);
+
 /* ------------------------------------------------------- attention half
  * The step before the MoE in every layer (ai.thesatyajit.com, "The
  * architecture around the quantization"; jj-blog, architecture list): layers

@@ -382,6 +382,22 @@ def moe_forward(W: MoEWeights, X, Y, ws, clamp: float = 7.0, idx=None, w=None, p
                                 ws.numel() * ws.element_size()), "moe_forward")
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TMOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(W: MoEWeights, X, Y, clamp: float = 7.0, idx=None, w=None, pos=None, n_fixup=None,
+                        resid_out=None, stream=None) -> None:
+    """moe_forward without a caller workspace: the library's fixed per-GPU
+    scratch array serves as the workspace (calls on one GPU must not overlap)."""
+    opt = _abi.MoEOptionsStruct()
+    opt.clamp = clamp
+    opt.reserved0 = 0
+    opt.idx, opt.w, opt.pos, opt.n_fixup, opt.resid_out = _ptr(idx), _ptr(w), _ptr(pos), _ptr(n_fixup), _ptr(resid_out)
+    T = X.shape[0]
+    _check(_load().tmoe_moe_forward_noalloc(_stream(stream), W.ref, _ptr(X), T, _ptr(Y), ctypes.byref(opt)),
+           "moe_forward_noalloc")
+
+
 # ------------------------------------------------------------- kernel timing
 def profile_begin(kernel: str, capacity: int) -> None:
     """Start recording HIP events around each launch of `kernel` (see _abi.KERNELS)."""

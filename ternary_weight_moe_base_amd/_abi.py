@@ -84,6 +84,7 @@ SIGNATURES = {
                              c_void_p]),
     "tmoe_moe_workspace_bytes": (c_int, [c_int64, c_void_p, POINTER(c_size_t)]),
     "tmoe_moe_forward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t]),
+    "tmoe_moe_forward_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
     "tmoe_attention_workspace_bytes": (c_size_t, [c_int64, c_void_p]),
     "tmoe_attention_forward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64,
                                        c_void_p, c_void_p, c_void_p, c_size_t]),

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtmoe.so")
 RUNNER = os.path.join(HERE, "tmoe_run")
-SOURCES = ["host_api.cpp", "quant.hip", "router.hip", "group.hip", "ffn.hip", "lmhead.hip", "attention.hip"]
+SOURCES = ["host_api.cpp", "quant.hip", "router.hip", "group.hip", "ffn.hip", "lmhead.hip", "attention.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

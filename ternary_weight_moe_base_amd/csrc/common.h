@@ -244,6 +244,12 @@ int launch_linear3(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N,
 int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,
                    float *Y, const uint16_t *resid_in, uint16_t *resid_out);
 
+// The whole layer (host_api.cpp): argument checks and the launch sequence of
+// tmoe_moe_forward on a given workspace, and that workspace's size.
+int moe_forward_impl(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
+                     const tmoe_moe_options *opt, void *ws, size_t ws_bytes);
+int moe_workspace_total(int64_t T, const tmoe_moe_weights *W, size_t *out);
+
 // LM head (lmhead.hip)
 size_t lmh_ws_bytes(int64_t T, int64_t V, int k);
 int launch_lm_head(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const uint16_t *W, int64_t V, int k,

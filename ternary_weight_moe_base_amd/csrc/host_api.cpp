@@ -487,6 +487,23 @@ int tmoe_moe_workspace_bytes(int64_t T, const tmoe_moe_weights *W, size_t *out) 
 int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
                      const tmoe_moe_options *opt, void *ws, size_t ws_bytes) {
   clear_error();
+  return moe_forward_impl(stream, W, X, T, Y, opt, ws, ws_bytes);
+}
+
+}  // extern "C"
+
+namespace tmoe {
+
+int moe_workspace_total(int64_t T, const tmoe_moe_weights *W, size_t *out) {
+  int rc = check_weights(W);
+  if (rc) return rc;
+  REQUIRE(T >= 0, TMOE_E_ARG, "negative T");
+  *out = layer_ws(T, W).total;
+  return TMOE_OK;
+}
+
+int moe_forward_impl(void *stream, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, float *Y,
+                     const tmoe_moe_options *opt, void *ws, size_t ws_bytes) {
   int rc = check_weights(W);
   if (rc) return rc;
   REQUIRE(T >= 0, TMOE_E_ARG, "negative T");
@@ -535,6 +552,10 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   if (rc) return rc;
   return launch_combine(st, O, wt, pos, T, k, H, Y, o.resid_out ? X : nullptr, o.resid_out);
 }
+
+}  // namespace tmoe
+
+extern "C" {
 
 int tmoe_profile_begin(int kernel, int capacity) {
   clear_error();
