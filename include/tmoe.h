@@ -166,12 +166,22 @@ int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t
  * top-(k+1) ranking is not separated by that bound is recomputed in
  * double-double arithmetic on the device. Indices therefore equal those of
  * the exact logits except for logits closer than ~1e-30 relative.
+ * From 1024 tokens on, when `logits` is NULL, the logits are first formed on the
+ * bf16 matrix cores (each fp32 weight as the sum of two bf16 parts, with a
+ * rigorous bound, about 2.5e-5 of |x| |w_e| for H = 2048) only to pick
+ * each token's candidates (the k+1 largest and every expert within twice
+ * that bound of the (k+1)-th); the candidates are recomputed in fp64 and
+ * ranked, and the softmax uses those fp64 values, with the same certificate
+ * and double-double fall-back. When `logits` is requested, all logits are
+ * accumulated in fp64 (on the fp64 matrix cores beyond 64 tokens).
  *   X bf16 [T][H]; Wr fp32 [E][H]; bias fp32 [E] or NULL;
  *   idx int32 [T][k]; w fp32 [T][k]; logits fp32 [T][E] or NULL;
  *   n_fixup: int32 device scalar or NULL, receives the number of tokens that
  *   took the double-double path.
  * Limits: 1 <= k <= min(E, 16), E <= 1024, H in {256, 512, 1024, 2048, 4096}. */
-size_t tmoe_router_workspace_bytes(int64_t T, int64_t E); /* fp64 logits and bound slots; no zero-fill needed */
+size_t tmoe_router_workspace_bytes(int64_t T, int64_t E); /* fp64 logits, bound slots and (T >= 1024) the bf16
+                                                              parts of the router rows for H up to 4096; no
+                                                              zero-fill needed */
 int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                      int64_t E, int k, int32_t *idx, float *w, float *logits, int32_t *n_fixup, void *ws,
                      size_t ws_bytes);

@@ -159,11 +159,18 @@ int launch_unpack_tiled(hipStream_t st, const uint8_t *Pt, int64_t R, int64_t K,
 // plain store per slot (no atomics, nothing to clear); a token's bound is the
 // maximum of its nb slots. nb = experts / 4 (VALU logits) or / 16 (matrix cores).
 struct RouterWs {
-  uint64_t *bnd;  // [T][nb], capacity T * ceil(E / 4)
-  double *lg;     // [T][E] fp64 logits
+  uint64_t *bnd;     // [T][nb], capacity T * ceil(E / 4)
+  double *lg;        // [T][E] fp64 logits (the bf16 matrix-core candidate logits on that path)
+  // from 1024 tokens on (the bf16 candidate path):
+  uint16_t *parts;   // [2][E][H] bf16 parts w1, w2 of the router rows (H <= 4096)
+  uint64_t *wmax;    // [2][ceil(E / 4)] largest row norm and |bias| per split workgroup
+  double *wnorm;     // [E] row norms |w_e|_2
+  float *part;       // [4][T][E] fp32 slice sums of the candidate logits
 };
-size_t router_ws_bytes(int64_t T, int64_t E);
-RouterWs router_ws_carve(void *ws, int64_t T, int64_t E);
+// H: the router's hidden size (the bf16 parts of its rows take 4 E H bytes from 1024 tokens on).
+size_t router_ws_bytes(int64_t T, int64_t E, int64_t H);
+RouterWs router_ws_carve(void *ws, int64_t T, int64_t E, int64_t H);
+constexpr int64_t kRouterMaxH = 4096;  // largest router hidden size (sizes tmoe_router_workspace_bytes)
 // Logits (fp64 VALU for T <= 64, fp64 matrix cores above) and the certified
 // top-k with its double-double fall-back (two kernels).
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,

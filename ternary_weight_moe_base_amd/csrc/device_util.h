@@ -13,6 +13,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// 16 bytes from LDS (one matrix-core operand of a lane)
+__device__ __forceinline__ u32x4 lds16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
 struct KeepChunk {
   __device__ uint4 operator()(int, uint4 v) const { return v; }
 };

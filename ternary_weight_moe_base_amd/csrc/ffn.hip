@@ -116,7 +116,6 @@ __device__ __forceinline__ f32x4 mfma_f16(const uint32_t *a, u32x4 b, f32x4 c) {
                                                 0);
 }
 
-__device__ __forceinline__ u32x4 lds16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // Workgroups of a batched gate/up or down grid that walks its items (two per
 // CU: the staged activations take 71 KB of LDS). With few pairs per expert
@@ -223,65 +222,70 @@ __device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const 
 // all-zero or non-finite row): hi = fp16(2^sig h) then never overflows, and
 // lo = fp16(2^sig h - hi) keeps the next 11 bits; values below 2^-28 of the
 // row's largest only lose bits under 2^-39 of it. Wavefront w of NW takes rows
-// w, w + NW, ... (at most RPW each); all loads of a wavefront are issued before
-// its first row is reduced.
-template <int NW, int RPW, int M>
+// w, w + NW, ... (at most RPW each), RB rows at a time: the loads of a batch
+// are all issued before its first row is reduced.
+template <int NW, int RPW, int M, int RB = RPW>
 __device__ inline void stage_h_parts(const float *h, int cnt, int I, int q5, char *pl0, char *pl1, int rs, int *sig) {
+  static_assert(RPW % RB == 0, "whole batches");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NCH = 4 * M;            // 16-byte chunks (8 positions) per staged row
   constexpr int NPL = (NCH + 63) / 64;  // chunks per lane
-  float v[RPW][NPL][8];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int n = wave + NW * i;
+  for (int b0 = 0; b0 < RPW; b0 += RB) {
+    if (wave + NW * b0 >= cnt) break;
+    float v[RB][NPL][8];
 #pragma unroll
-    for (int u = 0; u < NPL; ++u) {
-      const int c = lane + 64 * u;
-      const int quarter = c / M, j0 = 8 * (c - quarter * M), k0 = q5 * quarter + j0;
+    for (int i = 0; i < RB; ++i) {
+      const int n = wave + NW * (b0 + i);
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // q5, I and k0 are even, so both values of a pair are inputs or neither is
-        float2 f = make_float2(0.f, 0.f);
-        if (n < cnt && c < NCH && j0 + e < q5 && k0 + e < I)
-          f = *reinterpret_cast<const float2 *>(h + (int64_t)n * I + k0 + e);
-        v[i][u][e] = f.x;
-        v[i][u][e + 1] = f.y;
+      for (int u = 0; u < NPL; ++u) {
+        const int c = lane + 64 * u;
+        const int quarter = c / M, j0 = 8 * (c - quarter * M), k0 = q5 * quarter + j0;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          // q5, I and k0 are even, so both values of a pair are inputs or neither is
+          float2 f = make_float2(0.f, 0.f);
+          if (n < cnt && c < NCH && j0 + e < q5 && k0 + e < I)
+            f = *reinterpret_cast<const float2 *>(h + (int64_t)n * I + k0 + e);
+          v[i][u][e] = f.x;
+          v[i][u][e + 1] = f.y;
+        }
       }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int n = wave + NW * i;
-    if (n >= cnt) break;
-    uint32_t mx = 0;
+    for (int i = 0; i < RB; ++i) {
+      const int n = wave + NW * (b0 + i);
+      if (n >= cnt) break;
+      uint32_t mx = 0;
 #pragma unroll
-    for (int u = 0; u < NPL; ++u)
+      for (int u = 0; u < NPL; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = max(mx, __float_as_uint(v[i][u][e]) & 0x7FFFFFFFu);
-    mx = wave_max_u32(mx);
-    int s = 0;
-    if (mx != 0 && mx < 0x7F800000u) {
-      int ex;
-      (void)frexpf(__uint_as_float(mx), &ex);  // largest |h| = f 2^ex, f in [1/2, 1)
-      s = 15 - ex;
-    }
-#pragma unroll
-    for (int u = 0; u < NPL; ++u) {
-      const int c = lane + 64 * u;
-      if (c >= NCH) continue;
-      uint32_t w[2][4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float a0 = ldexpf(v[i][u][e], s), a1 = ldexpf(v[i][u][e + 1], s);
-        const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
-        const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
-        w[0][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        w[1][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        for (int e = 0; e < 8; ++e) mx = max(mx, __float_as_uint(v[i][u][e]) & 0x7FFFFFFFu);
+      mx = wave_max_u32(mx);
+      int sg = 0;
+      if (mx != 0 && mx < 0x7F800000u) {
+        int ex;
+        (void)frexpf(__uint_as_float(mx), &ex);  // largest |h| = f 2^ex, f in [1/2, 1)
+        sg = 15 - ex;
       }
-      *reinterpret_cast<uint4 *>(pl0 + n * rs + c * 16) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
-      *reinterpret_cast<uint4 *>(pl1 + n * rs + c * 16) = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+#pragma unroll
+      for (int u = 0; u < NPL; ++u) {
+        const int c = lane + 64 * u;
+        if (c >= NCH) continue;
+        uint32_t w[2][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float a0 = ldexpf(v[i][u][e], sg), a1 = ldexpf(v[i][u][e + 1], sg);
+          const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+          const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
+          w[0][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          w[1][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        *reinterpret_cast<uint4 *>(pl0 + n * rs + c * 16) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+        *reinterpret_cast<uint4 *>(pl1 + n * rs + c * 16) = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+      }
+      if (lane == 0) sig[n] = sg;
     }
-    if (lane == 0) sig[n] = s;
   }
 }
 
@@ -921,6 +925,132 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
     const int tile = item / groups;
     down_work<F, RT, R>(a, smem, tile, item - tile * groups);
     __syncthreads();  // the staged h parts are reused by the next item
+  }
+}
+
+// ------------------------------------------------ down, token-blocked
+// Many pairs per expert (prefill): a workgroup takes one of the gate/up
+// blocks (up to 64 pairs of one expert) and H / kDtbGroups output rows. The
+// block's h rows are staged once as their scaled fp16 parts (two planes of 64
+// rows, 138 KB of LDS); each wavefront then walks its row tiles kDtbR at a
+// time: the weights of a K step are decoded once and feed 4 token tiles x 2
+// parts x kDtbR row tiles, and each operand slice read from LDS feeds kDtbR
+// products. Token tiles past the block are skipped; columns past the block
+// read its last pair and are not stored. The next row tiles' weights are in
+// flight while the current ones are multiplied (the first ones while h is
+// staged).
+constexpr int kDtbWaves = 8, kDtbR = 4, kDtbGroups = 2;
+
+template <int F, int RT>
+struct DtbWeights {
+  uint2 d[kDtbR][F];
+  uint32_t dw[kDtbR], sh[kDtbR];
+  float4 sd[kDtbR];
+};
+
+template <int F, int RT>
+__device__ __forceinline__ void dtb_load(const DownArgs &a, int e, int rt, int lane, DtbWeights<F, RT> &w) {
+  const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
+#pragma unroll
+  for (int r = 0; r < kDtbR; ++r) {
+    const uint8_t *dt = a.down_p + (int64_t)e * a.stride_d + (int64_t)(rt + r) * tbytes;
+#pragma unroll
+    for (int s = 0; s < F; ++s) w.d[r][s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
+    w.dw[r] = w.sh[r] = 0;
+    if constexpr (RT > 0) load_tail<RT>(dt, F, lane, w.dw[r], w.sh[r]);
+    w.sd[r] = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + (rt + r) * 16 + 4 * (lane >> 4));
+  }
+}
+
+// One operand slice: the hi parts of the 4 token tiles into every row tile's
+// accumulator, then the lo parts (so no two consecutive products share an
+// accumulator).
+template <int NW>
+__device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, const char *const bq[4], int plane,
+                                          int off, int ntt, f32x4 (*acc)[4]) {
+  u32x4 b[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (t < ntt) {
+      b[0][t] = lds16(bq[t] + off);
+      b[1][t] = lds16(bq[t] + plane + off);
+    }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < ntt) {
+#pragma unroll
+        for (int r = 0; r < kDtbR; ++r) acc[r][t] = mfma_f16(pw[r] + w0, b[q][t], acc[r][t]);
+      }
+}
+
+template <int F, int RT>
+__global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
+  extern __shared__ __align__(16) char smem[];  // [2][64][rs]: the hi and lo planes
+  __shared__ int sig[64];
+  const int blk = blockIdx.x;
+  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
+  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
+  const int e = td.x, start = td.y, nb = td.z;
+  const int ntt = (nb + 15) / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  constexpr int M = 5 * F + tail_mfmas(RT);
+  const int rs = lds_row_bytes(a.slots);
+  const int plane = 64 * rs;
+  const int per_wave = a.H / 16 / kDtbGroups / kDtbWaves;  // row tiles of this wavefront
+  const int rt0 = blockIdx.y * (a.H / 16 / kDtbGroups) + wave * per_wave;
+
+  DtbWeights<F, RT> cur, nxt;
+  dtb_load<F, RT>(a, e, rt0, lane, cur);
+  stage_h_parts<kDtbWaves, 8, M, 4>(a.hf + (int64_t)start * a.I, nb, a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig);
+  __syncthreads();
+
+  const char *bq[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bq[t] = smem + min(16 * t + n, nb - 1) * rs + g * M * 16;
+#pragma unroll 1
+  for (int it = 0; it < per_wave; it += kDtbR) {
+    if (it + kDtbR < per_wave) dtb_load<F, RT>(a, e, rt0 + it + kDtbR, lane, nxt);
+    f32x4 acc[kDtbR][4];
+#pragma unroll
+    for (int r = 0; r < kDtbR; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < F; ++s) {
+      uint32_t pw[kDtbR][20];
+#pragma unroll
+      for (int r = 0; r < kDtbR; ++r) unpack8(cur.d[r][s], pw[r]);
+#pragma unroll
+      for (int m = 0; m < 5; ++m) dtb_slice(pw, 4 * m, bq, plane, (5 * s + m) * 16, ntt, acc);
+    }
+    if constexpr (RT > 0) {
+      uint32_t pw[kDtbR][16];
+#pragma unroll
+      for (int r = 0; r < kDtbR; ++r) unpack_tail<RT>(cur.dw[r], cur.sh[r], pw[r]);
+#pragma unroll
+      for (int m = 0; m < tail_mfmas(RT); ++m) dtb_slice(pw, 4 * m, bq, plane, (5 * F + m) * 16, ntt, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int col = 16 * t + n;
+      if (t >= ntt || col >= nb) continue;
+      const int us = -1 - sig[col];  // the trits entered as 2t, h as 2^sig h
+      float *op = a.O + (int64_t)(start + col) * a.H;
+#pragma unroll
+      for (int r = 0; r < kDtbR; ++r) {
+        const int row0 = (rt0 + it + r) * 16 + 4 * g;
+        float4 o;
+        o.x = ldexpf(acc[r][t][0], us) * cur.sd[r].x;
+        o.y = ldexpf(acc[r][t][1], us) * cur.sd[r].y;
+        o.z = ldexpf(acc[r][t][2], us) * cur.sd[r].z;
+        o.w = ldexpf(acc[r][t][3], us) * cur.sd[r].w;
+        *reinterpret_cast<float4 *>(op + row0) = o;
+      }
+    }
+    cur = nxt;
   }
 }
 
@@ -1632,6 +1762,30 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     rc = run_gateup<13, 0, 1, 0, 1, 8>(st, ga, max_tiles, (int)I, P < 4 * E);
   if (rc) return rc;
 
+  if (P >= 32 * E && H == (int64_t)16 * kDtbGroups * kDtbWaves * (H / (16 * kDtbGroups * kDtbWaves)) &&
+      (H / 16 / kDtbGroups / kDtbWaves) % kDtbR == 0) {
+    // token-blocked down over the same 64-pair blocks
+    DownArgs da;
+    da.down_p = W->down_p;
+    da.stride_d = W->stride_d;
+    da.down_s = W->down_s;
+    da.hf = fw.hf;
+    da.tiles = fw.blocks;
+    da.ntiles = fw.nblocks;
+    da.O = O;
+    da.H = (int)H;
+    da.I = (int)I;
+    da.slots = gi.slots;
+    da.gd = gi;
+    da.stream_w = 0;
+    const size_t lds = (size_t)2 * 64 * lds_row_bytes(gi.slots);
+    rc = allow_lds<down_tb_kernel<3, 2>>(lds);
+    if (rc) return rc;
+    TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_tb_kernel<3, 2>), dim3((unsigned)ffn_max_blocks(P, E), (unsigned)kDtbGroups),
+                dim3(64 * kDtbWaves), lds, st, da);
+    TMOE_LAUNCHED("down_tb");
+    return TMOE_OK;
+  }
   return run_down(st, W, fw, P, max_tiles, O);
 }
 

@@ -238,7 +238,7 @@ int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t
 // -------------------------------------------------------------------- router
 size_t tmoe_router_workspace_bytes(int64_t T, int64_t E) {
   if (T < 0 || E <= 0) return 0;
-  return router_ws_bytes(T, E);
+  return router_ws_bytes(T, E, kRouterMaxH);
 }
 
 static int check_router(const uint16_t *X, int64_t T, int64_t H, const float *Wr, int64_t E, int k, int32_t *idx,
@@ -261,10 +261,10 @@ int tmoe_router_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, cons
   int rc = check_router(X, T, H, Wr, E, k, idx, w);
   if (rc) return rc;
   if (T == 0) return TMOE_OK;
-  size_t need = router_ws_bytes(T, E);
+  size_t need = router_ws_bytes(T, E, kRouterMaxH);
   REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes", need);
   return launch_router((hipStream_t)stream, X, T, H, Wr, bias, E, k, idx, w, logits, n_fixup,
-                       router_ws_carve(ws, T, E));
+                       router_ws_carve(ws, T, E, kRouterMaxH));
 }
 
 // ------------------------------------------------------------ attention half
@@ -455,7 +455,7 @@ static LayerWs layer_ws(int64_t T, const tmoe_moe_weights *W) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.router = router_ws_bytes(T, E);
+  L.router = router_ws_bytes(T, E, H);
   L.group = group_ws_bytes(T, (int)k, E);
   L.ffn = ffn_ws_bytes(T, (int)k, E, H, W->inter);
   L.off_router = take(L.router);
@@ -532,7 +532,7 @@ int moe_forward_impl(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   int32_t *st_tok = (int32_t *)(base + L.off_st);
   int32_t *st_slot = (int32_t *)(base + L.off_ss);
   float *O = (float *)(base + L.off_O);
-  const RouterWs rw = router_ws_carve(base + L.off_router, T, E);
+  const RouterWs rw = router_ws_carve(base + L.off_router, T, E, H);
   const FfnWs fw = ffn_ws_carve(base + L.off_ffn, T, k, E, H, W->inter);
   if (T <= kDecodePathMaxT) {
     // logits; gate/up with the certified top-k and grouping in its prologue; down + combine

@@ -24,6 +24,29 @@ __device__ inline double wave_sum_d(double v) {
   return v;
 }
 
+// Sum over the 64 lanes with DPP steps (lane pairs xor 1 and xor 2, half-row
+// and row mirrors, then row broadcasts 15 and 31), read from lane 63 and
+// returned to every lane: a fixed tree of depth 6.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_step(double v) {
+  const uint64_t b = dbits(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+  return v + bitsd(((uint64_t)hi << 32) | lo);
+}
+__device__ inline double wave_sum_dpp(double v) {
+  v = dpp_add_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  const uint64_t b = dbits(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return bitsd(((uint64_t)hi << 32) | lo);
+}
+
 __device__ inline double gamma_d(int d) {
   const double u = 0x1p-53;
   return d * u / (1.0 - d * u);

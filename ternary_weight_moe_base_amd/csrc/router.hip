@@ -19,22 +19,47 @@
 namespace tmoe {
 
 static constexpr int kTokChunkBytes = 65536;  // LDS bytes of bf16 activations per workgroup
-static constexpr int kVectorRouterMaxT = 64;  // up to 64 tokens the VALU kernel beats the fp64 matrix cores
+static constexpr int kVectorRouterMaxT = 64;  // up to 64 tokens the VALU kernel beats the matrix cores
+// From this many tokens on, a call that does not return the logits picks
+// candidates on the bf16 matrix cores (below it the fp64 matrix-core logits
+// are faster)
+static constexpr int kBf16RouterMinT = 1024;
+static constexpr int kRgMaxSK = 4;  // input slices of the logits GEMM
 
-size_t router_ws_bytes(int64_t T, int64_t E) {
+size_t router_ws_bytes(int64_t T, int64_t E, int64_t H) {
   size_t o = 0;
   o = align_up(o + T * cdiv(E, 4) * 8, 256);  // bnd
   o = align_up(o + T * E * 8, 256);  // lg
+  if (T >= kBf16RouterMinT) {
+    o = align_up(o + (size_t)2 * E * H * 2, 256);  // bf16 parts w1, w2 of the router rows
+    o = align_up(o + (size_t)2 * cdiv(E, 4) * 8, 256);       // norm / bias maxima per split workgroup
+    o = align_up(o + (size_t)E * 8, 256);                    // row norms
+    o = align_up(o + (size_t)kRgMaxSK * T * E * 4, 256);     // fp32 slice sums of the candidate logits
+  }
   return o;
 }
 
-RouterWs router_ws_carve(void *ws, int64_t T, int64_t E) {
+RouterWs router_ws_carve(void *ws, int64_t T, int64_t E, int64_t H) {
   char *b = (char *)ws;
   RouterWs r;
   size_t o = 0;
   r.bnd = (uint64_t *)(b + o);
   o = align_up(o + T * cdiv(E, 4) * 8, 256);
   r.lg = (double *)(b + o);
+  o = align_up(o + T * E * 8, 256);
+  r.parts = nullptr;
+  r.wmax = nullptr;
+  r.wnorm = nullptr;
+  r.part = nullptr;
+  if (T >= kBf16RouterMinT) {
+    r.parts = (uint16_t *)(b + o);
+    o = align_up(o + (size_t)2 * E * H * 2, 256);
+    r.wmax = (uint64_t *)(b + o);
+    o = align_up(o + (size_t)2 * cdiv(E, 4) * 8, 256);
+    r.wnorm = (double *)(b + o);
+    o = align_up(o + (size_t)E * 8, 256);
+    r.part = (float *)(b + o);
+  }
   return r;
 }
 
@@ -221,6 +246,389 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// ------------------------------------------------- bf16 matrix-core logits
+// With many tokens the logits are first formed on the bf16 matrix cores, only
+// to pick each token's candidates; the candidates are then recomputed in fp64
+// by the top-k kernel, whose ranking and softmax use only those values. Each
+// fp32 router weight is split into bf16 parts w = w1 + w2 + w3 (each rounding
+// keeps the next 8 of its 24 significant bits; |w3| <= 2^-16 |w|); the
+// candidate logits use w1 + w2 (a bf16 activation times a bf16 part is exact
+// in fp32), and the bound counts the w3 left out.
+//
+// Split pass: wavefront w of workgroup b takes router row e = 4b + w: its
+// parts w1, w2 go to parts[q][e][*], its norm |w_e|_2 (fp64 sum of exact
+// squares) to wnorm[e], and the workgroup's largest row norm and largest
+// |b_e| to slots wmax[b], wmax[nslots + b] (fp64 bits). Also clears the
+// fix-up counter.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *Wr, const float *bias, int E, int H,
+                                                           uint16_t *parts, uint64_t *wmax, int nslots,
+                                                           double *wnorm, int32_t *n_fixup) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 4 + wave;
+  __shared__ double nw[4], nb[4];
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n_fixup) *n_fixup = 0;
+  double s2 = 0.0;
+  if (e < E) {
+    const size_t plane = (size_t)E * H;
+    for (int i = lane * 4; i < H; i += 256) {
+      const float4 v = *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + i);
+      const float f[4] = {v.x, v.y, v.z, v.w};
+      uint32_t pw[2][2] = {};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h = f32_to_bf16_rne(f[j]);
+        const uint32_t m = f32_to_bf16_rne(f[j] - bf16f((uint16_t)h));
+        const int sh = 16 * (j & 1);
+        pw[0][j >> 1] |= h << sh;
+        pw[1][j >> 1] |= m << sh;
+        s2 = fma((double)f[j], (double)f[j], s2);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<uint2 *>(parts + q * plane + (size_t)e * H + i) = make_uint2(pw[q][0], pw[q][1]);
+    }
+  }
+  s2 = wave_sum_dpp(s2);
+  if (lane == 0) {
+    nw[wave] = sqrt(s2);
+    if (e < E) wnorm[e] = nw[wave];
+    nb[wave] = (e < E && bias) ? fabs((double)bias[e]) : 0.0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    wmax[blockIdx.x] = dbits(fmax(fmax(nw[0], nw[1]), fmax(nw[2], nw[3])));
+    wmax[nslots + blockIdx.x] = dbits(fmax(fmax(nb[0], nb[1]), fmax(nb[2], nb[3])));
+  }
+}
+
+// Logits pass, a bf16 GEMM: workgroup = 4 wavefronts over a tile of 128
+// router rows x 128 tokens and one of SK slices of the inputs; wavefront
+// (we, wt) takes rows e0 + 64 we .. + 63 (4 row tiles of 16) and tokens
+// t0 + 64 wt .. + 63 (4 token tiles). Each K step of 32 inputs is staged in
+// LDS (parts w1, w2 of the 128 rows and the 128 token rows, 80-byte rows so
+// that 16 lanes reading 16 bytes of 16 rows hit distinct banks), the next
+// step's loads in flight while the current one is multiplied; per step a
+// wavefront runs 4 x 4 tiles x 2 parts products, w1 and w2 of a tile into one
+// fp32 accumulator. part[sk][t][e] = the slice's sum (fp32). Rows past E and
+// tokens past T read a valid row and are not stored.
+constexpr int kRgRow = 80;  // LDS bytes per staged row of 32 inputs
+template <int SK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void router_gemm_kernel(const uint16_t *X, int64_t T, const uint16_t *parts, int E,
+                                                          int H, int neb, float *part) {
+  extern __shared__ __align__(16) char lds[];  // [2][(256 + 128) rows][80 B]
+  constexpr int STAGE = 384 * kRgRow;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int we = wave & 1, wt = wave >> 1;
+  const int sk = blockIdx.x % SK, tile = blockIdx.x / SK;
+  const int eb = tile % neb, tb = tile / neb;
+  const int e0 = eb * 128;
+  const int64_t t0 = (int64_t)tb * 128;
+  const int nstep = H / 32 / SK;
+  const int kbase = sk * nstep * 32;
+  const size_t plane = (size_t)E * H;
+  // staging: thread handles P chunks i = tid + 256 u (u < 4) and X chunks i = tid + 256 u (u < 2)
+  const uint16_t *gp[4];
+  const uint16_t *gx[2];
+  int lp[4], lx[2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + 256 * u, row = i >> 2, c = i & 3;
+    const int q = row >> 7, e = min(e0 + (row & 127), E - 1);
+    gp[u] = parts + q * plane + (size_t)e * H + kbase + 8 * c;
+    lp[u] = row * kRgRow + c * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = threadIdx.x + 256 * u, row = i >> 2, c = i & 3;
+    gx[u] = X + min<int64_t>(t0 + row, T - 1) * H + kbase + 8 * c;
+    lx[u] = (256 + row) * kRgRow + c * 16;
+  }
+  uint4 rp0, rp1, rp2, rp3, rx0, rx1;
+#define RG_GLOAD(S)                                                \
+  do {                                                             \
+    rp0 = *reinterpret_cast<const uint4 *>(gp[0] + 32 * (S));      \
+    rp1 = *reinterpret_cast<const uint4 *>(gp[1] + 32 * (S));      \
+    rp2 = *reinterpret_cast<const uint4 *>(gp[2] + 32 * (S));      \
+    rp3 = *reinterpret_cast<const uint4 *>(gp[3] + 32 * (S));      \
+    rx0 = *reinterpret_cast<const uint4 *>(gx[0] + 32 * (S));      \
+    rx1 = *reinterpret_cast<const uint4 *>(gx[1] + 32 * (S));      \
+  } while (0)
+#define RG_LSTORE(BUF)                                             \
+  do {                                                             \
+    char *b_ = lds + (BUF) * STAGE;                                \
+    *reinterpret_cast<uint4 *>(b_ + lp[0]) = rp0;                  \
+    *reinterpret_cast<uint4 *>(b_ + lp[1]) = rp1;                  \
+    *reinterpret_cast<uint4 *>(b_ + lp[2]) = rp2;                  \
+    *reinterpret_cast<uint4 *>(b_ + lp[3]) = rp3;                  \
+    *reinterpret_cast<uint4 *>(b_ + lx[0]) = rx0;                  \
+    *reinterpret_cast<uint4 *>(b_ + lx[1]) = rx1;                  \
+  } while (0)
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, kq = lane >> 4;
+  RG_GLOAD(0);
+  RG_LSTORE(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int s = 0; s < nstep; ++s) {
+    if (s + 1 < nstep) RG_GLOAD(s + 1);
+    const char *b = lds + (s & 1) * STAGE;
+    u32x4 av[4][2], bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) av[i][q] = lds16(b + (q * 128 + we * 64 + 16 * i + r16) * kRgRow + kq * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = lds16(b + (256 + wt * 64 + 16 * j + r16) * kRgRow + kq * 16);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i][q]),
+                                                              __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
+    if (s + 1 < nstep) RG_LSTORE((s + 1) & 1);
+    __syncthreads();
+  }
+#undef RG_GLOAD
+#undef RG_LSTORE
+  // lane: token t0 + 64 wt + 16 j + r16, rows e0 + 64 we + 16 i + 4 kq .. + 3
+  float *out = part + (size_t)sk * T * E;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + wt * 64 + 16 * j + r16;
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + we * 64 + 16 * i + 4 * kq;
+      if (e + 3 < E && (E & 3) == 0) {
+        *reinterpret_cast<float4 *>(out + t * E + e) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (e + v < E) out[t * E + e + v] = acc[i][j][v];
+      }
+    }
+  }
+}
+
+// Certified top-k from the matrix-core logits l~ (error <= B1 for every
+// expert), one wavefront per token:
+//  1. the (k+1)-th largest of 32-bit keys (l~ rounded to fp32, order-
+//     preserving, low IB bits replaced by the expert index) gives a bucket
+//     whose lowest value f_low is at most the (k+1)-th largest l~ up to the
+//     fp32 rounding; every expert with l~ >= thr = f_low - 2^-22 |f_low| - 2 B1
+//     is a candidate (the true top k+1 are among them: any other has a true
+//     logit below c - B1, under all k+1 of those with l~ >= c, the (k+1)-th
+//     largest l~). The list goes to LDS in ascending expert order.
+//  2. each candidate is recomputed in fp64 (exact products, an FMA chain of
+//     4 NC per lane, a DPP butterfly of depth 6), kRfBatch at a time with all
+//     their loads in flight; lane i keeps candidate i.
+//  3. each candidate's rank is counted (larger value first, equal values to
+//     the lower expert); the top k+1 adjacent gaps are certified against
+//     2 B2, B2 = 1.01 gamma_d max over the candidates of |x|_2 |w_e|_2 +
+//     |b_e|, and idx and the softmax over the k (fp64 values) are written.
+// A token with more than 64 candidates, or not certified, is recomputed in
+// double-double (counted in *n_fixup).
+constexpr int kRfBatch = 3;
+
+template <int NPL, int NC>
+__global__ __launch_bounds__(256) void router_topk_refine_kernel(int64_t T, const uint16_t *X, const float *Wr,
+                                                                 const float *bias, const float *part, int SK,
+                                                                 const uint64_t *wmax, int nslots,
+                                                                 const double *wnorm, int E, int k, double gfac,
+                                                                 double babs, int32_t *idx, float *wout,
+                                                                 int32_t *n_fixup) {
+  constexpr int H = NC * 256;
+  constexpr int IB = NPL * 64 <= 256 ? 8 : 10;  // index bits of a key
+  __shared__ int32_t cand[4][64];
+  __shared__ double rank_v[4][17];
+  __shared__ int32_t rank_e[4][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const uint16_t *x = X + t * H;
+  uint2 xp[NC];
+  double s2 = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    xp[c] = reinterpret_cast<const uint2 *>(x)[c * 64 + lane];
+    const double q[4] = {__uint_as_float(xp[c].x << 16), __uint_as_float(xp[c].x & 0xFFFF0000u),
+                         __uint_as_float(xp[c].y << 16), __uint_as_float(xp[c].y & 0xFFFF0000u)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s2 = fma(q[i], q[i], s2);
+  }
+  const double nx = 1.01 * sqrt(wave_sum_dpp(s2));  // |x_t|_2 with a 1% margin
+  uint64_t wm = 0, bm = 0;
+  for (int j = lane; j < nslots; j += 64) {
+    wm = wm > wmax[j] ? wm : wmax[j];
+    bm = bm > wmax[nslots + j] ? bm : wmax[nslots + j];
+  }
+  const double B1 = gfac * (nx * __longlong_as_double((long long)wave_max_u64(wm)) +
+                            __longlong_as_double((long long)wave_max_u64(bm))) + babs;
+
+  // ---- 1. candidates
+  double v[NPL];
+  uint32_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) v[j] = 0.0;
+  for (int q = 0; q < SK; ++q) {
+    const float *pr = part + ((size_t)q * T + t) * E;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane * NPL + j;
+      if (e < E) v[j] += (double)pr[e];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane * NPL + j;
+    if (e < E && bias) v[j] += (double)bias[e];
+    uint32_t u = __float_as_uint((float)v[j]);
+    if (u == 0x80000000u) u = 0u;
+    const uint32_t o = (u >> 31) ? ~u : (u | 0x80000000u);
+    key[j] = e < E ? (((o >> IB) << IB) | (uint32_t)(E - 1 - e)) : 0u;
+  }
+#pragma unroll
+  for (int pass = 0; pass < NPL; ++pass)
+#pragma unroll
+    for (int j = pass & 1; j + 1 < NPL; j += 2)
+      if (key[j] < key[j + 1]) {
+        const uint32_t tk = key[j];
+        key[j] = key[j + 1];
+        key[j + 1] = tk;
+      }
+  const int m = min(k + 1, E);
+  uint32_t mx = 0u;
+  for (int r = 0; r < m; ++r) {
+    mx = wave_max_u32(key[0]);
+    if (key[0] == mx) {
+#pragma unroll
+      for (int j = 0; j + 1 < NPL; ++j) key[j] = key[j + 1];
+      key[NPL - 1] = 0u;
+    }
+  }
+  const uint32_t ob = (mx >> IB) << IB;  // the (k+1)-th key's bucket, lowest value
+  const float flow = __uint_as_float((ob >> 31) ? (ob & 0x7FFFFFFFu) : ~ob);
+  const double thr = (double)flow - 0x1p-22 * fabs((double)flow) - 2.0 * B1;
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) mine += (lane * NPL + j < E && v[j] >= thr) ? 1 : 0;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const int nc = __builtin_amdgcn_readlane(incl, 63);
+  bool ok = nc <= 64 && nc >= m;
+  if (ok) {
+    int at = incl - mine;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (lane * NPL + j < E && v[j] >= thr) cand[wave][at++] = lane * NPL + j;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- 2. fp64 values of the candidates
+    double myv = 0.0, myb = 0.0;
+    int mye = 0;
+    for (int i0 = 0; i0 < nc; i0 += kRfBatch) {
+      int eb[kRfBatch];
+      float4 q[kRfBatch][NC];
+#pragma unroll
+      for (int u = 0; u < kRfBatch; ++u) {
+        eb[u] = cand[wave][min(i0 + u, nc - 1)];
+        const float4 *wr = reinterpret_cast<const float4 *>(Wr + (size_t)eb[u] * H);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) q[u][c] = wr[c * 64 + lane];
+      }
+      double acc[kRfBatch];
+#pragma unroll
+      for (int u = 0; u < kRfBatch; ++u) acc[u] = 0.0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const double x0 = __uint_as_float(xp[c].x << 16), x1 = __uint_as_float(xp[c].x & 0xFFFF0000u);
+        const double x2 = __uint_as_float(xp[c].y << 16), x3 = __uint_as_float(xp[c].y & 0xFFFF0000u);
+#pragma unroll
+        for (int u = 0; u < kRfBatch; ++u) {
+          acc[u] = fma((double)q[u][c].x, x0, acc[u]);
+          acc[u] = fma((double)q[u][c].y, x1, acc[u]);
+          acc[u] = fma((double)q[u][c].z, x2, acc[u]);
+          acc[u] = fma((double)q[u][c].w, x3, acc[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kRfBatch; ++u) {
+        const double sum = wave_sum_dpp(acc[u]);
+        if (lane == i0 + u) {
+          const double b = bias ? (double)bias[eb[u]] : 0.0;
+          myv = sum + b;
+          myb = nx * wnorm[eb[u]] + fabs(b);
+          mye = eb[u];
+        }
+      }
+    }
+    // B2 over the candidates; chain 4 NC, butterfly 6, bias 1, margin 2
+    const double B2 = 1.01 * gamma_d(4 * NC + 9) * __longlong_as_double((long long)wave_max_u64(dbits(myb)));
+
+    // ---- 3. ranks (lane i < nc: larger values first, equal values to the lower expert = lower lane)
+    int rank = 0;
+    for (int j = 0; j < nc; ++j) {
+      const double vj = readlane_d(myv, j);
+      rank += (vj > myv || (vj == myv && j < lane)) ? 1 : 0;
+    }
+    if (lane < nc && rank <= k) {
+      rank_v[wave][rank] = myv;
+      rank_e[wave][rank] = mye;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    const int m2 = min(k + 1, nc);
+    const double rv = lane < m2 ? rank_v[wave][lane] : 0.0;
+    const double nv = lane + 1 < m2 ? rank_v[wave][lane + 1] : 0.0;
+    ok = __ballot(lane + 1 < m2 && !(rv - nv > 2.0 * B2)) == 0ull;
+    if (ok) {
+      const double v0 = readlane_d(rv, 0);
+      const double p = lane < k ? exp(rv - v0) : 0.0;
+      double den = 0.0;
+      for (int r = 0; r < k; ++r) den += readlane_d(p, r);
+      if (lane < k) {
+        idx[t * k + lane] = rank_e[wave][lane];
+        wout[t * k + lane] = (float)(p / den);
+      }
+    }
+  }
+  if (!ok) {
+    if (lane == 0 && n_fixup) atomicAdd(n_fixup, 1);
+    topk_dd<NPL>(x, H, Wr, bias, E, k, idx + t * k, wout + t * k, nullptr);
+  }
+}
+
+// Bound factor of the matrix-core logits (unit roundoff 2^-24 for fp32, 2^-53
+// for fp64; Higham's gamma_n = n u / (1 - n u), which bounds a sum of n + 1
+// terms in any order): |l~ - l| <= gfac (|x|_2 max_e |w_e|_2 + max_e |b_e|) +
+// babs, with sum_i |x_i w_i| <= |x|_2 |w|_2 (Cauchy-Schwarz). Terms: each of
+// the SK slice sums adds 2 x 32 exact products per K step to one fp32 sum
+// (at most 66 roundings a step on any path; |w1| + |w2| <= (1 + 2^-7)|w|);
+// the w3 left out (|w3| <= 2^-16 |w|); the fp64 sum of the slices and the
+// bias; 1% margin for the norms' own rounding. babs covers subnormal parts
+// and products the matrix cores may flush.
+static void router_bf16_bound(int H, int SK, double *gfac, double *babs) {
+  auto g32 = [](double n) { const double u = 0x1p-24; return n * u / (1.0 - n * u); };
+  auto g64 = [](double n) { const double u = 0x1p-53; return n * u / (1.0 - n * u); };
+  const double steps = H / 32.0 / SK;
+  const double t1 = g32(66.0 * steps) * (1.0 + 0x1p-7);
+  const double t2 = 0x1p-16;
+  const double t3 = g64(SK + 2.0) * (1.0 + 0x1p-7);
+  *gfac = 1.01 * (t1 + t2 + t3);
+  *babs = (double)H * 0x1p-120;
+}
+
 // One wavefront per token: certified top-k from the fp64 logits, else the
 // double-double recompute (counted in *n_fixup).
 template <int NPL>
@@ -264,9 +672,40 @@ static int launch_logits_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
 
 template <int NC, int NPL>
 static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const float *Wr, const float *bias,
-                            int64_t E, int k, int32_t *idx, float *w, int32_t *n_fixup, const RouterWs &rw) {
+                            int64_t E, int k, int32_t *idx, float *w, int32_t *n_fixup, const RouterWs &rw,
+                            bool want_logits) {
   constexpr int H = NC * 256;
   int depth, nb;
+  if (T >= kBf16RouterMinT && !want_logits) {
+    // candidates from the bf16 matrix cores, ranked on fp64 recomputed values
+    const int nslots = (int)cdiv(E, 4);
+    TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_split_kernel, dim3((unsigned)nslots), dim3(256), 0, st, Wr, bias,
+                (int)E, H, rw.parts, rw.wmax, nslots, rw.wnorm, n_fixup);
+    TMOE_LAUNCHED("router_split");
+    const int64_t ntile = cdiv(T, 128) * cdiv(E, 128);
+    if (ntile * kRgMaxSK > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
+    // input slices so that about 256 workgroups run (at least 4 K steps each)
+    int SK = 1;
+    while (SK < kRgMaxSK && ntile * SK < 256 && H / 32 / (2 * SK) >= 4) SK *= 2;
+    const size_t lds = (size_t)2 * 384 * kRgRow;
+    const dim3 grid((unsigned)(ntile * SK));
+    float *part = rw.part;
+    switch (SK) {
+      case 1: TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_gemm_kernel<1>, grid, dim3(256), lds, st, X, T, rw.parts,
+                          (int)E, H, (int)cdiv(E, 128), part); break;
+      case 2: TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_gemm_kernel<2>, grid, dim3(256), lds, st, X, T, rw.parts,
+                          (int)E, H, (int)cdiv(E, 128), part); break;
+      default: TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_gemm_kernel<4>, grid, dim3(256), lds, st, X, T, rw.parts,
+                           (int)E, H, (int)cdiv(E, 128), part); break;
+    }
+    TMOE_LAUNCHED("router_gemm");
+    double gfac, babs;
+    router_bf16_bound(H, SK, &gfac, &babs);
+    TMOE_LAUNCH(TMOE_KERNEL_ROUTER_TOPK, (router_topk_refine_kernel<NPL, NC>), dim3((unsigned)cdiv(T, 4)), dim3(256), 0,
+                st, T, X, Wr, bias, part, SK, rw.wmax, nslots, rw.wnorm, (int)E, k, gfac, babs, idx, w, n_fixup);
+    TMOE_LAUNCHED("router_topk_refine");
+    return TMOE_OK;
+  }
   if (T <= kVectorRouterMaxT) {
     int rc = launch_logits_nc<NC>(st, X, T, Wr, bias, E, rw, n_fixup, &depth, &nb);
     if (rc) return rc;
@@ -313,7 +752,10 @@ int launch_router_logits(hipStream_t st, const uint16_t *X, int64_t T, int64_t H
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,
                   int64_t E, int k, int32_t *idx, float *w, float *logits_out, int32_t *n_fixup, const RouterWs &rw) {
   if (T > 0x7FFFFFFF / 4) return fail(TMOE_E_UNSUPPORTED, "T too large");
-  int rc = [&]() -> int { TMOE_ROUTER_DISPATCH(launch_router_nc, st, X, T, Wr, bias, E, k, idx, w, n_fixup, rw); }();
+  const bool want = logits_out != nullptr;
+  int rc = [&]() -> int {
+    TMOE_ROUTER_DISPATCH(launch_router_nc, st, X, T, Wr, bias, E, k, idx, w, n_fixup, rw, want);
+  }();
   if (rc || !logits_out) return rc;
   hipLaunchKernelGGL(copy_d2f_kernel, dim3((unsigned)cdiv(T * E, 256)), dim3(256), 0, st, rw.lg, T * E, logits_out);
   TMOE_LAUNCHED("logits_copy");
