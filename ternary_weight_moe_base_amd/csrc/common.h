@@ -204,6 +204,7 @@ struct FfnWs {
   float *pw;         // [T*k] routing weight of each grouped pair (decode path)
   int32_t *blocks;   // [max_blocks][4]: expert, start, count (<= 64), 0 (token-blocked gate/up)
   int32_t *nblocks;  // [1]
+  uint32_t *hmax;    // [T*k][4] largest |h| (fp32 bits) of each pair per gate/up row group (token-blocked path)
 };
 int64_t ffn_max_tiles(int64_t pairs, int64_t E);
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I);

@@ -187,6 +187,7 @@ struct GateUpArgs {
   const int32_t *tiles, *ntiles, *sorted_token;
   float *h;            // [pairs][I] fp32 (grouped order) or null: a copy of h for the caller
   float *hf;           // [pairs][I] fp32 h in grouped order (the down projection's input)
+  uint32_t *hmax;      // [pairs][kTbMaxGroups] largest |h| (fp32 bits) per row group (token-blocked path)
   Geom gx, gd;         // operand geometry of gate/up (K = H) and of down (K = I)
   int I;
   float clamp;
@@ -196,22 +197,29 @@ struct GateUpArgs {
   int T, E, k;
 };
 
-__device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
-                                const float4 &sg, const float4 &su) {
+__device__ inline uint32_t store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
+                                    const float4 &sg, const float4 &su, bool store = true) {
   const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
   const float c = a.clamp;
   float hv[4];
+  uint32_t mx = 0u;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float gg = (gs[v] * 0.5f) * sgv[v];
     const float uu = (us[v] * 0.5f) * suv[v];
     const float z = fminf(gg, c);
     hv[v] = __fdividef(z, 1.f + __expf(-z)) * fminf(fmaxf(uu, -c), c);
+    mx = max(mx, __float_as_uint(hv[v]) & 0x7FFFFFFFu);
   }
-  const float4 h4 = make_float4(hv[0], hv[1], hv[2], hv[3]);
-  *reinterpret_cast<float4 *>(a.hf + p * a.I + row0) = h4;
-  if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = h4;
+  if (store) {
+    const float4 h4 = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<float4 *>(a.hf + p * a.I + row0) = h4;
+    if (a.h) *reinterpret_cast<float4 *>(a.h + p * a.I + row0) = h4;
+  }
+  return mx;
 }
+
+constexpr int kTbMaxGroupsH = 4;  // row groups per pair in the gate/up's hmax (kTbMaxGroups)
 
 // ------------------------------------------------ down operand staging
 // The h rows of `cnt` grouped pairs (fp32, row n at h + n * I) become the down
@@ -286,6 +294,59 @@ __device__ inline void stage_h_parts(const float *h, int cnt, int I, int q5, cha
       }
       if (lane == 0) sig[n] = sg;
     }
+  }
+}
+
+// The same operand staging when each row's largest |h| is already known (the
+// token-blocked gate/up writes it per row group, hmax[row][q] for q <
+// ngroups): every thread takes whole 16-byte chunks of any rows, all of its
+// loads in flight at once, with no reduction across lanes.
+template <int NT, int M>
+__device__ inline void stage_h_known(const float *h, const uint32_t *hmax, int ngroups, int cnt, int I, int q5,
+                                     char *pl0, char *pl1, int rs, int *sig) {
+  constexpr int NCH = 4 * M;                    // 16-byte chunks per staged row
+  constexpr int PER = (64 * NCH + NT - 1) / NT;  // chunks per thread (at most 64 rows)
+  for (int r = threadIdx.x; r < cnt; r += NT) {
+    uint32_t mx = 0u;
+    for (int q = 0; q < ngroups; ++q) mx = max(mx, hmax[(int64_t)r * kTbMaxGroupsH + q]);
+    int sg = 0;
+    if (mx != 0 && mx < 0x7F800000u) {
+      int ex;
+      (void)frexpf(__uint_as_float(mx), &ex);
+      sg = 15 - ex;
+    }
+    sig[r] = sg;
+  }
+  float v[PER][8];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = threadIdx.x + NT * u, row = i / NCH, c = i - row * NCH;
+    const int quarter = c / M, j0 = 8 * (c - quarter * M), k0 = q5 * quarter + j0;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float2 f = make_float2(0.f, 0.f);
+      if (row < cnt && j0 + e < q5 && k0 + e < I) f = *reinterpret_cast<const float2 *>(h + (int64_t)row * I + k0 + e);
+      v[u][e] = f.x;
+      v[u][e + 1] = f.y;
+    }
+  }
+  __syncthreads();  // sig[] written
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = threadIdx.x + NT * u, row = i / NCH, c = i - row * NCH;
+    if (row >= cnt) continue;
+    const int sg = sig[row];
+    uint32_t w[2][4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float a0 = ldexpf(v[u][e], sg), a1 = ldexpf(v[u][e + 1], sg);
+      const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+      const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1);
+      w[0][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      w[1][e >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    *reinterpret_cast<uint4 *>(pl0 + row * rs + c * 16) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+    *reinterpret_cast<uint4 *>(pl1 + row * rs + c * 16) = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
   }
 }
 
@@ -449,8 +510,8 @@ __device__ __forceinline__ float silu(float z) { return __fdividef(z, 1.f + __ex
 // 2t) and the row scales; stored as fp32 in grouped order (one 16-byte store),
 // and into the caller's copy if requested.
 struct GateUpArgs;
-__device__ inline void store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
-                                const float4 &sg, const float4 &su);
+__device__ inline uint32_t store_h4(const GateUpArgs &a, int64_t p, int row0, const f32x4 &gs, const f32x4 &us,
+                                    const float4 &sg, const float4 &su, bool store);
 
 // Workgroup = 4 wavefronts. KS wavefronts split the K steps of one 16-row tile
 // (partial sums reduced in LDS in fixed order); with KS = 1 each wavefront
@@ -645,7 +706,7 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
   if (n >= cnt) return;
   const int64_t p = start + n;
 #pragma unroll
-  for (int r = 0; r < R; ++r) store_h4(a, p, (rtb + RTB * r) * 16 + 4 * g, accg[r], accu[r], sg[r], su[r]);
+  for (int r = 0; r < R; ++r) store_h4(a, p, (rtb + RTB * r) * 16 + 4 * g, accg[r], accu[r], sg[r], su[r], true);
 }
 
 // Decode (RNPL > 0): the grid is (hit experts, row-tile groups). Otherwise the
@@ -678,59 +739,86 @@ __global__ __launch_bounds__(64 * NW) void gateup_kernel(GateUpArgs a) {
 
 // ------------------------------------------- gate / up, token-blocked
 // Many pairs per expert (prefill): a workgroup takes a block of up to 64 pairs
-// of one expert and 128 rows (eight wavefronts, a row tile each, all K steps
-// of its weights in registers). Each wavefront decodes its weights of a K step
-// once and applies them to all four token tiles, so the trit decoding is
-// amortized over 64 tokens. Activations stream through LDS one K step at a
-// time by direct global-to-LDS loads, kTbDepth steps in flight; a step's
-// buffer is [token tile][slice m][quarter g][column n] x 16 B, so the 16
-// columns of an operand read are consecutive (no bank conflicts). Inputs past
-// K are read from a valid address (their trits are zero).
-constexpr int kTbWaves = 8, kTbDepth = 4, kTbStepBytes = 4 * 5 * 64 * 16;
+// of one expert and 256 intermediate rows (eight wavefronts, two row tiles
+// each). Each wavefront decodes the weights of a K step once for its two row
+// tiles and applies them to all four token tiles, and each activation slice it
+// reads from LDS feeds both row tiles, so a product costs 1/2 of an LDS read
+// and 1/4 of a decode. Activations stream through LDS one K step at a time by
+// direct global-to-LDS loads, kTbDepth steps in flight; a step's buffer is
+// [token tile][slice m][quarter g][column n] x 16 B, so the 16 columns of an
+// operand read are consecutive (no bank conflicts). Inputs past K are read
+// from a valid address (their trits are zero). Weights stream kTbWDepth steps
+// ahead of their use. The epilogue also writes, per pair, the largest |h| of
+// the workgroup's rows (hmax[pair][row group]), which the down projection
+// uses to pick the pair's scale.
+constexpr int kTbWaves = 8, kTbR = 2, kTbDepth = 4, kTbWDepth = 3, kTbStepBytes = 4 * 5 * 64 * 16;
+constexpr int kTbRows = 16 * kTbWaves * kTbR;  // intermediate rows per workgroup
+constexpr int kTbMaxGroups = kTbMaxGroupsH;   // row groups per pair kept in hmax
 
-// Waits until at most `later` steps of this wavefront's loads (nj per step) are in flight.
-__device__ __forceinline__ void wait_steps(int later, int nj) {
-  switch (later * 4 + nj) {
-    case 0 * 4 + 2: case 0 * 4 + 3: TMOE_WAIT_VM(0); break;
-    case 1 * 4 + 2: TMOE_WAIT_VM(2); break;
-    case 1 * 4 + 3: TMOE_WAIT_VM(3); break;
-    case 2 * 4 + 2: TMOE_WAIT_VM(4); break;
-    case 2 * 4 + 3: TMOE_WAIT_VM(6); break;
-    case 3 * 4 + 2: TMOE_WAIT_VM(6); break;
-    default: TMOE_WAIT_VM(9); break;
+// s_waitcnt vmcnt(n) for a value known only after unrolling (0 <= n <= 31)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define TMOE_VM_CASE(k) case k: TMOE_WAIT_VM(k); break;
+    TMOE_VM_CASE(0) TMOE_VM_CASE(1) TMOE_VM_CASE(2) TMOE_VM_CASE(3) TMOE_VM_CASE(4) TMOE_VM_CASE(5)
+    TMOE_VM_CASE(6) TMOE_VM_CASE(7) TMOE_VM_CASE(8) TMOE_VM_CASE(9) TMOE_VM_CASE(10) TMOE_VM_CASE(11)
+    TMOE_VM_CASE(12) TMOE_VM_CASE(13) TMOE_VM_CASE(14) TMOE_VM_CASE(15) TMOE_VM_CASE(16) TMOE_VM_CASE(17)
+    TMOE_VM_CASE(18) TMOE_VM_CASE(19) TMOE_VM_CASE(20) TMOE_VM_CASE(21) TMOE_VM_CASE(22) TMOE_VM_CASE(23)
+    TMOE_VM_CASE(24) TMOE_VM_CASE(25) TMOE_VM_CASE(26) TMOE_VM_CASE(27) TMOE_VM_CASE(28) TMOE_VM_CASE(29)
+    TMOE_VM_CASE(30)
+#undef TMOE_VM_CASE
+    default: TMOE_WAIT_VM(0); break;
   }
+}
+
+// Vector-memory loads issued after step s's activation loads, at the wait of
+// step s. Issue order: prologue W(0..kTbWDepth-1), A(0..kTbDepth-2); then in
+// step i: A(i + kTbDepth - 1), W(i + kTbWDepth) while they exist. A(s) = nj
+// loads, W(s) = 2 kTbR loads.
+__device__ __forceinline__ int tb_after_act(int s, int nj, int F) {
+  constexpr int WL = 2 * kTbR;
+  int n = 0;
+  if (s <= kTbDepth - 2) {
+    n += (kTbDepth - 2 - s) * nj;
+  } else {
+    const int i = s - (kTbDepth - 1);  // the step that issued A(s)
+    if (i + kTbWDepth < F) n += WL;
+  }
+  const int i0 = s <= kTbDepth - 2 ? 0 : s - (kTbDepth - 2);
+  for (int i = i0; i <= s; ++i) {
+    if (i + kTbDepth - 1 < F) n += nj;
+    if (i + kTbWDepth < F) n += WL;
+  }
+  return n;
 }
 
 template <int F>
 __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) {
   extern __shared__ __align__(16) char xs[];  // [kTbDepth][kTbStepBytes]
+  __shared__ uint32_t wmaxs[kTbWaves][64];
   const int blk = blockIdx.x;
   if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
   const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
   const int e = td.x, start = td.y;
   const int nb = td.z;  // pairs of this block (<= 64)
-  const int ntt = (nb + 15) / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int rt = blockIdx.y * kTbWaves + wave;
+  const int rt0 = (blockIdx.y * kTbWaves + wave) * kTbR;  // row tiles rt0 .. rt0 + kTbR - 1
   constexpr int Q5 = 5 * 8 * F;  // inputs per quarter (H = 2048: 520)
   const int K = (int)a.gx.K;
 
-  // weights of all K steps and the row scales
   const int64_t tbytes = 64 * (int64_t)(8 * F);
-  const uint8_t *gt = a.gate_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
-  const uint8_t *ut = a.up_p + (int64_t)e * a.stride_gu + (int64_t)rt * tbytes;
-  uint2 gd[F], ud[F];
-#pragma unroll
-  for (int s = 0; s < F; ++s) {
-    gd[s] = *reinterpret_cast<const uint2 *>(gt + (int64_t)s * 512 + lane * 8);
-    ud[s] = *reinterpret_cast<const uint2 *>(ut + (int64_t)s * 512 + lane * 8);
-  }
-  const int row0 = rt * 16 + 4 * g;
-  const float4 sg = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
-  const float4 su = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
+  const uint8_t *gt = a.gate_p + (int64_t)e * a.stride_gu + (int64_t)rt0 * tbytes + lane * 8;
+  const uint8_t *ut = a.up_p + (int64_t)e * a.stride_gu + (int64_t)rt0 * tbytes + lane * 8;
+  uint2 wg[kTbWDepth][kTbR], wu[kTbWDepth][kTbR];
+#define TB_WLOAD(S)                                                                                          \
+  do {                                                                                                       \
+    _Pragma("unroll") for (int r = 0; r < kTbR; ++r) {                                                       \
+      wg[(S) % kTbWDepth][r] = *reinterpret_cast<const uint2 *>(gt + r * tbytes + (int64_t)(S) * 512);       \
+      wu[(S) % kTbWDepth][r] = *reinterpret_cast<const uint2 *>(ut + r * tbytes + (int64_t)(S) * 512);       \
+    }                                                                                                        \
+  } while (0)
 
-  // this wavefront's load instructions of a step: j = wave, wave + 8, wave + 16 (< 20),
+  // this wavefront's activation load instructions of a step: j = wave, wave + 8, wave + 16 (< 20),
   // j = (token tile, slice m); lane (g, n) fetches 16 B of column n, quarter g
   constexpr int NJ = 3;
   const int nj = wave + 16 < 20 ? 3 : 2;
@@ -744,72 +832,98 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
     srow[q] = a.X + (int64_t)a.sorted_token[start + col] * K;
     kq[q] = Q5 * g + 8 * m;  // input index at step 0
   }
-  auto issue = [&](int s) {
-    char *buf = xs + (s % kTbDepth) * kTbStepBytes;
-#pragma unroll
-    for (int q = 0; q < NJ; ++q) {
-      if (q < nj) {
-        const int j = wave + 8 * q;
-        int k0 = kq[q] + 40 * s;
-        k0 = k0 < K ? k0 : K - 8;
-        __builtin_amdgcn_global_load_lds((const void *)(srow[q] + k0),
-                                         (__attribute__((address_space(3))) void *)(buf + j * 1024), 16, 0, 0);
-      }
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < kTbDepth - 1; ++s) issue(s);
+#define TB_ALOAD(S)                                                                                          \
+  do {                                                                                                       \
+    char *buf_ = xs + ((S) % kTbDepth) * kTbStepBytes;                                                       \
+    _Pragma("unroll") for (int q = 0; q < NJ; ++q) {                                                         \
+      if (q < nj) {                                                                                          \
+        const int j_ = wave + 8 * q;                                                                         \
+        int k0 = kq[q] + 40 * (S);                                                                           \
+        k0 = k0 < K ? k0 : K - 8;                                                                            \
+        __builtin_amdgcn_global_load_lds((const void *)(srow[q] + k0),                                       \
+                                         (__attribute__((address_space(3))) void *)(buf_ + j_ * 1024), 16, 0, 0); \
+      }                                                                                                      \
+    }                                                                                                        \
+  } while (0)
 
-  f32x4 accg[4], accu[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    accg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kTbWDepth; ++s) TB_WLOAD(s);
+#pragma unroll
+  for (int s = 0; s < kTbDepth - 1; ++s) TB_ALOAD(s);
+  float4 sg[kTbR], su[kTbR];
+#pragma unroll
+  for (int r = 0; r < kTbR; ++r) {
+    const int row0 = (rt0 + r) * 16 + 4 * g;
+    sg[r] = *reinterpret_cast<const float4 *>(a.gate_s + (int64_t)e * a.I + row0);
+    su[r] = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
   }
-  // the decode of step s + 1 is interleaved with the products of step s (VALU
-  // beside the matrix cores); the four token tiles run unconditionally
-  // (columns past the block hold a clamped pair and are not stored)
-  uint32_t pg[20], pu[20];
-  unpack8(gd[0], pg);
-  unpack8(ud[0], pu);
+
+  f32x4 accg[kTbR][4], accu[kTbR][4];
+#pragma unroll
+  for (int r = 0; r < kTbR; ++r)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      accg[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accu[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
   for (int s = 0; s < F; ++s) {
-    if (s + kTbDepth - 1 < F) issue(s + kTbDepth - 1);
-    // wait for this wavefront's loads of step s, then for everyone's
-    static_assert(kTbDepth == 4, "wait_steps covers three steps in flight");
-    wait_steps((F - 1 - s) < (kTbDepth - 1) ? (F - 1 - s) : (kTbDepth - 1), nj);
+    if (s + kTbDepth - 1 < F) TB_ALOAD(s + kTbDepth - 1);
+    uint32_t pg[kTbR][20], pu[kTbR][20];
+#pragma unroll
+    for (int r = 0; r < kTbR; ++r) {
+      unpack8(wg[s % kTbWDepth][r], pg[r]);
+      unpack8(wu[s % kTbWDepth][r], pu[r]);
+    }
+    if (s + kTbWDepth < F) TB_WLOAD(s + kTbWDepth);
+    // this wavefront's activation loads of step s, then everyone's
+    wait_vm(tb_after_act(s, nj, F));
     __builtin_amdgcn_s_barrier();
     const char *buf = xs + (s % kTbDepth) * kTbStepBytes + (g * 16 + n) * 16;
-    uint32_t ng[20], nu[20];
-    if (s + 1 < F) {
-      unpack8(gd[s + 1], ng);
-      unpack8(ud[s + 1], nu);
-    }
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
       u32x4 bx[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) bx[t] = lds16(buf + (t * 5 + m) * 1024);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) accg[t] = mfma_bf16(pg + 4 * m, bx[t], accg[t]);
+      for (int r = 0; r < kTbR; ++r)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) accu[t] = mfma_bf16(pu + 4 * m, bx[t], accu[t]);
+        for (int t = 0; t < 4; ++t) {
+          accg[r][t] = mfma_bf16(pg[r] + 4 * m, bx[t], accg[r][t]);
+          accu[r][t] = mfma_bf16(pu[r] + 4 * m, bx[t], accu[r][t]);
+        }
     }
-    lds_barrier();  // the buffer of step s is refilled by the next issue
-    if (s + 1 < F) {
-#pragma unroll
-      for (int i = 0; i < 20; ++i) {
-        pg[i] = ng[i];
-        pu[i] = nu[i];
-      }
-    }
+    lds_barrier();  // the buffer of step s is refilled by a later issue
   }
+#undef TB_WLOAD
+#undef TB_ALOAD
 
+  uint32_t mx[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
+    mx[t] = 0u;
     const int col = 16 * t + n;
-    if (t >= ntt || col >= nb) continue;
-    store_h4(a, start + col, row0, accg[t], accu[t], sg, su);
+#pragma unroll
+    for (int r = 0; r < kTbR; ++r) {
+      const int row0 = (rt0 + r) * 16 + 4 * g;
+      const uint32_t m4 = store_h4(a, start + min(col, nb - 1), row0, accg[r][t], accu[r][t], sg[r], su[r],
+                                   col < nb);
+      mx[t] = max(mx[t], m4);
+    }
+    // over the four lane groups that hold the other rows of column col
+    mx[t] = max(mx[t], (uint32_t)__shfl_xor((int)mx[t], 16, 64));
+    mx[t] = max(mx[t], (uint32_t)__shfl_xor((int)mx[t], 32, 64));
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wmaxs[wave][16 * t + n] = mx[t];
+  }
+  __syncthreads();
+  if (threadIdx.x < nb) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int w = 0; w < kTbWaves; ++w) m = max(m, wmaxs[w][threadIdx.x]);
+    a.hmax[(int64_t)(start + threadIdx.x) * kTbMaxGroups + blockIdx.y] = m;
   }
 }
 
@@ -818,7 +932,9 @@ struct DownArgs {
   const uint8_t *down_p;
   int64_t stride_d;
   const float *down_s;
-  const float *hf;  // [pairs][I] fp32 h in grouped order
+  const float *hf;        // [pairs][I] fp32 h in grouped order
+  const uint32_t *hmax;   // token-blocked path: [pairs][kTbMaxGroups] largest |h| per row group
+  int hgroups;            // row groups in hmax
   const int32_t *tiles, *ntiles;
   float *O;  // [pairs][H]
   int H, I, slots;
@@ -935,8 +1051,7 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
 // rows, 138 KB of LDS); each wavefront then walks its row tiles kDtbR at a
 // time: the weights of a K step are decoded once and feed 4 token tiles x 2
 // parts x kDtbR row tiles, and each operand slice read from LDS feeds kDtbR
-// products. Token tiles past the block are skipped; columns past the block
-// read its last pair and are not stored. The next row tiles' weights are in
+// products. Columns past the block read its last pair and are not stored. The next row tiles' weights are in
 // flight while the current ones are multiplied (the first ones while h is
 // staged).
 constexpr int kDtbWaves = 8, kDtbR = 4, kDtbGroups = 2;
@@ -964,25 +1079,23 @@ __device__ __forceinline__ void dtb_load(const DownArgs &a, int e, int rt, int l
 
 // One operand slice: the hi parts of the 4 token tiles into every row tile's
 // accumulator, then the lo parts (so no two consecutive products share an
-// accumulator).
+// accumulator). All four token tiles run (straight-line code schedules the
+// LDS reads ahead of the products); columns past the block read its last pair.
 template <int NW>
 __device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, const char *const bq[4], int plane,
-                                          int off, int ntt, f32x4 (*acc)[4]) {
+                                          int off, f32x4 (*acc)[4]) {
   u32x4 b[2][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    if (t < ntt) {
-      b[0][t] = lds16(bq[t] + off);
-      b[1][t] = lds16(bq[t] + plane + off);
-    }
+  for (int t = 0; t < 4; ++t) {
+    b[0][t] = lds16(bq[t] + off);
+    b[1][t] = lds16(bq[t] + plane + off);
+  }
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      if (t < ntt) {
 #pragma unroll
-        for (int r = 0; r < kDtbR; ++r) acc[r][t] = mfma_f16(pw[r] + w0, b[q][t], acc[r][t]);
-      }
+      for (int r = 0; r < kDtbR; ++r) acc[r][t] = mfma_f16(pw[r] + w0, b[q][t], acc[r][t]);
 }
 
 template <int F, int RT>
@@ -993,7 +1106,6 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
   if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
   const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
   const int e = td.x, start = td.y, nb = td.z;
-  const int ntt = (nb + 15) / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   constexpr int M = 5 * F + tail_mfmas(RT);
@@ -1002,9 +1114,10 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
   const int per_wave = a.H / 16 / kDtbGroups / kDtbWaves;  // row tiles of this wavefront
   const int rt0 = blockIdx.y * (a.H / 16 / kDtbGroups) + wave * per_wave;
 
-  DtbWeights<F, RT> cur, nxt;
+  DtbWeights<F, RT> cur;
   dtb_load<F, RT>(a, e, rt0, lane, cur);
-  stage_h_parts<kDtbWaves, 8, M, 4>(a.hf + (int64_t)start * a.I, nb, a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig);
+  stage_h_known<64 * kDtbWaves, M>(a.hf + (int64_t)start * a.I, a.hmax + (int64_t)start * kTbMaxGroups, a.hgroups, nb,
+                                   a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig);
   __syncthreads();
 
   const char *bq[4];
@@ -1012,45 +1125,56 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
   for (int t = 0; t < 4; ++t) bq[t] = smem + min(16 * t + n, nb - 1) * rs + g * M * 16;
 #pragma unroll 1
   for (int it = 0; it < per_wave; it += kDtbR) {
-    if (it + kDtbR < per_wave) dtb_load<F, RT>(a, e, rt0 + it + kDtbR, lane, nxt);
     f32x4 acc[kDtbR][4];
 #pragma unroll
     for (int r = 0; r < kDtbR; ++r)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float4 sd[kDtbR];
 #pragma unroll
-    for (int s = 0; s < F; ++s) {
-      uint32_t pw[kDtbR][20];
-#pragma unroll
-      for (int r = 0; r < kDtbR; ++r) unpack8(cur.d[r][s], pw[r]);
-#pragma unroll
-      for (int m = 0; m < 5; ++m) dtb_slice(pw, 4 * m, bq, plane, (5 * s + m) * 16, ntt, acc);
-    }
+    for (int r = 0; r < kDtbR; ++r) sd[r] = cur.sd[r];
+    // the tail slices first, then the full steps: after the last step is
+    // decoded the weight registers are free for the next row tiles' loads,
+    // which land while that step's products run
     if constexpr (RT > 0) {
       uint32_t pw[kDtbR][16];
 #pragma unroll
       for (int r = 0; r < kDtbR; ++r) unpack_tail<RT>(cur.dw[r], cur.sh[r], pw[r]);
 #pragma unroll
-      for (int m = 0; m < tail_mfmas(RT); ++m) dtb_slice(pw, 4 * m, bq, plane, (5 * F + m) * 16, ntt, acc);
+      for (int m = 0; m < tail_mfmas(RT); ++m) {
+        dtb_slice(pw, 4 * m, bq, plane, (5 * F + m) * 16, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < F; ++s) {
+      uint32_t pw[kDtbR][20];
+#pragma unroll
+      for (int r = 0; r < kDtbR; ++r) unpack8(cur.d[r][s], pw[r]);
+      if (s == F - 1 && it + kDtbR < per_wave) dtb_load<F, RT>(a, e, rt0 + it + kDtbR, lane, cur);
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        dtb_slice(pw, 4 * m, bq, plane, (5 * s + m) * 16, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int col = 16 * t + n;
-      if (t >= ntt || col >= nb) continue;
+      if (col >= nb) continue;
       const int us = -1 - sig[col];  // the trits entered as 2t, h as 2^sig h
       float *op = a.O + (int64_t)(start + col) * a.H;
 #pragma unroll
       for (int r = 0; r < kDtbR; ++r) {
         const int row0 = (rt0 + it + r) * 16 + 4 * g;
         float4 o;
-        o.x = ldexpf(acc[r][t][0], us) * cur.sd[r].x;
-        o.y = ldexpf(acc[r][t][1], us) * cur.sd[r].y;
-        o.z = ldexpf(acc[r][t][2], us) * cur.sd[r].z;
-        o.w = ldexpf(acc[r][t][3], us) * cur.sd[r].w;
+        o.x = ldexpf(acc[r][t][0], us) * sd[r].x;
+        o.y = ldexpf(acc[r][t][1], us) * sd[r].y;
+        o.z = ldexpf(acc[r][t][2], us) * sd[r].z;
+        o.w = ldexpf(acc[r][t][3], us) * sd[r].w;
         *reinterpret_cast<float4 *>(op + row0) = o;
       }
     }
-    cur = nxt;
   }
 }
 
@@ -1566,6 +1690,7 @@ size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I) {
   o = align_up(o + (size_t)P * 4, 256);
   o = align_up(o + ffn_max_blocks(P, E) * 16, 256);
   o = align_up(o + 16, 256);
+  o = align_up(o + (size_t)P * kTbMaxGroups * 4, 256);
   return o;
 }
 
@@ -1586,6 +1711,8 @@ FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I) 
   f.blocks = (int32_t *)(b + o);
   o = align_up(o + ffn_max_blocks(P, E) * 16, 256);
   f.nblocks = (int32_t *)(b + o);
+  o = align_up(o + 16, 256);
+  f.hmax = (uint32_t *)(b + o);
   return f;
 }
 
@@ -1618,6 +1745,7 @@ static GateUpArgs gateup_args(const tmoe_moe_weights *W, const uint16_t *X, int6
   ga.sorted_token = sorted_token;
   ga.h = Hout;
   ga.hf = fw.hf;
+  ga.hmax = fw.hmax;
   ga.gx = gh;
   ga.gd = gi;
   ga.I = (int)W->inter;
@@ -1741,8 +1869,9 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
 
   GateUpArgs ga = gateup_args(W, X, P, clamp, Hout, fw, sorted_token);
   ga.offsets = offsets;
-  if (P >= 32 * E) {
-    // many pairs per expert: token-blocked (64 pairs x 128 rows per workgroup)
+  const bool tb = P >= 32 * E && I % kTbRows == 0 && I / kTbRows <= kTbMaxGroups;
+  if (tb) {
+    // many pairs per expert: token-blocked (64 pairs x 256 rows per workgroup)
     hipLaunchKernelGGL(make_tiles_kernel<64>, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.blocks, fw.nblocks);
     TMOE_LAUNCHED("make_blocks");
     GateUpArgs gb = ga;
@@ -1751,8 +1880,8 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     const size_t lds = (size_t)kTbDepth * kTbStepBytes;
     rc = allow_lds<gateup_tb_kernel<13>>(lds);
     if (rc) return rc;
-    TMOE_LAUNCH(TMOE_KERNEL_GATEUP, gateup_tb_kernel<13>,
-                dim3((unsigned)ffn_max_blocks(P, E), (unsigned)(I / (16 * kTbWaves))), dim3(64 * kTbWaves), lds, st, gb);
+    TMOE_LAUNCH(TMOE_KERNEL_GATEUP, gateup_tb_kernel<13>, dim3((unsigned)ffn_max_blocks(P, E), (unsigned)(I / kTbRows)),
+                dim3(64 * kTbWaves), lds, st, gb);
     TMOE_LAUNCHED("gateup_tb");
   } else if (P <= 64)
     rc = run_gateup<13, 0, 4, 0>(st, ga, max_tiles, (int)I, P < 4 * E);
@@ -1762,14 +1891,15 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     rc = run_gateup<13, 0, 1, 0, 1, 8>(st, ga, max_tiles, (int)I, P < 4 * E);
   if (rc) return rc;
 
-  if (P >= 32 * E && H == (int64_t)16 * kDtbGroups * kDtbWaves * (H / (16 * kDtbGroups * kDtbWaves)) &&
-      (H / 16 / kDtbGroups / kDtbWaves) % kDtbR == 0) {
+  if (tb && H % (16 * kDtbGroups * kDtbWaves) == 0 && (H / 16 / kDtbGroups / kDtbWaves) % kDtbR == 0) {
     // token-blocked down over the same 64-pair blocks
     DownArgs da;
     da.down_p = W->down_p;
     da.stride_d = W->stride_d;
     da.down_s = W->down_s;
     da.hf = fw.hf;
+    da.hmax = fw.hmax;
+    da.hgroups = (int)(I / kTbRows);
     da.tiles = fw.blocks;
     da.ntiles = fw.nblocks;
     da.O = O;
