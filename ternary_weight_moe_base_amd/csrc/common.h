@@ -171,6 +171,8 @@ struct RouterWs {
 size_t router_ws_bytes(int64_t T, int64_t E, int64_t H);
 RouterWs router_ws_carve(void *ws, int64_t T, int64_t E, int64_t H);
 constexpr int64_t kRouterMaxH = 4096;  // largest router hidden size (sizes tmoe_router_workspace_bytes)
+// bound slots per token of the fp64 logits kernel: one per four experts, E <= 1024
+constexpr int kRouterMaxSlots = 256;
 // Logits (fp64 VALU for T <= 64, fp64 matrix cores above) and the certified
 // top-k with its double-double fall-back (two kernels).
 int launch_router(hipStream_t st, const uint16_t *X, int64_t T, int64_t H, const float *Wr, const float *bias,

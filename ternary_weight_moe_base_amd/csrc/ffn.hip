@@ -368,51 +368,81 @@ struct RouteLds {
   int32_t nfix;
 };
 
+// largest of a lane's bound slots (fp64 bits of values >= 0 order as integers)
+__device__ inline uint64_t slot_max(const uint64_t (&v)[kRouterMaxSlots / 64]) {
+  uint64_t m = v[0];
+#pragma unroll
+  for (int u = 1; u < kRouterMaxSlots / 64; ++u) m = m > v[u] ? m : v[u];
+  return m;
+}
+
 template <int NPL>
 __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *smem, int rs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const DecodeRoute &r = a.r;
   const int T = a.T, E = a.E, k = a.k, P = T * k;
   const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
-  // logits of this wavefront's tokens (t = wave + 4q), in flight with the staging below
+  // every token's activations (2048 inputs = 4 KB, operand order = natural
+  // order) into LDS row t by direct buffer loads, issued first: wavefront w
+  // copies the w-th KB of each row. The buffer range bounds every read.
+  {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    for (int t = 0; t < T; ++t) {
+      const __amdgpu_buffer_rsrc_t row =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(a.X + (int64_t)t * 2048), (short)0, 4096, kBufWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          row, (__attribute__((address_space(3))) void *)(smem + t * rs + wv * 1024), 16, lane * 16 + wv * 1024, 0, 0,
+          0);
+    }
+  }
+  // logits and bound slots of this wavefront's tokens (t = wave + 4q; only
+  // read for t < T), in flight with the staging below. No load has an
+  // alternative value merged with it (indices are clamped, duplicate slots are
+  // harmless to a maximum, logits past E are replaced after arrival): a load
+  // merged with another value at a branch makes the compiler wait for it
+  // there, one round trip per load.
   double lv[kDecodeMaxT / 4][NPL];
-  uint64_t bm[kDecodeMaxT / 4];  // this lane's largest bound slot of each of the wavefront's tokens
+  uint64_t bs[kDecodeMaxT / 4][kRouterMaxSlots / 64];
 #pragma unroll
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
-    bm[q] = 0;
     if (t < T) {
-      topk_load<NPL>(r.lg + (int64_t)t * E, E, lv[q]);
+      const double *lg = r.lg + (int64_t)t * E;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) lv[q][j] = lg[min(lane * NPL + j, E - 1)];
       const uint64_t *slots = r.bnd + (int64_t)t * r.nb;
-      for (int j = lane; j < r.nb; j += 64) bm[q] = bm[q] > slots[j] ? bm[q] : slots[j];
+#pragma unroll
+      for (int u = 0; u < kRouterMaxSlots / 64; ++u) bs[q][u] = slots[min(lane + 64 * u, r.nb - 1)];
     }
   }
-  // every token's activations into LDS row t, zero row 16
-  const int vec = a.gx.slots / 8, kv = (int)(a.gx.K / 8);
-  copy16<256>(
-      T * vec,
-      [&](int i) {
-        const int t = i / vec, c = i - t * vec;
-        return c < kv ? reinterpret_cast<const uint4 *>(a.X + (int64_t)t * a.gx.K)[c] : make_uint4(0, 0, 0, 0);
-      },
-      [&](int i) {
-        const int t = i / vec, c = i - t * vec;
-        return reinterpret_cast<uint4 *>(smem + t * rs + c * 16);
-      });
+  // padding inputs 2048..2079 of the token rows and the zero row 16
+  const int nc = a.gx.slots / 8;
+  for (int i = threadIdx.x; i < T * (nc - 256); i += 256)
+    *reinterpret_cast<uint4 *>(smem + (i / (nc - 256)) * rs + (256 + i % (nc - 256)) * 16) = make_uint4(0, 0, 0, 0);
   zero_row(smem + 16 * rs, a.gx.slots, threadIdx.x, 256);
   if (threadIdx.x < 32) s.hit[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     s.info[0] = -1;
     s.nfix = 0;
   }
-  lds_barrier();  // the logits may still be in flight
+  TMOE_WAIT_VM(0);  // the activation rows and the routing loads above
+  // the slot maxima are formed only now (otherwise the compiler reduces each
+  // token's slots right after their loads, waiting there token by token)
+#pragma unroll
+  for (int q = 0; q < kDecodeMaxT / 4; ++q)
+    if (wave + 4 * q < T)
+#pragma unroll
+      for (int u = 0; u < kRouterMaxSlots / 64; ++u) asm volatile("" : "+v"(bs[q][u]));
+  lds_barrier();
   if (T == 1) {
     // one token: wavefront 0 selects its k experts; their ranks among the k
     // (all distinct) are the grouped positions and the tile indices
     if (wave == 0) {
-      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(bm[0]));
+      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(slot_max(bs[0])));
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) lv[0][j] = lane * NPL + j < E ? lv[0][j] : 0.0;
       int nfix = 0;
-      if (!topk_certified_v<NPL>(lv[0], r.lg, E, k, B, s.sidx, s.sw)) {
+      if (!topk_certified_v<NPL, true>(lv[0], r.lg, E, k, B, s.sidx, s.sw)) {
         nfix = 1;
         topk_dd<NPL>(a.X, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx, s.sw, nullptr);
       }
@@ -449,8 +479,10 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
     if (t < T) {
-      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(bm[q]));
-      if (!topk_certified_v<NPL>(lv[q], r.lg + (int64_t)t * E, E, k, B, s.sidx + t * k, s.sw + t * k)) {
+      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(slot_max(bs[q])));
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) lv[q][j] = lane * NPL + j < E ? lv[q][j] : 0.0;
+      if (!topk_certified_v<NPL, true>(lv[q], r.lg + (int64_t)t * E, E, k, B, s.sidx + t * k, s.sw + t * k)) {
         if (lane == 0) atomicAdd(&s.nfix, 1);
         topk_dd<NPL>(a.X + (int64_t)t * a.gx.K, (int)a.gx.K, r.Wr, r.bias, E, k, s.sidx + t * k, s.sw + t * k,
                      nullptr);
@@ -527,6 +559,7 @@ __device__ inline void gateup_work(const GateUpArgs &a, char *smem, int tile_id,
   const int32_t *toks;
   const int rs0 = lds_row_bytes(a.gx.slots);
   if constexpr (RNPL > 0) {
+    static_assert(F == 13 && RT == 0, "the prologue copies activation rows as 2048 inputs");
     __shared__ RouteLds rl;
     route_prologue<RNPL>(a, rl, smem, rs0);
     e = rl.info[0];
@@ -1217,8 +1250,12 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   const int n = lane & 15, g = lane >> 4;
   const int64_t tbytes = 64 * (int64_t)(8 * F + RT);
   const int nt = *a.ntiles;
-  int4 td0 = make_int4(0, 0, 1, 0);
-  if (wave < a.max_tiles) td0 = reinterpret_cast<const int4 *>(a.tiles)[wave];  // first tile, before nt is known
+  // first tile (before nt is known), then each pair's token and weight: all
+  // issued unconditionally (clamped indices), so they share one round trip
+  const int4 td0 = reinterpret_cast<const int4 *>(a.tiles)[min(wave, a.max_tiles - 1)];
+  const int pi = min((int)threadIdx.x, a.P - 1);
+  const int32_t tok_i = a.sorted_token[pi];
+  const float pw_i = a.pair_w[pi];
   // the first tile's weights in flight while h is staged
   uint2 dd0[F];
   uint32_t ddw0 = 0, dsh0 = 0;
@@ -1234,8 +1271,8 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_kernel(DownCombine
   stage_h_parts<kDcWaves, kDcMaxPairs / kDcWaves, M>(a.hf, a.P, a.I, 5 * a.gd.Q, hps, hps + plane, a.slots * 2,
                                                      s_sig);
   if ((int)threadIdx.x < a.P) {
-    s_tok[threadIdx.x] = a.sorted_token[threadIdx.x];
-    s_pw[threadIdx.x] = a.pair_w[threadIdx.x];
+    s_tok[threadIdx.x] = tok_i;
+    s_pw[threadIdx.x] = pw_i;
   }
   for (int i = lane; i < kDecodeMaxT * 16; i += 64) (&yacc[wave][0][0])[i] = 0.f;
   lds_barrier();  // the first tile's weights may still be in flight
@@ -1801,7 +1838,8 @@ int launch_decode_tail(hipStream_t st, const tmoe_moe_weights *W, const uint16_t
   const int64_t E = W->n_experts, H = W->hidden, I = W->inter;
   const int k = W->top_k;
   const int64_t P = T * k;
-  if (T < 1 || T > kDecodeMaxT || k > 16 || E > 1024) return fail(TMOE_E_UNSUPPORTED, "decode path limits");
+  if (T < 1 || T > kDecodeMaxT || k > 16 || E > 1024 || r.nb < 1 || r.nb > kRouterMaxSlots)
+    return fail(TMOE_E_UNSUPPORTED, "decode path limits");
   const Geom gi = make_geom(I);
   GateUpArgs ga = gateup_args(W, X, P, clamp, nullptr, fw, r.sorted_token);
   ga.r = r;

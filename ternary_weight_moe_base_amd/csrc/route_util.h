@@ -170,7 +170,9 @@ __device__ inline double readlane_d(double v, int l) {
 // outside ROW_MASK keep their value).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+  // lanes outside ROW_MASK read 0, the identity of an unsigned maximum, which
+  // lets the compiler fold the permutation into the max instruction itself
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
   return o > v ? o : v;
 }
 
@@ -357,7 +359,10 @@ __device__ inline bool topk_select(uint64_t key[NPL], int E, int k, double B, in
 // Otherwise it returns false and writes nothing (about 0.1% of tokens with
 // logits ~ N(0, 1); the caller then runs topk_select). When it returns true,
 // idx and w are those topk_select writes: same ranks, same fp64 softmax.
-template <int NPL>
+// kLanes: the selected logits come from the lanes holding them (one latency
+// chain fewer, for a single token) instead of a re-read of lg (cheaper when
+// many wavefronts share the memory pipeline).
+template <int NPL, bool kLanes = false>
 __device__ inline bool topk_fast(const double v[NPL], const double *lg, int E, int k, double B, int32_t *idx,
                                  float *w) {
   constexpr int IB = NPL * 64 <= 256 ? 8 : (NPL * 64 <= 1024 ? 10 : 12);
@@ -396,8 +401,21 @@ __device__ inline bool topk_fast(const double v[NPL], const double *lg, int E, i
   const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)mine, m - 1);
   if (__ballot(key[0] >= ((last >> IB) << IB)) != 0ull) return false;  // bucket shared with an unselected expert
   const int myi = E - 1 - (int)(mine & ((1u << IB) - 1u));
-  // (a re-read of lg measured faster than fetching the values from other lanes)
-  const double myv = lane < m ? lg[myi] : 0.0;
+  double myv;
+  if constexpr (kLanes) {
+    // slot myi = NPL * lane' + j' lives in lane' (every lane takes part in the
+    // shuffles; lanes past m hold a valid index and discard the value)
+    const int src = myi / NPL, sj = myi - src * NPL;
+    double got = 0.0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const double t = __shfl(v[j], src, 64);
+      got = j == sj ? t : got;
+    }
+    myv = lane < m ? got : 0.0;
+  } else {
+    myv = lane < m ? lg[myi] : 0.0;
+  }
   const double nxt = __shfl_down(myv, 1, 64);
   if (__ballot(lane + 1 < m && !(myv - nxt > 2.0 * B)) != 0ull) return false;
   const double v0 = readlane_d(myv, 0);
@@ -414,10 +432,10 @@ __device__ inline bool topk_fast(const double v[NPL], const double *lg, int E, i
 // Certified top-k of one token's logits lg[0..E) (also held as by topk_load)
 // by one wavefront: the fast 32-bit path, then the 64-bit tournament. False:
 // not certifiable in fp64.
-template <int NPL>
+template <int NPL, bool kLanes = false>
 __device__ inline bool topk_certified_v(const double v[NPL], const double *lg, int E, int k, double B, int32_t *idx,
                                         float *w) {
-  if (topk_fast<NPL>(v, lg, E, k, B, idx, w)) return true;
+  if (topk_fast<NPL, kLanes>(v, lg, E, k, B, idx, w)) return true;
   uint64_t key[NPL];
   topk_keys<NPL>(v, E, key);
   return topk_select<NPL>(key, E, k, B, idx, w);

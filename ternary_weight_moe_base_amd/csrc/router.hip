@@ -64,14 +64,15 @@ RouterWs router_ws_carve(void *ws, int64_t T, int64_t E, int64_t H) {
 }
 
 // ------------------------------------------------------------ fp64 logits
-// Each lane keeps 4*NC router weights (elements c*256 + 4*lane + 0..3) as fp64
+// Each lane keeps 4*NC router weights (elements c*256 + 4*lane + 0..3, loaded
+// by the caller as wv[c]) as fp64
 // and runs one FMA chain of 4*NC exact products per logit, then a 6-level
 // butterfly: depth 4*NC + 6, plus 1 for the bias. The same chain accumulates
 // A = sum |x w| for the bound. Results for token n go to lgs[n*4 + wave] and
 // abs_s[n*4 + wave] (LDS).
 template <int NC>
-__device__ inline void logits_rows(const uint16_t *xs, int nt, const float *Wr, const float *bias, int64_t e, int E,
-                                   double *lgs, double *abs_s) {
+__device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv)[NC], const float *bias, int64_t e,
+                                   int E, double *lgs, double *abs_s) {
   constexpr int H = NC * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (e >= E) {
@@ -86,7 +87,7 @@ __device__ inline void logits_rows(const uint16_t *xs, int nt, const float *Wr, 
   double w[4 * NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    float4 v = reinterpret_cast<const float4 *>(Wr + e * H)[c * 64 + lane];
+    const float4 v = wv[c];
     w[4 * c] = v.x;
     w[4 * c + 1] = v.y;
     w[4 * c + 2] = v.z;
@@ -137,9 +138,17 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *X, i
   const int64_t t0 = (int64_t)blockIdx.y * tchunk;
   const int nt = (int)min<int64_t>(tchunk, T - t0);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && n_fixup) *n_fixup = 0;
+  // this wavefront's router row first, so its fetch overlaps the activation
+  // staging (rows past E read row E - 1 and are not used: no branch around the
+  // loads, which would make the compiler wait for each one)
+  const int64_t e = e0 + (threadIdx.x >> 6);
+  const float4 *wrow = reinterpret_cast<const float4 *>(Wr + min<int64_t>(e, E - 1) * (NC * 256));
+  float4 wv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) wv[c] = wrow[c * 64 + (threadIdx.x & 63)];
   stage_x(xs, X, t0, nt, NC * 256);
   __syncthreads();
-  logits_rows<NC>(xs, nt, Wr, bias, e0 + (threadIdx.x >> 6), (int)E, lgs, abs_s);
+  logits_rows<NC>(xs, nt, wv, bias, e, (int)E, lgs, abs_s);
   __syncthreads();
   for (int i = threadIdx.x; i < nt * 4; i += 256) {
     const int n = i >> 2, q = i & 3;
