@@ -289,7 +289,7 @@ int tmoe_moe_forward(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
  * which must be the stream's). Requests whose workspace
  * (tmoe_moe_workspace_bytes) exceeds the array fail with TMOE_E_WORKSPACE
  * before anything is enqueued: at the model's shape (hidden 2048, 256 experts,
- * top 8, inter 512) up to 384 tokens fit. All calls on one GPU share its
+ * top 8, inter 512) up to 395 tokens fit. All calls on one GPU share its
  * array, so calls that may overlap on one GPU (different streams, or
  * different threads) race and must be serialized by the caller; each call
  * writes every byte of it that it reads, so nothing needs clearing between
