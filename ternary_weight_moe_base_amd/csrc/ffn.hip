@@ -41,32 +41,42 @@ __device__ __forceinline__ uint32_t fma16x2(uint32_t a, uint32_t b, uint32_t c) 
                                                                 __builtin_bit_cast(f16x2, b),
                                                                 __builtin_bit_cast(f16x2, c)));
 }
-__device__ __forceinline__ uint32_t shl14x2(uint32_t w) {
-  u16x2 v = __builtin_bit_cast(u16x2, w);
-  v = v << (unsigned short)14;
-  return __builtin_bit_cast(uint32_t, v);
-}
-// ((v + 3) << 14) per 16-bit half
-__device__ __forceinline__ uint32_t top_digit_x2(uint32_t w) {
-  u16x2 v = __builtin_bit_cast(u16x2, w);
-  v = v * (unsigned short)0x4000 + (unsigned short)0xC000;
-  return __builtin_bit_cast(uint32_t, v);
+// v * 2^14 + c per 16-bit half (mod 2^16): moves the two low bits of v to the
+// top of the half and adds c. The multiplier passes through an empty asm so
+// that the compiler cannot see the power of two (it would emit a shift and an
+// add instead of one v_pk_mad_u16).
+__device__ __forceinline__ uint32_t mad14x2(uint32_t v, uint32_t c) {
+  uint32_t m = 0x40004000u;
+  asm("" : "+s"(m));
+  const u16x2 x = __builtin_bit_cast(u16x2, v), y = __builtin_bit_cast(u16x2, c), k = __builtin_bit_cast(u16x2, m);
+  return __builtin_bit_cast(uint32_t, (u16x2)(x * k + y));
 }
 
 // fp16 constants (two copies per dword)
 #define K_THIRD 0x35553555u  // 0.333251953125
 #define K_C1 0x61556155u     // 682.5
-#define K_43 0x3D553D55u     // 1.3330078125
-#define K_C2 0xDD49DD49u     // -338.25
 
 // Five pair-words (digits q = 0..4 of both bytes) from v = fp16 (1024 + b0, 1024 + b1).
+// With v_q = 1024 + R_q, the chain FMA v_(q+1) = fp16(K_THIRD v_q + 682.5) is
+// 1023.75 + R_q / 3 - 8e-5 R_q before rounding, so fp16's integer grid on
+// [1024, 2048) rounds it to 1024 + R_(q+1), R_(q+1) = floor(R_q / 3); hence
+// the bit patterns of v_q and v_(q+1) sum to 0xC800 + R_q + R_(q+1) =
+// 0xC800 + 4 R_(q+1) + d_q, and 2^14 (v_q + v_(q+1) + 3) mod 2^16 is
+// ((d_q + 3) mod 4) << 14: 0xC000, 0, 0x4000 for d = 0, 1, 2, the bf16 and
+// fp16 bit pattern of 2t. Per digit: one chain FMA, one integer multiply-add
+// for (v_(q+1) + 3) << 14, one for the operand.
 __device__ __forceinline__ void digits5(uint32_t v, uint32_t *pw) {
+  uint32_t c[5];
+  c[0] = v;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    pw[q] = shl14x2(fma16x2(v, K_43, K_C2));
-    v = fma16x2(v, K_THIRD, K_C1);
+  for (int q = 1; q < 5; ++q) c[q] = fma16x2(c[q - 1], K_THIRD, K_C1);
+  uint32_t hi = mad14x2(c[4], 0xC000C000u);  // (v_4 + 3) << 14: the top digit's operand
+  pw[4] = hi;
+#pragma unroll
+  for (int q = 3; q >= 0; --q) {
+    pw[q] = mad14x2(c[q], hi);
+    if (q > 0) hi = mad14x2(c[q], 0xC000C000u);
   }
-  pw[4] = top_digit_x2(v);
 }
 // bytes 0,1 (lo) or 2,3 (hi) of d as fp16 (1024 + b) pairs
 __device__ __forceinline__ uint32_t pair_lo(uint32_t d) { return __builtin_amdgcn_perm(0x64646464u, d, 0x04010400u); }
