@@ -111,10 +111,10 @@ int tmoe_validate_packed_host(const uint8_t *P, int64_t R, int64_t K, int64_t ld
 int64_t tmoe_tiled_bytes(int64_t R, int64_t K);
 
 /* Device absmean ternarize + canonical pack of fp32 W [R][K] (row stride K):
- * same definition as tmoe_ternarize_absmean_host (the fp64 sum is a fixed
- * tree instead of index order; both are exact for the synthetic weights,
- * whose values are multiples of 2^-16). Out: P [R][ldp] (bytes past ceil(K/5)
- * untouched), s [R]. */
+ * the definition of tmoe_ternarize_absmean_host, bit for bit for any finite
+ * fp32 input (the fp64 sum of |w| runs in index order, one thread per row).
+ * Out: P [R][ldp] (bytes past ceil(K/5) untouched), s [R]. Non-finite inputs
+ * are not checked on the device. */
 int tmoe_ternarize_pack(void *stream, const float *W, int64_t R, int64_t K, uint8_t *P, int64_t ldp, float *s);
 
 /* Device unpack of canonical bytes (the bit-exact parity hook): T int8 [R][K]. */

@@ -53,25 +53,43 @@ int launch_synth_ih12(hipStream_t st, uint64_t key0, uint64_t key1, uint64_t sid
 }
 
 // ------------------------------------------------- ternarize + pack (device)
-// One workgroup per row. s = fp32(sum |w| / K) with the sum in fp64 over a
-// fixed tree (per-thread strided partial sums, then a binary tree over the
-// 256 threads); trit = sign(w) if 2|w| > s else 0; canonical base-3 bytes.
-__global__ __launch_bounds__(256) void ternarize_pack_kernel(const float *W, int64_t K, uint8_t *P, int64_t ldp,
-                                                             float *S) {
-  __shared__ double red[256];
-  const int64_t r = blockIdx.x;
+// Scales first: one lane per row, s = fp32(sum |w| / K) with the fp64 sum in
+// index order, the same additions in the same order as the host definition,
+// so s is bit-identical to it for any finite fp32 row. Each lane walks its own
+// row, 64 inputs (two cache lines) in flight ahead of the additions when rows
+// are 16-byte aligned.
+__global__ __launch_bounds__(256) void absmean_rows_kernel(const float *W, int64_t R, int64_t K, float *S) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
   const float *w = W + r * K;
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < K; i += 256) acc += fabs((double)w[i]);
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
+  int64_t i = 0;
+  if ((K & 3) == 0 && ((uintptr_t)W & 15) == 0) {
+    const float4 *w4 = reinterpret_cast<const float4 *>(w);
+    for (; i + 64 <= K; i += 64) {
+      float4 v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = w4[i / 4 + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc += fabs((double)v[j].x);
+        acc += fabs((double)v[j].y);
+        acc += fabs((double)v[j].z);
+        acc += fabs((double)v[j].w);
+      }
+    }
   }
-  const float s = K ? (float)(red[0] / (double)K) : 0.0f;
-  if (threadIdx.x == 0) S[r] = s;
-  const double sd = (double)s;
+  for (; i < K; ++i) acc += fabs((double)w[i]);
+  S[r] = K ? (float)(acc / (double)K) : 0.0f;
+}
+
+// Then one workgroup per row: trit = sign(w) if 2|w| > s else 0 (in fp64,
+// exact), canonical base-3 bytes.
+__global__ __launch_bounds__(256) void ternarize_pack_kernel(const float *W, int64_t K, uint8_t *P, int64_t ldp,
+                                                             const float *S) {
+  const int64_t r = blockIdx.x;
+  const float *w = W + r * K;
+  const double sd = (double)S[r];
   const int64_t Kb = (K + 4) / 5;
   for (int64_t j = threadIdx.x; j < Kb; j += 256) {
     int code = 0, p3 = 1;
@@ -91,6 +109,8 @@ __global__ __launch_bounds__(256) void ternarize_pack_kernel(const float *W, int
 
 int launch_ternarize_pack(hipStream_t st, const float *W, int64_t R, int64_t K, uint8_t *P, int64_t ldp, float *s) {
   if (R > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "R too large");
+  hipLaunchKernelGGL(absmean_rows_kernel, dim3((unsigned)cdiv(R, 256)), dim3(256), 0, st, W, R, K, s);
+  TMOE_LAUNCHED("absmean_rows");
   hipLaunchKernelGGL(ternarize_pack_kernel, dim3((unsigned)R), dim3(256), 0, st, W, K, P, ldp, s);
   TMOE_LAUNCHED("ternarize_pack");
   return TMOE_OK;

@@ -59,6 +59,17 @@ def test_host_synthetic_weights_match_oracle():
     assert np.array_equal(T, To) and np.array_equal(s, so)
 
 
+def test_host_scale_sums_in_index_order():
+    # |w| = (1, 2^-53, 2^-24, 2^-53): index order rounds the mean to 0.25, a
+    # pairwise order would give 0.25 + 2^-25 (see the device test of the same rows)
+    base = np.array([1.0, 2.0 ** -53, 2.0 ** -24, 2.0 ** -53])
+    W = np.stack([base, 4.0 * base, -0.5 * base]).astype(np.float32)
+    T, s = tm.ternarize_absmean_host(W)
+    assert np.array_equal(s, np.array([0.25, 1.0, 0.125], np.float32))
+    t_ref, s_ref = O.ternarize_absmean(W)
+    assert np.array_equal(s, s_ref) and np.array_equal(T, t_ref)
+
+
 def test_host_exhaustive_codes():
     import itertools
     tuples = np.array(list(itertools.product([-1, 0, 1], repeat=5)), dtype=np.int8)

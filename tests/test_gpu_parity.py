@@ -78,6 +78,23 @@ def test_ternarize_pack_device(tm, R, K, kind):
     assert np.array_equal(host(T), t_ref)
 
 
+def test_ternarize_scale_sums_in_index_order(tm):
+    """The scale's fp64 sum runs in index order, as the definition states: for
+    |w| = (1, 2^-53, 2^-24, 2^-53) index order loses both 2^-53 terms to
+    round-half-even and the mean 1/4 + 2^-26 rounds (half-even) to fp32 0.25,
+    while pairing (1 + 2^-24) + (2^-53 + 2^-53) keeps 2^-52 and rounds up to
+    0.25 + 2^-25. Rows: that pattern, scaled by powers of two and negated."""
+    base = np.array([1.0, 2.0 ** -53, 2.0 ** -24, 2.0 ** -53])
+    W = np.stack([base, 4.0 * base, -0.5 * base, base * np.array([1, -1, 1, -1])]).astype(np.float32)
+    P = torch.empty((4, 1), dtype=torch.uint8, device="cuda")
+    s = torch.empty(4, dtype=torch.float32, device="cuda")
+    tm.ternarize_pack(dev(W), P, s)
+    t_ref, s_ref = O.ternarize_absmean(W)
+    assert np.array_equal(s_ref, np.array([0.25, 1.0, 0.125, 0.25], np.float32))
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(P)[:, 0], O.pack_trits(t_ref)[:, 0])
+
+
 def test_unpack_all_codes(tm):
     codes = np.tile(np.arange(243, dtype=np.uint8), (3, 1))
     T = torch.empty((3, 243 * 5), dtype=torch.int8, device="cuda")
