@@ -443,10 +443,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 //     |b_e|, and idx and the softmax over the k (fp64 values) are written.
 // A token with more than 64 candidates, or not certified, is recomputed in
 // double-double (counted in *n_fixup).
-constexpr int kRfBatch = 3;
+constexpr int kRfBatch = 2;  // rows in flight per batch (three waves per SIMD fit)
 
 template <int NPL, int NC>
-__global__ __launch_bounds__(256) void router_topk_refine_kernel(int64_t T, const uint16_t *X, const float *Wr,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void router_topk_refine_kernel(int64_t T, const uint16_t *X, const float *Wr,
                                                                  const float *bias, const float *part, int SK,
                                                                  const uint64_t *wmax, int nslots,
                                                                  const double *wnorm, int E, int k, double gfac,
@@ -461,11 +461,29 @@ __global__ __launch_bounds__(256) void router_topk_refine_kernel(int64_t T, cons
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
   const uint16_t *x = X + t * H;
+  // every load the first step needs is issued before the first wait (no
+  // branches around them: indices are clamped, extra values unused): the
+  // token's inputs, the slots of row-norm and bias maxima, the SK partial sums
   uint2 xp[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) xp[c] = reinterpret_cast<const uint2 *>(x)[c * 64 + lane];
+  uint64_t wmv[kRouterMaxSlots / 64], bmv[kRouterMaxSlots / 64];
+#pragma unroll
+  for (int u = 0; u < kRouterMaxSlots / 64; ++u) {
+    const int j = min(lane + 64 * u, nslots - 1);
+    wmv[u] = wmax[j];
+    bmv[u] = wmax[nslots + j];
+  }
+  float pv[kRgMaxSK][NPL];
+#pragma unroll
+  for (int q = 0; q < kRgMaxSK; ++q) {
+    const float *pr = part + ((size_t)min(q, SK - 1) * T + t) * E;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) pv[q][j] = pr[min(lane * NPL + j, E - 1)];
+  }
   double s2 = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    xp[c] = reinterpret_cast<const uint2 *>(x)[c * 64 + lane];
     const double q[4] = {__uint_as_float(xp[c].x << 16), __uint_as_float(xp[c].x & 0xFFFF0000u),
                          __uint_as_float(xp[c].y << 16), __uint_as_float(xp[c].y & 0xFFFF0000u)};
 #pragma unroll
@@ -473,26 +491,23 @@ __global__ __launch_bounds__(256) void router_topk_refine_kernel(int64_t T, cons
   }
   const double nx = 1.01 * sqrt(wave_sum_dpp(s2));  // |x_t|_2 with a 1% margin
   uint64_t wm = 0, bm = 0;
-  for (int j = lane; j < nslots; j += 64) {
-    wm = wm > wmax[j] ? wm : wmax[j];
-    bm = bm > wmax[nslots + j] ? bm : wmax[nslots + j];
+#pragma unroll
+  for (int u = 0; u < kRouterMaxSlots / 64; ++u) {
+    wm = wm > wmv[u] ? wm : wmv[u];
+    bm = bm > bmv[u] ? bm : bmv[u];
   }
   const double B1 = gfac * (nx * __longlong_as_double((long long)wave_max_u64(wm)) +
                             __longlong_as_double((long long)wave_max_u64(bm))) + babs;
 
-  // ---- 1. candidates
+  // ---- 1. candidates (the slice sums added in slice order, as before)
   double v[NPL];
   uint32_t key[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) v[j] = 0.0;
-  for (int q = 0; q < SK; ++q) {
-    const float *pr = part + ((size_t)q * T + t) * E;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int e = lane * NPL + j;
-      if (e < E) v[j] += (double)pr[e];
-    }
-  }
+  for (int q = 0; q < kRgMaxSK; ++q)
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) v[j] += q < SK ? (double)pv[q][j] : 0.0;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane * NPL + j;
@@ -543,9 +558,13 @@ __global__ __launch_bounds__(256) void router_topk_refine_kernel(int64_t T, cons
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
 
-    // ---- 2. fp64 values of the candidates
-    double myv = 0.0, myb = 0.0;
-    int mye = 0;
+    // ---- 2. fp64 values of the candidates. Lane i fetches candidate i's bias
+    // and row norm now, in flight with the first batch of rows (loaded where
+    // they are used, they would cost a round trip per candidate).
+    const int mye = cand[wave][min(lane, nc - 1)];
+    const double cb = bias ? (double)bias[mye] : 0.0;
+    const double cw = wnorm[mye];
+    double myv = 0.0;
     for (int i0 = 0; i0 < nc; i0 += kRfBatch) {
       int eb[kRfBatch];
       float4 q[kRfBatch][NC];
@@ -574,14 +593,10 @@ __global__ __launch_bounds__(256) void router_topk_refine_kernel(int64_t T, cons
 #pragma unroll
       for (int u = 0; u < kRfBatch; ++u) {
         const double sum = wave_sum_dpp(acc[u]);
-        if (lane == i0 + u) {
-          const double b = bias ? (double)bias[eb[u]] : 0.0;
-          myv = sum + b;
-          myb = nx * wnorm[eb[u]] + fabs(b);
-          mye = eb[u];
-        }
+        myv = lane == i0 + u ? sum + cb : myv;
       }
     }
+    const double myb = lane < nc ? nx * cw + fabs(cb) : 0.0;
     // B2 over the candidates; chain 4 NC, butterfly 6, bias 1, margin 2
     const double B2 = 1.01 * gamma_d(4 * NC + 9) * __longlong_as_double((long long)wave_max_u64(dbits(myb)));
 
