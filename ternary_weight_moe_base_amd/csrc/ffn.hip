@@ -1684,36 +1684,50 @@ __global__ __launch_bounds__(256) void linear3_kernel(Linear3Args a) {
 }
 
 // ------------------------------------------------------------------ combine
-// grid (T, H / 512), 128 threads x one float4 each; fixed slot order j = 0..k-1.
+// grid (T, H / 512), 128 threads x one float4 each; fixed slot order j = 0..k-1
+// (slots with pos < 0 are skipped). The slots go 8 at a time with all 8 output
+// rows in flight before the first product: no load sits under a branch (an
+// invalid slot reads row 0 and is dropped by a select, so nothing it holds can
+// reach the sum), which would make each product wait for its own load.
 // NT: the expert outputs are far larger than the caches and read once, non-temporally.
 template <bool NT>
 __global__ __launch_bounds__(128) void combine_kernel(const float *O, const float *w, const int32_t *pos, int k,
                                                        int H, float *Y, const uint16_t *resid_in,
                                                        uint16_t *resid_out) {
+  constexpr int B = 8;
   const int64_t t = blockIdx.x;
   const int c = blockIdx.y * 128 + threadIdx.x;  // float4 column
   if (c * 4 >= H) return;
+  uint2 xi = make_uint2(0u, 0u);  // the residual input, fetched with the first slots
+  if (resid_out) xi = reinterpret_cast<const uint2 *>(resid_in + t * H)[c];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int j = 0; j < k; ++j) {
-    const int p = pos[t * k + j];
-    if (p < 0) continue;
-    const float wj = w[t * k + j];
-    float4 o;
-    if constexpr (NT) {
-      const f32x4 o4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(O + (int64_t)p * H) + c);
-      o = make_float4(o4[0], o4[1], o4[2], o4[3]);
-    } else {
-      o = reinterpret_cast<const float4 *>(O + (int64_t)p * H)[c];
+  for (int j0 = 0; j0 < k; j0 += B) {
+    int pj[B];
+    float wj[B];
+    f32x4 o[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int j = min(j0 + u, k - 1);
+      pj[u] = pos[t * k + j];
+      wj[u] = w[t * k + j];
     }
-    acc.x = fmaf(wj, o.x, acc.x);
-    acc.y = fmaf(wj, o.y, acc.y);
-    acc.z = fmaf(wj, o.z, acc.z);
-    acc.w = fmaf(wj, o.w, acc.w);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(O + (int64_t)max(pj[u], 0) * H) + c;
+      if constexpr (NT) o[u] = __builtin_nontemporal_load(src);
+      else o[u] = *src;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const bool use = j0 + u < k && pj[u] >= 0;
+      acc.x = use ? fmaf(wj[u], o[u][0], acc.x) : acc.x;
+      acc.y = use ? fmaf(wj[u], o[u][1], acc.y) : acc.y;
+      acc.z = use ? fmaf(wj[u], o[u][2], acc.z) : acc.z;
+      acc.w = use ? fmaf(wj[u], o[u][3], acc.w) : acc.w;
+    }
   }
   if (Y) reinterpret_cast<float4 *>(Y + t * H)[c] = acc;
   if (resid_out) {
-    const uint2 xi = reinterpret_cast<const uint2 *>(resid_in + t * H)[c];
     const float x0 = __uint_as_float(xi.x << 16), x1 = __uint_as_float(xi.x & 0xFFFF0000u);
     const float x2 = __uint_as_float(xi.y << 16), x3 = __uint_as_float(xi.y & 0xFFFF0000u);
     uint2 r;
