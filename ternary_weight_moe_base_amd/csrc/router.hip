@@ -269,18 +269,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // squares) to wnorm[e], and the workgroup's largest row norm and largest
 // |b_e| to slots wmax[b], wmax[nslots + b] (fp64 bits). Also clears the
 // fix-up counter.
-__global__ __launch_bounds__(256) void router_split_kernel(const float *Wr, const float *bias, int E, int H,
+template <int NC>
+__global__ __launch_bounds__(256) void router_split_kernel(const float *Wr, const float *bias, int E,
                                                            uint16_t *parts, uint64_t *wmax, int nslots,
                                                            double *wnorm, int32_t *n_fixup) {
+  constexpr int H = NC * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 4 + wave;
   __shared__ double nw[4], nb[4];
   if (blockIdx.x == 0 && threadIdx.x == 0 && n_fixup) *n_fixup = 0;
+  // |b_e| fetched first and unconditionally (a valid address either way)
+  const float bv = (bias ? bias : Wr)[min(e, E - 1)];
   double s2 = 0.0;
   if (e < E) {
     const size_t plane = (size_t)E * H;
-    for (int i = lane * 4; i < H; i += 256) {
-      const float4 v = *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + i);
+    // the row's NC loads are all in flight before the first conversion
+    float4 rv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) rv[c] = *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + c * 256 + lane * 4);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = c * 256 + lane * 4;
+      const float4 v = rv[c];
       const float f[4] = {v.x, v.y, v.z, v.w};
       uint32_t pw[2][2] = {};
 #pragma unroll
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *Wr, cons
   if (lane == 0) {
     nw[wave] = sqrt(s2);
     if (e < E) wnorm[e] = nw[wave];
-    nb[wave] = (e < E && bias) ? fabs((double)bias[e]) : 0.0;
+    nb[wave] = (e < E && bias) ? fabs((double)bv) : 0.0;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -703,8 +713,8 @@ static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
   if (T >= kBf16RouterMinT && !want_logits) {
     // candidates from the bf16 matrix cores, ranked on fp64 recomputed values
     const int nslots = (int)cdiv(E, 4);
-    TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_split_kernel, dim3((unsigned)nslots), dim3(256), 0, st, Wr, bias,
-                (int)E, H, rw.parts, rw.wmax, nslots, rw.wnorm, n_fixup);
+    TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_split_kernel<NC>, dim3((unsigned)nslots), dim3(256), 0, st, Wr,
+                bias, (int)E, rw.parts, rw.wmax, nslots, rw.wnorm, n_fixup);
     TMOE_LAUNCHED("router_split");
     const int64_t ntile = cdiv(T, 128) * cdiv(E, 128);
     if (ntile * kRgMaxSK > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
