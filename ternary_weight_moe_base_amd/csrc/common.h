@@ -193,10 +193,12 @@ struct GroupWs {
 };
 size_t group_ws_bytes(int64_t T, int k, int64_t E);
 GroupWs group_ws_carve(void *ws, int64_t T, int k, int64_t E);
-// tiles / ntiles (may be null): also write the work tiles (<= 16 pairs of one expert each)
+// tiles / ntiles (may be null): also write the work tiles (<= `tile` pairs of one expert each)
 int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
                  int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw, int32_t *tiles,
-                 int32_t *ntiles);
+                 int32_t *ntiles, int tile);
+// Whether the expert kernels take the token-blocked form (64-pair blocks) for P pairs.
+bool ffn_blocked(int64_t P, int64_t E, int64_t H, int64_t I);
 
 struct FfnWs {
   int32_t *tiles;    // [max_tiles][4]: expert, start, count, 0
@@ -212,7 +214,9 @@ int64_t ffn_max_tiles(int64_t pairs, int64_t E);
 size_t ffn_ws_bytes(int64_t T, int k, int64_t E, int64_t H, int64_t I);
 FfnWs ffn_ws_carve(void *ws, int64_t T, int k, int64_t E, int64_t H, int64_t I);
 // Grouped expert FFN (gate/up + SiLU/clamp, down) from grouping offsets;
-// tiles_ready: fw.tiles / fw.ntiles were already written by the grouping.
+// tiles_ready: the grouping already wrote the work tiles the expert kernels
+// take: fw.blocks / fw.nblocks (64 pairs) when ffn_blocked, else fw.tiles /
+// fw.ntiles (16 pairs).
 int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int64_t T, const int32_t *offsets,
                const int32_t *sorted_token, float clamp, float *O, float *Hout, const FfnWs &fw, bool tiles_ready);
 

@@ -1923,7 +1923,8 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
   const int64_t max_tiles = ffn_max_tiles(P, E);
   if (max_tiles > 0x7FFFFFFF || T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "too many tokens");
 
-  if (!tiles_ready) {
+  const bool tb = ffn_blocked(P, E, H, I);
+  if (!tiles_ready && !tb) {
     TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel<16>, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.tiles,
                 fw.ntiles);
     TMOE_LAUNCHED("make_tiles");
@@ -1931,11 +1932,13 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
 
   GateUpArgs ga = gateup_args(W, X, P, clamp, Hout, fw, sorted_token);
   ga.offsets = offsets;
-  const bool tb = P >= 32 * E && I % kTbRows == 0 && I / kTbRows <= kTbMaxGroups;
   if (tb) {
     // many pairs per expert: token-blocked (64 pairs x 256 rows per workgroup)
-    hipLaunchKernelGGL(make_tiles_kernel<64>, dim3(1), dim3(256), 0, st, offsets, (int)E, fw.blocks, fw.nblocks);
-    TMOE_LAUNCHED("make_blocks");
+    if (!tiles_ready) {
+      TMOE_LAUNCH(TMOE_KERNEL_MAKE_TILES, make_tiles_kernel<64>, dim3(1), dim3(256), 0, st, offsets, (int)E,
+                  fw.blocks, fw.nblocks);
+      TMOE_LAUNCHED("make_blocks");
+    }
     GateUpArgs gb = ga;
     gb.tiles = fw.blocks;
     gb.ntiles = fw.nblocks;
@@ -1953,7 +1956,7 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     rc = run_gateup<13, 0, 1, 0, 1, 8>(st, ga, max_tiles, (int)I, P < 4 * E);
   if (rc) return rc;
 
-  if (tb && H % (16 * kDtbGroups * kDtbWaves) == 0 && (H / 16 / kDtbGroups / kDtbWaves) % kDtbR == 0) {
+  if (tb) {
     // token-blocked down over the same 64-pair blocks
     DownArgs da;
     da.down_p = W->down_p;
@@ -1979,6 +1982,11 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     return TMOE_OK;
   }
   return run_down(st, W, fw, P, max_tiles, O);
+}
+
+bool ffn_blocked(int64_t P, int64_t E, int64_t H, int64_t I) {
+  return P >= 32 * E && I % kTbRows == 0 && I / kTbRows <= kTbMaxGroups && H % (16 * kDtbGroups * kDtbWaves) == 0 &&
+         (H / 16 / kDtbGroups / kDtbWaves) % kDtbR == 0;
 }
 
 size_t linear_ws_bytes(int64_t T, int64_t K) {

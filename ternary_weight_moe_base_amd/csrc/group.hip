@@ -117,16 +117,16 @@ __device__ inline void scatter_block_r(const uint32_t *bits, const int *base, co
   }
 }
 
-// Work tiles of up to 16 grouped pairs of one expert, in expert order, from
-// the per-expert counts c[] and offsets off[] (tc[], tmp[]: LDS scratch).
+// Work tiles of up to `tile` grouped pairs of one expert, in expert order,
+// from the per-expert counts c[] and offsets off[] (tc[], tmp[]: LDS scratch).
 __device__ inline void write_tiles(const int *c, const int *off, int E, int *tc, int *tmp, int32_t *tiles,
-                                   int32_t *ntiles) {
-  for (int e = threadIdx.x; e < E; e += kBlockTok) tc[e] = (c[e] + 15) / 16;
+                                   int32_t *ntiles, int tile) {
+  for (int e = threadIdx.x; e < E; e += kBlockTok) tc[e] = (c[e] + tile - 1) / tile;
   __syncthreads();
   const int total = block_exclusive_scan<kBlockTok>(tc, E, tmp);
   for (int e = threadIdx.x; e < E; e += kBlockTok)
-    for (int i = 0; 16 * i < c[e]; ++i)
-      reinterpret_cast<int4 *>(tiles)[tc[e] + i] = make_int4(e, off[e] + 16 * i, min(16, c[e] - 16 * i), 0);
+    for (int i = 0; tile * i < c[e]; ++i)
+      reinterpret_cast<int4 *>(tiles)[tc[e] + i] = make_int4(e, off[e] + tile * i, min(tile, c[e] - tile * i), 0);
   if (threadIdx.x == 0) *ntiles = total;
 }
 
@@ -135,7 +135,8 @@ template <int KM>
 __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *idx, int64_t T, int k, int E,
                                                                 int32_t *counts, int32_t *offsets,
                                                                 int32_t *sorted_token, int32_t *sorted_slot,
-                                                                int32_t *pos, int32_t *tiles, int32_t *ntiles) {
+                                                                int32_t *pos, int32_t *tiles, int32_t *ntiles,
+                                                                int tile) {
   __shared__ uint32_t bits[1024 * 8];
   __shared__ int cnt[1024], c0[1024], tc[1024];
   __shared__ int tmp[kBlockTok];
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kBlockTok) void group_fused_kernel(const int32_t *i
     scatter_block_r<KM>(bits, cnt, ch, T, k, E, 0, sorted_token, sorted_slot, pos);
   else
     scatter_block(bits, cnt, idx, T, k, E, 0, sorted_token, sorted_slot, pos);
-  if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles);
+  if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles, tile);
 }
 
 template <int KM>
@@ -177,16 +178,27 @@ __global__ __launch_bounds__(kBlockTok) void group_count_kernel(const int32_t *i
   for (int e = threadIdx.x; e < E; e += kBlockTok) bcount[(int64_t)blockIdx.x * E + e] = block_count(bits, e);
 }
 
+// Per expert, the block counts are read 16 blocks at a time, all 16 loads in
+// flight before the running sum is stored (stores to bbase may alias bcount as
+// far as the compiler knows, so a load after each store would wait for it).
 __global__ __launch_bounds__(kBlockTok) void group_scan_kernel(const int32_t *bcount, int nb, int E, int32_t *bbase,
                                                                int32_t *counts, int32_t *offsets, int32_t *tiles,
-                                                               int32_t *ntiles) {
+                                                               int32_t *ntiles, int tile) {
+  constexpr int B = 16;
   __shared__ int cnt[1024], c0[1024], tc[1024];
   __shared__ int tmp[kBlockTok];
   for (int e = threadIdx.x; e < E; e += kBlockTok) {
     int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      bbase[(int64_t)b * E + e] = run;
-      run += bcount[(int64_t)b * E + e];
+    for (int b0 = 0; b0 < nb; b0 += B) {
+      int c[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) c[u] = bcount[(int64_t)min(b0 + u, nb - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (b0 + u < nb) {
+          bbase[(int64_t)(b0 + u) * E + e] = run;
+          run += c[u];
+        }
     }
     cnt[e] = run;
     c0[e] = run;
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(kBlockTok) void group_scan_kernel(const int32_t *bc
   int total = block_exclusive_scan<kBlockTok>(cnt, E, tmp);
   for (int e = threadIdx.x; e < E; e += kBlockTok) offsets[e] = cnt[e];
   if (threadIdx.x == 0) offsets[E] = total;
-  if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles);
+  if (tiles) write_tiles(c0, cnt, E, tc, tmp, tiles, ntiles, tile);
 }
 
 template <int KM>
@@ -222,11 +234,11 @@ __global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t 
 template <int KM>
 static int launch_group_k(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos,
-                          const GroupWs &gw, int32_t *tiles, int32_t *ntiles) {
+                          const GroupWs &gw, int32_t *tiles, int32_t *ntiles, int tile) {
   const int64_t nb = cdiv(T, kBlockTok);
   if (nb <= 1) {
     TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_fused_kernel<KM>, dim3(1), dim3(kBlockTok), 0, st, idx, T, k, (int)E, counts,
-                offsets, sorted_token, sorted_slot, pos, tiles, ntiles);
+                offsets, sorted_token, sorted_slot, pos, tiles, ntiles, tile);
     TMOE_LAUNCHED("group_fused");
     return TMOE_OK;
   }
@@ -235,7 +247,7 @@ static int launch_group_k(hipStream_t st, const int32_t *idx, int64_t T, int k, 
               gw.bcount);
   TMOE_LAUNCHED("group_count");
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kBlockTok), 0, st, gw.bcount, (int)nb, (int)E, gw.bbase, counts,
-                     offsets, tiles, ntiles);
+                     offsets, tiles, ntiles, tile);
   TMOE_LAUNCHED("group_scan");
   hipLaunchKernelGGL(group_scatter_kernel<KM>, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E, offsets,
                      gw.bbase, sorted_token, sorted_slot, pos);
@@ -245,12 +257,15 @@ static int launch_group_k(hipStream_t st, const int32_t *idx, int64_t T, int k, 
 
 int launch_group(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts, int32_t *offsets,
                  int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos, const GroupWs &gw, int32_t *tiles,
-                 int32_t *ntiles) {
+                 int32_t *ntiles, int tile) {
+  if (tiles && tile < 1) return fail(TMOE_E_ARG, "tile size %d", tile);
   if (k <= 8)
-    return launch_group_k<8>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles);
+    return launch_group_k<8>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles,
+                             tile);
   if (k <= 16)
-    return launch_group_k<16>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles);
-  return launch_group_k<0>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles);
+    return launch_group_k<16>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles,
+                              tile);
+  return launch_group_k<0>(st, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos, gw, tiles, ntiles, tile);
 }
 
 }  // namespace tmoe

@@ -382,7 +382,7 @@ int tmoe_group_by_expert(void *stream, const int32_t *idx, int64_t T, int k, int
   REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), TMOE_E_WORKSPACE, "workspace needs %zu bytes",
           need);
   return launch_group((hipStream_t)stream, idx, T, k, E, counts, offsets, sorted_token, sorted_slot, pos,
-                      group_ws_carve(ws, T, k, E), nullptr, nullptr);
+                      group_ws_carve(ws, T, k, E), nullptr, nullptr, 16);
 }
 
 // --------------------------------------------------------------- expert FFN
@@ -545,8 +545,10 @@ int moe_forward_impl(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
   }
   rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup, rw);
   if (rc) return rc;
+  // the grouping also writes the work tiles of the expert kernels' form
+  const bool blocked = ffn_blocked(T * k, E, H, W->inter);
   rc = launch_group(st, idx, T, k, E, counts, offsets, st_tok, st_slot, pos, group_ws_carve(base + L.off_group, T, k, E),
-                    fw.tiles, fw.ntiles);
+                    blocked ? fw.blocks : fw.tiles, blocked ? fw.nblocks : fw.ntiles, blocked ? 64 : 16);
   if (rc) return rc;
   rc = launch_ffn(st, W, X, T, offsets, st_tok, o.clamp, O, nullptr, fw, true);
   if (rc) return rc;
