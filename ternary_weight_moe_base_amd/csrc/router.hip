@@ -64,15 +64,39 @@ RouterWs router_ws_carve(void *ws, int64_t T, int64_t E, int64_t H) {
 }
 
 // ------------------------------------------------------------ fp64 logits
-// Each lane keeps 4*NC router weights (elements c*256 + 4*lane + 0..3, loaded
-// by the caller as wv[c]) as fp64
-// and runs one FMA chain of 4*NC exact products per logit, then a 6-level
-// butterfly: depth 4*NC + 6, plus 1 for the bias. The same chain accumulates
-// A = sum |x w| for the bound. Results for token n go to lgs[n*4 + wave] and
-// abs_s[n*4 + wave] (LDS).
+// One token's chains over this lane's inputs (exact bf16 x fp32 products in
+// fp64): the logit sum and the sum of |x w| for the bound.
 template <int NC>
-__device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv)[NC], const float *bias, int64_t e,
-                                   int E, double *lgs, double *abs_s) {
+__device__ __forceinline__ void logit_chains(const uint2 *xr, const double (&w)[4 * NC], int lane, double &acc,
+                                             double &aab) {
+  acc = 0.0;
+  aab = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    uint2 xv = xr[c * 64 + lane];
+    const double x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xFFFF0000u);
+    const double x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xFFFF0000u);
+    acc = fma(w[4 * c], x0, acc);
+    acc = fma(w[4 * c + 1], x1, acc);
+    acc = fma(w[4 * c + 2], x2, acc);
+    acc = fma(w[4 * c + 3], x3, acc);
+    aab = fma(fabs(w[4 * c]), fabs(x0), aab);
+    aab = fma(fabs(w[4 * c + 1]), fabs(x1), aab);
+    aab = fma(fabs(w[4 * c + 2]), fabs(x2), aab);
+    aab = fma(fabs(w[4 * c + 3]), fabs(x3), aab);
+  }
+}
+
+// Each lane keeps 4*NC router weights (elements c*256 + 4*lane + 0..3, loaded
+// by the caller as wv[c]) as fp64 and runs one FMA chain of 4*NC exact
+// products per logit, then a 6-level butterfly: depth 4*NC + 6, plus 1 for the
+// bias (bv: the caller's bias value, used when bias is not null). The same
+// chain accumulates A = sum |x w| for the bound. Four tokens go together
+// (eight independent chains) when the chunk holds them. Results for token n go
+// to lgs[n*4 + wave] and abs_s[n*4 + wave] (LDS).
+template <int NC>
+__device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv)[NC], const float *bias, float bv,
+                                   int64_t e, int E, double *lgs, double *abs_s) {
   constexpr int H = NC * 256;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (e >= E) {
@@ -93,24 +117,29 @@ __device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv
     w[4 * c + 2] = v.z;
     w[4 * c + 3] = v.w;
   }
-  const double b = bias ? (double)bias[e] : 0.0;
-  for (int n = 0; n < nt; ++n) {
-    const uint2 *xr = reinterpret_cast<const uint2 *>(xs + (size_t)n * H);
-    double acc = 0.0, aab = 0.0;
+  const double b = bias ? (double)bv : 0.0;
+  int n = 0;
+  for (; n + 4 <= nt; n += 4) {
+    double acc[4], aab[4];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint2 xv = xr[c * 64 + lane];
-      const double x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xFFFF0000u);
-      const double x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xFFFF0000u);
-      acc = fma(w[4 * c], x0, acc);
-      acc = fma(w[4 * c + 1], x1, acc);
-      acc = fma(w[4 * c + 2], x2, acc);
-      acc = fma(w[4 * c + 3], x3, acc);
-      aab = fma(fabs(w[4 * c]), fabs(x0), aab);
-      aab = fma(fabs(w[4 * c + 1]), fabs(x1), aab);
-      aab = fma(fabs(w[4 * c + 2]), fabs(x2), aab);
-      aab = fma(fabs(w[4 * c + 3]), fabs(x3), aab);
+    for (int u = 0; u < 4; ++u)
+      logit_chains<NC>(reinterpret_cast<const uint2 *>(xs + (size_t)(n + u) * H), w, lane, acc[u], aab[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] = wave_sum_d(acc[u]);
+      aab[u] = wave_sum_d(aab[u]);
     }
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lgs[(n + u) * 4 + wave] = acc[u] + b;
+        abs_s[(n + u) * 4 + wave] = aab[u] + fabs(b);
+      }
+    }
+  }
+  for (; n < nt; ++n) {
+    double acc, aab;
+    logit_chains<NC>(reinterpret_cast<const uint2 *>(xs + (size_t)n * H), w, lane, acc, aab);
     acc = wave_sum_d(acc);
     aab = wave_sum_d(aab);
     if (lane == 0) {
@@ -119,7 +148,6 @@ __device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv
     }
   }
 }
-
 __device__ inline void stage_x(uint16_t *xs, const uint16_t *X, int64_t t0, int nt, int H) {
   const int vpr = H / 8;
   copy16<256>(
@@ -146,9 +174,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *X, i
   float4 wv[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) wv[c] = wrow[c * 64 + (threadIdx.x & 63)];
+  const float bv = (bias ? bias : Wr)[min<int64_t>(e, E - 1)];  // unused without a bias
   stage_x(xs, X, t0, nt, NC * 256);
   __syncthreads();
-  logits_rows<NC>(xs, nt, wv, bias, e, (int)E, lgs, abs_s);
+  logits_rows<NC>(xs, nt, wv, bias, bv, e, (int)E, lgs, abs_s);
   __syncthreads();
   for (int i = threadIdx.x; i < nt * 4; i += 256) {
     const int n = i >> 2, q = i & 3;
