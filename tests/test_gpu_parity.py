@@ -661,7 +661,9 @@ def test_layer_empty_batch(tm, layers):
 
 def test_stack_teacher_forced(tm, layers):
     # 24-layer stack workload, first layers: the oracle's layer l consumes the
-    # GPU's residual stream X_l (teacher forcing) on sampled tokens
+    # GPU's residual stream X_l (teacher forcing); Y of layer 1 on every one of
+    # the 256 tokens (grouped oracle experts), and two tokens of each layer
+    # through the oracle's per-token loop
     cfg, T = 5, 256
     xb = ti.activations(cfg, T)
     for layer in range(2):
@@ -678,6 +680,13 @@ def test_stack_teacher_forced(tm, layers):
         # the residual stream is bf16(x + y) of the GPU's own y
         assert np.array_equal(xn, O.residual_bf16(xb, Yh))
         x = O.bf16_to_f64(xb)
+        if layer == 1:  # the layer fed by the GPU's own residual stream: every token
+            _, offsets, st, _, pos = O.group_by_expert(ridx, 256)
+            _prefetch_experts(cfg, layer, range(256))
+            Oref = _grouped_ffn_reference(cfg, layer, x, st, offsets, (7.0,))[7.0][1]
+            err = O.max_normalized_error(Yh, O.combine(Oref, rw, pos))
+            say(f"  stack layer {layer}: Y max normalized error over all {T} tokens {err:.2e}")
+            assert err <= TOL
         for t in (3, 200):
             y = np.zeros(2048)
             for j in range(8):
