@@ -834,15 +834,11 @@ __device__ __forceinline__ int tb_after_act(int s, int nj, int F) {
   return n;
 }
 
-template <int F>
-__global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) {
-  extern __shared__ __align__(16) char xs[];  // [kTbDepth][kTbStepBytes]
-  __shared__ uint32_t wmaxs[kTbWaves][64];
-  const int blk = blockIdx.x;
-  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
-  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
-  const int e = td.x, start = td.y;
-  const int nb = td.z;  // pairs of this block (<= 64)
+// NT: token tiles of the block that hold pairs (the block's last tiles past
+// its pairs are neither loaded nor multiplied).
+template <int F, int NT>
+__device__ __forceinline__ void gateup_tb_body(const GateUpArgs &a, char *xs, uint32_t (*wmaxs)[64], int e,
+                                               int start, int nb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int rt0 = (blockIdx.y * kTbWaves + wave) * kTbR;  // row tiles rt0 .. rt0 + kTbR - 1
@@ -861,10 +857,10 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
     }                                                                                                        \
   } while (0)
 
-  // this wavefront's activation load instructions of a step: j = wave, wave + 8, wave + 16 (< 20),
+  // this wavefront's activation load instructions of a step: j = wave, wave + 8, wave + 16 (< 5 NT),
   // j = (token tile, slice m); lane (g, n) fetches 16 B of column n, quarter g
-  constexpr int NJ = 3;
-  const int nj = wave + 16 < 20 ? 3 : 2;
+  constexpr int NJ = (5 * NT + kTbWaves - 1) / kTbWaves;
+  const int nj = (wave < 5 * NT) + (wave + 8 < 5 * NT) + (wave + 16 < 5 * NT);
   const uint16_t *srow[NJ];
   int kq[NJ];
 #pragma unroll
@@ -901,11 +897,11 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
     su[r] = *reinterpret_cast<const float4 *>(a.up_s + (int64_t)e * a.I + row0);
   }
 
-  f32x4 accg[kTbR][4], accu[kTbR][4];
+  f32x4 accg[kTbR][NT], accu[kTbR][NT];
 #pragma unroll
   for (int r = 0; r < kTbR; ++r)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
       accg[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       accu[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -925,13 +921,13 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
     const char *buf = xs + (s % kTbDepth) * kTbStepBytes + (g * 16 + n) * 16;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
-      u32x4 bx[4];
+      u32x4 bx[NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bx[t] = lds16(buf + (t * 5 + m) * 1024);
+      for (int t = 0; t < NT; ++t) bx[t] = lds16(buf + (t * 5 + m) * 1024);
 #pragma unroll
       for (int r = 0; r < kTbR; ++r)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NT; ++t) {
           accg[r][t] = mfma_bf16(pg[r] + 4 * m, bx[t], accg[r][t]);
           accu[r][t] = mfma_bf16(pu[r] + 4 * m, bx[t], accu[r][t]);
         }
@@ -941,9 +937,9 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
 #undef TB_WLOAD
 #undef TB_ALOAD
 
-  uint32_t mx[4];
+  uint32_t mx[NT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
     mx[t] = 0u;
     const int col = 16 * t + n;
 #pragma unroll
@@ -959,7 +955,7 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
   }
   if (g == 0) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wmaxs[wave][16 * t + n] = mx[t];
+    for (int t = 0; t < NT; ++t) wmaxs[wave][16 * t + n] = mx[t];
   }
   __syncthreads();
   if (threadIdx.x < nb) {
@@ -967,6 +963,23 @@ __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) 
 #pragma unroll
     for (int w = 0; w < kTbWaves; ++w) m = max(m, wmaxs[w][threadIdx.x]);
     a.hmax[(int64_t)(start + threadIdx.x) * kTbMaxGroups + blockIdx.y] = m;
+  }
+}
+
+template <int F>
+__global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) {
+  extern __shared__ __align__(16) char xs[];  // [kTbDepth][kTbStepBytes]
+  __shared__ uint32_t wmaxs[kTbWaves][64];
+  const int blk = blockIdx.x;
+  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
+  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
+  const int e = td.x, start = td.y;
+  const int nb = td.z;  // pairs of this block (1..64)
+  switch ((nb + 15) >> 4) {
+    case 1: gateup_tb_body<F, 1>(a, xs, wmaxs, e, start, nb); break;
+    case 2: gateup_tb_body<F, 2>(a, xs, wmaxs, e, start, nb); break;
+    case 3: gateup_tb_body<F, 3>(a, xs, wmaxs, e, start, nb); break;
+    default: gateup_tb_body<F, 4>(a, xs, wmaxs, e, start, nb); break;
   }
 }
 
@@ -1124,31 +1137,27 @@ __device__ __forceinline__ void dtb_load(const DownArgs &a, int e, int rt, int l
 // accumulator, then the lo parts (so no two consecutive products share an
 // accumulator). All four token tiles run (straight-line code schedules the
 // LDS reads ahead of the products); columns past the block read its last pair.
-template <int NW>
-__device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, const char *const bq[4], int plane,
-                                          int off, f32x4 (*acc)[4]) {
-  u32x4 b[2][4];
+template <int NT, int NW>
+__device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, const char *const bq[NT], int plane,
+                                          int off, f32x4 (*acc)[NT]) {
+  u32x4 b[2][NT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
     b[0][t] = lds16(bq[t] + off);
     b[1][t] = lds16(bq[t] + plane + off);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < kDtbR; ++r) acc[r][t] = mfma_f16(pw[r] + w0, b[q][t], acc[r][t]);
 }
 
-template <int F, int RT>
-__global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
-  extern __shared__ __align__(16) char smem[];  // [2][64][rs]: the hi and lo planes
-  __shared__ int sig[64];
-  const int blk = blockIdx.x;
-  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
-  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
-  const int e = td.x, start = td.y, nb = td.z;
+// NT: token tiles multiplied (those past the block's pairs read its last pair
+// and are not stored).
+template <int F, int RT, int NT>
+__device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int *sig, int e, int start, int nb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   constexpr int M = 5 * F + tail_mfmas(RT);
@@ -1163,16 +1172,16 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
                                    a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig);
   __syncthreads();
 
-  const char *bq[4];
+  const char *bq[NT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) bq[t] = smem + min(16 * t + n, nb - 1) * rs + g * M * 16;
+  for (int t = 0; t < NT; ++t) bq[t] = smem + min(16 * t + n, nb - 1) * rs + g * M * 16;
 #pragma unroll 1
   for (int it = 0; it < per_wave; it += kDtbR) {
-    f32x4 acc[kDtbR][4];
+    f32x4 acc[kDtbR][NT];
 #pragma unroll
     for (int r = 0; r < kDtbR; ++r)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float4 sd[kDtbR];
 #pragma unroll
     for (int r = 0; r < kDtbR; ++r) sd[r] = cur.sd[r];
@@ -1185,7 +1194,7 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
       for (int r = 0; r < kDtbR; ++r) unpack_tail<RT>(cur.dw[r], cur.sh[r], pw[r]);
 #pragma unroll
       for (int m = 0; m < tail_mfmas(RT); ++m) {
-        dtb_slice(pw, 4 * m, bq, plane, (5 * F + m) * 16, acc);
+        dtb_slice<NT>(pw, 4 * m, bq, plane, (5 * F + m) * 16, acc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1197,12 +1206,12 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
       if (s == F - 1 && it + kDtbR < per_wave) dtb_load<F, RT>(a, e, rt0 + it + kDtbR, lane, cur);
 #pragma unroll
       for (int m = 0; m < 5; ++m) {
-        dtb_slice(pw, 4 * m, bq, plane, (5 * s + m) * 16, acc);
+        dtb_slice<NT>(pw, 4 * m, bq, plane, (5 * s + m) * 16, acc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int col = 16 * t + n;
       if (col >= nb) continue;
       const int us = -1 - sig[col];  // the trits entered as 2t, h as 2^sig h
@@ -1219,6 +1228,19 @@ __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
       }
     }
   }
+}
+
+template <int F, int RT>
+__global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
+  extern __shared__ __align__(16) char smem[];  // [2][64][rs]: the hi and lo planes
+  __shared__ int sig[64];
+  const int blk = blockIdx.x;
+  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
+  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
+  const int e = td.x, start = td.y, nb = td.z;  // nb: 1..64 pairs
+  // all four token tiles (a form per live-tile count would need more than
+  // the 256 registers two wavefronts per SIMD leave each one)
+  down_tb_body<F, RT, 4>(a, smem, sig, e, start, nb);
 }
 
 // ------------------------------------------------- down + combine (decode)
