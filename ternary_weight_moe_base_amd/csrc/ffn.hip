@@ -815,21 +815,24 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 // Vector-memory loads issued after step s's activation loads, at the wait of
 // step s. Issue order: prologue W(0..kTbWDepth-1), A(0..kTbDepth-2); then in
-// step i: A(i + kTbDepth - 1), W(i + kTbWDepth) while they exist. A(s) = nj
-// loads, W(s) = 2 kTbR loads.
+// step i: W(i + kTbWDepth), the wait and the barrier, A(i + kTbDepth - 1),
+// each while it exists. A(s) = nj loads, W(s) = 2 kTbR loads.
 __device__ __forceinline__ int tb_after_act(int s, int nj, int F) {
   constexpr int WL = 2 * kTbR;
   int n = 0;
-  if (s <= kTbDepth - 2) {
-    n += (kTbDepth - 2 - s) * nj;
-  } else {
-    const int i = s - (kTbDepth - 1);  // the step that issued A(s)
-    if (i + kTbWDepth < F) n += WL;
+  bool issued = false;  // A(s) already issued at this point of the order
+  for (int t = 0; t <= kTbDepth - 2; ++t) {
+    if (issued) n += nj;
+    if (t == s) issued = true;
   }
-  const int i0 = s <= kTbDepth - 2 ? 0 : s - (kTbDepth - 2);
-  for (int i = i0; i <= s; ++i) {
-    if (i + kTbDepth - 1 < F) n += nj;
-    if (i + kTbWDepth < F) n += WL;
+  for (int i = 0; i <= s; ++i) {
+    if (issued && i + kTbWDepth < F) n += WL;
+    if (i == s) break;
+    const int t = i + kTbDepth - 1;
+    if (t < F) {
+      if (issued) n += nj;
+      if (t == s) issued = true;
+    }
   }
   return n;
 }
@@ -907,7 +910,6 @@ __device__ __forceinline__ void gateup_tb_body(const GateUpArgs &a, char *xs, ui
     }
 #pragma unroll
   for (int s = 0; s < F; ++s) {
-    if (s + kTbDepth - 1 < F) TB_ALOAD(s + kTbDepth - 1);
     uint32_t pg[kTbR][20], pu[kTbR][20];
 #pragma unroll
     for (int r = 0; r < kTbR; ++r) {
@@ -915,9 +917,12 @@ __device__ __forceinline__ void gateup_tb_body(const GateUpArgs &a, char *xs, ui
       unpack8(wu[s % kTbWDepth][r], pu[r]);
     }
     if (s + kTbWDepth < F) TB_WLOAD(s + kTbWDepth);
-    // this wavefront's activation loads of step s, then everyone's
+    // this wavefront's activation loads of step s, then everyone's; past the
+    // barrier every wavefront has also finished its LDS reads of step s - 1,
+    // whose buffer the next issue refills
     wait_vm(tb_after_act(s, nj, F));
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
+    if (s + kTbDepth - 1 < F) TB_ALOAD(s + kTbDepth - 1);
     const char *buf = xs + (s % kTbDepth) * kTbStepBytes + (g * 16 + n) * 16;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
@@ -932,7 +937,6 @@ __device__ __forceinline__ void gateup_tb_body(const GateUpArgs &a, char *xs, ui
           accu[r][t] = mfma_bf16(pu[r] + 4 * m, bx[t], accu[r][t]);
         }
     }
-    lds_barrier();  // the buffer of step s is refilled by a later issue
   }
 #undef TB_WLOAD
 #undef TB_ALOAD
