@@ -19,6 +19,14 @@
 //       a plain 16-byte-per-lane device copy of M MiB: the known-size kernel
 //       that calibrates hardware byte counters; with --host-experts 1 the
 //       source is pinned host memory (the host link's read rate).
+//   tmoe_run issue
+//       issue cost, in core-clock cycles per wavefront instruction and per
+//       SIMD, of the instruction kinds the trit decode and the products are
+//       made of (eight independent chains per wavefront, one and four
+//       wavefronts per SIMD), of one product followed by V decode
+//       instructions (whether the two overlap), and the core clock while
+//       every SIMD of the chip issues packed fp16 FMAs: the figures that
+//       turn a kernel's instruction counts into its issue-bound time.
 //
 // Model shape: hidden 2048, 256 experts, top-8, moe_intermediate 512 (the
 // Maple-Preview configuration as the jj-blog architecture section and
@@ -83,6 +91,70 @@ __global__ void to_bf16_kernel(const float *__restrict__ src, uint16_t *__restri
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const uint32_t u = __float_as_uint(src[i]);
     dst[i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+
+// ------------------------------------------------------------ issue costs
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kIssueKinds = 9;
+const char *const kIssueNames[kIssueKinds] = {"v_pk_fma_f16", "v_pk_mad_u16", "v_pk_mul_lo_u16", "v_perm_b32",
+                                              "v_add_u32",    "v_and_b32",    "v_lshlrev_b32",   "v_mov_b32",
+                                              "v_fma_f32"};
+
+// one instruction of kind KIND on x (ALU only)
+template <int KIND>
+__device__ __forceinline__ void issue_op(uint32_t &x, uint32_t k, uint32_t c) {
+  if constexpr (KIND == 0) asm volatile("v_pk_fma_f16 %0, %0, %1, %2" : "+v"(x) : "s"(k), "v"(c));
+  else if constexpr (KIND == 1) asm volatile("v_pk_mad_u16 %0, %0, %1, %2" : "+v"(x) : "s"(k), "v"(c));
+  else if constexpr (KIND == 2) asm volatile("v_pk_mul_lo_u16 %0, %0, %1" : "+v"(x) : "s"(k));
+  else if constexpr (KIND == 3) asm volatile("v_perm_b32 %0, %1, %0, %2" : "+v"(x) : "s"(k), "v"(c));
+  else if constexpr (KIND == 4) asm volatile("v_add_u32 %0, %0, %1" : "+v"(x) : "v"(c));
+  else if constexpr (KIND == 5) asm volatile("v_and_b32 %0, %0, %1" : "+v"(x) : "v"(c));
+  else if constexpr (KIND == 6) asm volatile("v_lshlrev_b32 %0, 14, %0" : "+v"(x));
+  else if constexpr (KIND == 7) asm volatile("v_mov_b32 %0, %1" : "+v"(x) : "v"(c));
+  else asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x) : "s"(k), "v"(c));
+}
+
+// out[wave slot] = cycles of the timed loop, out[16384 + slot] = 100 MHz ticks
+// of it; out[32768 + thread] keeps the chains live. The buffer holds
+// 32768 + gridDim.x * blockDim.x words, gridDim.x <= 1024, blockDim.x <= 1024.
+// MFMA: per unrolled step, MF products (four accumulators in turn) and V
+// instructions of kind KIND.
+template <int KIND, int V, int MF>
+__global__ __launch_bounds__(1024) void issue_kernel(uint32_t *out, int iters, uint32_t k) {
+  uint32_t a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = threadIdx.x + j;
+  const uint32_t c = threadIdx.x ^ 0x1234u;
+  bf16x8_t A, B;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    A[j] = (__bf16)(float)(threadIdx.x & 7);
+    B[j] = (__bf16)(float)j;
+  }
+  f32x4_t acc[4] = {};
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int m = 0; m < MF; ++m) acc[m & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[m & 3], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < V; ++v) issue_op<KIND>(a[v & 7], k, c);
+    }
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r ^= a[j];
+  const f32x4_t sacc = acc[0] + acc[1] + acc[2] + acc[3];
+  out[32768 + blockIdx.x * blockDim.x + threadIdx.x] = r ^ __float_as_uint(sacc[0] + sacc[1] + sacc[2] + sacc[3]);
+  if ((threadIdx.x & 63) == 0) {
+    const int slot = blockIdx.x * 16 + (threadIdx.x >> 6);
+    out[slot] = (uint32_t)(c1 - c0);
+    out[16384 + slot] = (uint32_t)(r1 - r0);
   }
 }
 
@@ -259,6 +331,65 @@ int run_copy(const Args &a, hipStream_t st) {
   return 0;
 }
 
+// Cycles per instruction per SIMD, the largest over the wavefronts of one
+// workgroup on one CU (64 threads: one wavefront per SIMD in use; 1024: four).
+template <int KIND, int V, int MF>
+double issue_cycles(uint32_t *d, std::vector<uint32_t> &h, int threads, int iters, double per_step) {
+  issue_kernel<KIND, V, MF><<<1, threads>>>(d, iters, 0x35553555u);
+  CHECK_HIP(hipGetLastError());
+  CHECK_HIP(hipDeviceSynchronize());
+  CHECK_HIP(hipMemcpy(h.data(), d, 16 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+  uint32_t mx = 0;
+  for (int w = 0; w < threads / 64; ++w) mx = h[w] > mx ? h[w] : mx;
+  const double waves_per_simd = threads >= 256 ? threads / 256.0 : 1.0;
+  return (double)mx / (iters * 4.0 * per_step) / waves_per_simd;
+}
+
+template <int KIND>
+void issue_row(uint32_t *d, std::vector<uint32_t> &h) {
+  const double c1 = issue_cycles<KIND, 8, 0>(d, h, 64, 2000, 8), c4 = issue_cycles<KIND, 8, 0>(d, h, 1024, 2000, 8);
+  std::printf("  %-22s %8.2f %8.2f\n", kIssueNames[KIND], c1, c4);
+}
+
+int run_issue() {
+  uint32_t *d = dalloc<uint32_t>(32768 + 1024 * 1024);
+  std::vector<uint32_t> h(32768);
+  std::printf("issue cost, cycles per wavefront instruction per SIMD (8 independent chains per wavefront)\n");
+  std::printf("  %-22s %8s %8s\n", "instruction", "1 wave", "4 waves");
+  issue_row<0>(d, h);
+  issue_row<1>(d, h);
+  issue_row<2>(d, h);
+  issue_row<3>(d, h);
+  issue_row<4>(d, h);
+  issue_row<5>(d, h);
+  issue_row<6>(d, h);
+  issue_row<7>(d, h);
+  issue_row<8>(d, h);
+  std::printf("  %-22s %8.2f %8.2f\n", "v_mfma_f32_16x16x32_bf16", issue_cycles<0, 0, 4>(d, h, 64, 1000, 4),
+              issue_cycles<0, 0, 4>(d, h, 1024, 1000, 4));
+  std::printf("one product + V v_pk_fma_f16, cycles per step per SIMD (4 waves): additive if = mfma + V x fma\n");
+  std::printf("  V = 4: %.2f   V = 8: %.2f   V = 12: %.2f   V = 24: %.2f\n", issue_cycles<0, 4, 1>(d, h, 1024, 1000, 1),
+              issue_cycles<0, 8, 1>(d, h, 1024, 1000, 1), issue_cycles<0, 12, 1>(d, h, 1024, 1000, 1),
+              issue_cycles<0, 24, 1>(d, h, 1024, 1000, 1));
+  // the core clock under a chip-wide packed fp16 FMA load
+  const int wgs = 1024;
+  issue_kernel<0, 8, 0><<<wgs, 1024>>>(d, 4000, 0x35553555u);
+  CHECK_HIP(hipGetLastError());
+  CHECK_HIP(hipDeviceSynchronize());
+  CHECK_HIP(hipMemcpy(h.data(), d, 32768 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+  double ghz_sum = 0.0;
+  int nw = 0;
+  for (int i = 0; i < wgs * 16; ++i)
+    if (h[16384 + i] > 0) {
+      ghz_sum += 0.1 * h[i] / h[16384 + i];
+      ++nw;
+    }
+  std::printf("core clock under a chip-wide v_pk_fma_f16 load: %.3f GHz (mean over %d wavefronts)\n",
+              nw ? ghz_sum / nw : 0.0, nw);
+  CHECK_HIP(hipFree(d));
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char **argv) {
@@ -269,7 +400,8 @@ int main(int argc, char **argv) {
   if (a.mode == "layer") rc = run_layer(a, st);
   else if (a.mode == "lmhead") rc = run_lmhead(a, st);
   else if (a.mode == "copy") rc = run_copy(a, st);
-  else std::fprintf(stderr, "unknown mode %s (layer | lmhead | copy)\n", a.mode.c_str());
+  else if (a.mode == "issue") rc = run_issue();
+  else std::fprintf(stderr, "unknown mode %s (layer | lmhead | copy | issue)\n", a.mode.c_str());
   CHECK_HIP(hipStreamSynchronize(st));
   CHECK_HIP(hipStreamDestroy(st));
   std::fflush(stdout);
