@@ -794,6 +794,31 @@ __global__ __launch_bounds__(64 * NW) void gateup_kernel(GateUpArgs a) {
 // ahead of their use. The epilogue also writes, per pair, the largest |h| of
 // the workgroup's rows (hmax[pair][row group]), which the down projection
 // uses to pick the pair's scale.
+// Work item of a token-blocked kernel: a 64-pair block and a row group. The
+// grid is 1-D, 8 * groups * ceil(max blocks / 8) workgroups; the dispatcher
+// hands consecutive workgroups to the eight XCDs in turn, so XCD x runs
+// workgroups x, x + 8, x + 16, ... It gets blocks x * per .. x * per + per - 1
+// (per = ceil(nblk / 8)) in order, the row groups of each block one after
+// another: the row groups of a block (the same activations) and the blocks of
+// one expert (the same weights) run on one XCD close together in time and
+// share its L2. blk = nblk: no work.
+struct TbItem {
+  int blk, grp;
+};
+__device__ __forceinline__ TbItem tb_item(int nblk, int groups) {
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int per = (nblk + 7) >> 3;
+  const int b = j / groups;
+  TbItem it;
+  it.grp = j - b * groups;
+  it.blk = b < per ? min(x * per + b, nblk) : nblk;
+  return it;
+}
+// workgroups of a token-blocked launch
+static inline unsigned tb_grid(int64_t max_blocks, int groups) {
+  return (unsigned)(8 * groups * ((max_blocks + 7) / 8));
+}
+
 constexpr int kTbWaves = 8, kTbR = 2, kTbDepth = 4, kTbWDepth = 3, kTbStepBytes = 4 * 5 * 64 * 16;
 constexpr int kTbRows = 16 * kTbWaves * kTbR;  // intermediate rows per workgroup
 constexpr int kTbMaxGroups = kTbMaxGroupsH;   // row groups per pair kept in hmax
@@ -841,10 +866,10 @@ __device__ __forceinline__ int tb_after_act(int s, int nj, int F) {
 // its pairs are neither loaded nor multiplied).
 template <int F, int NT>
 __device__ __forceinline__ void gateup_tb_body(const GateUpArgs &a, char *xs, uint32_t (*wmaxs)[64], int e,
-                                               int start, int nb) {
+                                               int start, int nb, int grp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int rt0 = (blockIdx.y * kTbWaves + wave) * kTbR;  // row tiles rt0 .. rt0 + kTbR - 1
+  const int rt0 = (grp * kTbWaves + wave) * kTbR;  // row tiles rt0 .. rt0 + kTbR - 1
   constexpr int Q5 = 5 * 8 * F;  // inputs per quarter (H = 2048: 520)
   const int K = (int)a.gx.K;
 
@@ -966,7 +991,7 @@ __device__ __forceinline__ void gateup_tb_body(const GateUpArgs &a, char *xs, ui
     uint32_t m = 0u;
 #pragma unroll
     for (int w = 0; w < kTbWaves; ++w) m = max(m, wmaxs[w][threadIdx.x]);
-    a.hmax[(int64_t)(start + threadIdx.x) * kTbMaxGroups + blockIdx.y] = m;
+    a.hmax[(int64_t)(start + threadIdx.x) * kTbMaxGroups + grp] = m;
   }
 }
 
@@ -974,16 +999,17 @@ template <int F>
 __global__ __launch_bounds__(64 * kTbWaves) void gateup_tb_kernel(GateUpArgs a) {
   extern __shared__ __align__(16) char xs[];  // [kTbDepth][kTbStepBytes]
   __shared__ uint32_t wmaxs[kTbWaves][64];
-  const int blk = blockIdx.x;
-  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
-  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
+  const int nblk = *a.ntiles;  // here: the 64-pair blocks
+  const TbItem it = tb_item(nblk, a.I / kTbRows);
+  if (it.blk >= nblk) return;
+  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[it.blk];
   const int e = td.x, start = td.y;
   const int nb = td.z;  // pairs of this block (1..64)
   switch ((nb + 15) >> 4) {
-    case 1: gateup_tb_body<F, 1>(a, xs, wmaxs, e, start, nb); break;
-    case 2: gateup_tb_body<F, 2>(a, xs, wmaxs, e, start, nb); break;
-    case 3: gateup_tb_body<F, 3>(a, xs, wmaxs, e, start, nb); break;
-    default: gateup_tb_body<F, 4>(a, xs, wmaxs, e, start, nb); break;
+    case 1: gateup_tb_body<F, 1>(a, xs, wmaxs, e, start, nb, it.grp); break;
+    case 2: gateup_tb_body<F, 2>(a, xs, wmaxs, e, start, nb, it.grp); break;
+    case 3: gateup_tb_body<F, 3>(a, xs, wmaxs, e, start, nb, it.grp); break;
+    default: gateup_tb_body<F, 4>(a, xs, wmaxs, e, start, nb, it.grp); break;
   }
 }
 
@@ -1161,14 +1187,15 @@ __device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, cons
 // NT: token tiles multiplied (those past the block's pairs read its last pair
 // and are not stored).
 template <int F, int RT, int NT>
-__device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int *sig, int e, int start, int nb) {
+__device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int *sig, int e, int start, int nb,
+                                             int grp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   constexpr int M = 5 * F + tail_mfmas(RT);
   const int rs = lds_row_bytes(a.slots);
   const int plane = 64 * rs;
   const int per_wave = a.H / 16 / kDtbGroups / kDtbWaves;  // row tiles of this wavefront
-  const int rt0 = blockIdx.y * (a.H / 16 / kDtbGroups) + wave * per_wave;
+  const int rt0 = grp * (a.H / 16 / kDtbGroups) + wave * per_wave;
 
   DtbWeights<F, RT> cur;
   dtb_load<F, RT>(a, e, rt0, lane, cur);
@@ -1238,13 +1265,14 @@ template <int F, int RT>
 __global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
   extern __shared__ __align__(16) char smem[];  // [2][64][rs]: the hi and lo planes
   __shared__ int sig[64];
-  const int blk = blockIdx.x;
-  if (blk >= *a.ntiles) return;  // here: the 64-pair blocks
-  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[blk];
+  const int nblk = *a.ntiles;  // here: the 64-pair blocks
+  const TbItem it = tb_item(nblk, kDtbGroups);
+  if (it.blk >= nblk) return;
+  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[it.blk];
   const int e = td.x, start = td.y, nb = td.z;  // nb: 1..64 pairs
   // all four token tiles (a form per live-tile count would need more than
   // the 256 registers two wavefronts per SIMD leave each one)
-  down_tb_body<F, RT, 4>(a, smem, sig, e, start, nb);
+  down_tb_body<F, RT, 4>(a, smem, sig, e, start, nb, it.grp);
 }
 
 // ------------------------------------------------- down + combine (decode)
@@ -1971,7 +1999,7 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     const size_t lds = (size_t)kTbDepth * kTbStepBytes;
     rc = allow_lds<gateup_tb_kernel<13>>(lds);
     if (rc) return rc;
-    TMOE_LAUNCH(TMOE_KERNEL_GATEUP, gateup_tb_kernel<13>, dim3((unsigned)ffn_max_blocks(P, E), (unsigned)(I / kTbRows)),
+    TMOE_LAUNCH(TMOE_KERNEL_GATEUP, gateup_tb_kernel<13>, dim3(tb_grid(ffn_max_blocks(P, E), (int)(I / kTbRows))),
                 dim3(64 * kTbWaves), lds, st, gb);
     TMOE_LAUNCHED("gateup_tb");
   } else if (P <= 64)
@@ -2002,7 +2030,7 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     const size_t lds = (size_t)2 * 64 * lds_row_bytes(gi.slots);
     rc = allow_lds<down_tb_kernel<3, 2>>(lds);
     if (rc) return rc;
-    TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_tb_kernel<3, 2>), dim3((unsigned)ffn_max_blocks(P, E), (unsigned)kDtbGroups),
+    TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_tb_kernel<3, 2>), dim3(tb_grid(ffn_max_blocks(P, E), kDtbGroups)),
                 dim3(64 * kDtbWaves), lds, st, da);
     TMOE_LAUNCHED("down_tb");
     return TMOE_OK;
