@@ -13,6 +13,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt not waited)
+#define TMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family parts
+constexpr int kBufWord3 = 0x00020000;
+
 // 16 bytes from LDS (one matrix-core operand of a lane)
 __device__ __forceinline__ u32x4 lds16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
 

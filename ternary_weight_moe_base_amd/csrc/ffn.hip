@@ -30,10 +30,6 @@
 
 namespace tmoe {
 
-// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt not waited)
-#define TMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family parts
-constexpr int kBufWord3 = 0x00020000;
 
 // ---------------------------------------------------------- trit decoding
 __device__ __forceinline__ uint32_t fma16x2(uint32_t a, uint32_t b, uint32_t c) {

@@ -352,20 +352,38 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *Wr, cons
 // Logits pass, a bf16 GEMM: workgroup = 4 wavefronts over a tile of 128
 // router rows x 128 tokens and one of SK slices of the inputs; wavefront
 // (we, wt) takes rows e0 + 64 we .. + 63 (4 row tiles of 16) and tokens
-// t0 + 64 wt .. + 63 (4 token tiles). Each K step of 32 inputs is staged in
-// LDS (parts w1, w2 of the 128 rows and the 128 token rows, 80-byte rows so
-// that 16 lanes reading 16 bytes of 16 rows hit distinct banks), the next
-// step's loads in flight while the current one is multiplied; per step a
-// wavefront runs 4 x 4 tiles x 2 parts products, w1 and w2 of a tile into one
-// fp32 accumulator. part[sk][t][e] = the slice's sum (fp32). Rows past E and
-// tokens past T read a valid row and are not stored.
-constexpr int kRgRow = 80;  // LDS bytes per staged row of 32 inputs
+// t0 + 64 wt .. + 63 (4 token tiles). Each K step of 32 inputs (parts w1, w2
+// of the 128 rows and the 128 token rows: 384 rows of 64 B) goes from memory
+// straight into LDS by buffer loads (no registers), kRgStages - 1 steps ahead
+// of its products. A staged row holds its four 16-byte chunks in the order
+// c ^ ((row >> 2) & 3), so the 16 lanes that read one chunk of 16 consecutive
+// rows hit 16 distinct groups of four banks. One barrier per step: past it
+// every wavefront's loads of the step have landed and every wavefront has
+// finished its reads of the previous step, whose buffer the loads issued next
+// refill. Per step a wavefront runs 4 x 4 tiles x 2 parts products, w1 and w2
+// of a tile into one fp32 accumulator. part[sk][t][e] = the slice's sum
+// (fp32). Rows past E and tokens past T read a valid row and are not stored.
+constexpr int kRgStages = 6;            // staged K steps (kRgStages - 1 in flight ahead)
+constexpr int kRgStage = 384 * 64;      // bytes per staged step
+constexpr int kRgLoads = 384 * 4 / 256;  // 16-byte loads per thread per step (6)
+
+// s_waitcnt vmcnt(n) for n = kRgLoads * m, m = 0 .. kRgStages - 2
+__device__ __forceinline__ void rg_wait(int m) {
+  switch (m) {
+    case 0: TMOE_WAIT_VM(0); break;
+    case 1: TMOE_WAIT_VM(kRgLoads); break;
+    case 2: TMOE_WAIT_VM(2 * kRgLoads); break;
+    case 3: TMOE_WAIT_VM(3 * kRgLoads); break;
+    default: TMOE_WAIT_VM(4 * kRgLoads); break;
+  }
+}
+static_assert(kRgStages - 2 <= 4, "rg_wait covers up to four later steps");
+
 template <int SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void router_gemm_kernel(const uint16_t *X, int64_t T, const uint16_t *parts, int E,
                                                           int H, int neb, float *part) {
-  extern __shared__ __align__(16) char lds[];  // [2][(256 + 128) rows][80 B]
-  constexpr int STAGE = 384 * kRgRow;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  extern __shared__ __align__(16) char lds[];  // [kRgStages][384 rows][64 B]
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int we = wave & 1, wt = wave >> 1;
   const int sk = blockIdx.x % SK, tile = blockIdx.x / SK;
   const int eb = tile % neb, tb = tile / neb;
@@ -373,43 +391,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int64_t t0 = (int64_t)tb * 128;
   const int nstep = H / 32 / SK;
   const int kbase = sk * nstep * 32;
-  const size_t plane = (size_t)E * H;
-  // staging: thread handles P chunks i = tid + 256 u (u < 4) and X chunks i = tid + 256 u (u < 2)
-  const uint16_t *gp[4];
-  const uint16_t *gx[2];
-  int lp[4], lx[2];
+  // load instruction u of this wavefront fills LDS chunks 64 (kRgLoads wave + u) + lane of a step:
+  // staged row (chunks / 4) < 256 are router rows (w1: 0..127, w2: 128..255), the rest token rows
+  const int ntok = (int)min<int64_t>(128, T - t0);
+  const __amdgpu_buffer_rsrc_t rp =
+      __builtin_amdgcn_make_buffer_rsrc((void *)parts, (short)0, (int)((int64_t)2 * E * H * 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(X + t0 * H), (short)0, ntok * H * 2, kBufWord3);
+  int voff[kRgLoads];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = threadIdx.x + 256 * u, row = i >> 2, c = i & 3;
-    const int q = row >> 7, e = min(e0 + (row & 127), E - 1);
-    gp[u] = parts + q * plane + (size_t)e * H + kbase + 8 * c;
-    lp[u] = row * kRgRow + c * 16;
+  for (int u = 0; u < kRgLoads; ++u) {
+    const int L = (kRgLoads * wave + u) * 64 + lane, row = L >> 2;
+    const int c = (L & 3) ^ ((row >> 2) & 3);  // the input chunk this lane stages
+    if (row < 256) {
+      const int q = row >> 7, e = min(e0 + (row & 127), E - 1);
+      voff[u] = ((q * E + e) * H + kbase + 8 * c) * 2;
+    } else {
+      voff[u] = (min(row - 256, ntok - 1) * H + kbase + 8 * c) * 2;
+    }
   }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = threadIdx.x + 256 * u, row = i >> 2, c = i & 3;
-    gx[u] = X + min<int64_t>(t0 + row, T - 1) * H + kbase + 8 * c;
-    lx[u] = (256 + row) * kRgRow + c * 16;
-  }
-  uint4 rp0, rp1, rp2, rp3, rx0, rx1;
-#define RG_GLOAD(S)                                                \
-  do {                                                             \
-    rp0 = *reinterpret_cast<const uint4 *>(gp[0] + 32 * (S));      \
-    rp1 = *reinterpret_cast<const uint4 *>(gp[1] + 32 * (S));      \
-    rp2 = *reinterpret_cast<const uint4 *>(gp[2] + 32 * (S));      \
-    rp3 = *reinterpret_cast<const uint4 *>(gp[3] + 32 * (S));      \
-    rx0 = *reinterpret_cast<const uint4 *>(gx[0] + 32 * (S));      \
-    rx1 = *reinterpret_cast<const uint4 *>(gx[1] + 32 * (S));      \
-  } while (0)
-#define RG_LSTORE(BUF)                                             \
-  do {                                                             \
-    char *b_ = lds + (BUF) * STAGE;                                \
-    *reinterpret_cast<uint4 *>(b_ + lp[0]) = rp0;                  \
-    *reinterpret_cast<uint4 *>(b_ + lp[1]) = rp1;                  \
-    *reinterpret_cast<uint4 *>(b_ + lp[2]) = rp2;                  \
-    *reinterpret_cast<uint4 *>(b_ + lp[3]) = rp3;                  \
-    *reinterpret_cast<uint4 *>(b_ + lx[0]) = rx0;                  \
-    *reinterpret_cast<uint4 *>(b_ + lx[1]) = rx1;                  \
+  // instructions u with (kRgLoads wave + u) < 16 stage router rows (wave-uniform)
+#define RG_ISSUE(S)                                                                                            \
+  do {                                                                                                         \
+    char *b_ = lds + ((S) % kRgStages) * kRgStage;                                                             \
+    _Pragma("unroll") for (int u = 0; u < kRgLoads; ++u) {                                                     \
+      __attribute__((address_space(3))) void *d_ = (__attribute__((address_space(3))) void *)(b_ + (kRgLoads * wave + u) * 1024); \
+      if (kRgLoads * wave + u < 16)                                                                            \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, d_, 16, voff[u], 64 * (S), 0, 0);                        \
+      else                                                                                                     \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, d_, 16, voff[u], 64 * (S), 0, 0);                        \
+    }                                                                                                          \
   } while (0)
   f32x4 acc[4][4];
 #pragma unroll
@@ -417,20 +428,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int r16 = lane & 15, kq = lane >> 4;
-  RG_GLOAD(0);
-  RG_LSTORE(0);
-  __syncthreads();
+  const int rd = r16 * 64 + ((kq ^ ((r16 >> 2) & 3)) << 4);  // this lane's chunk in a group of 16 rows
+#pragma unroll
+  for (int s = 0; s < kRgStages - 1; ++s)
+    if (s < nstep) RG_ISSUE(s);
 #pragma unroll 1
   for (int s = 0; s < nstep; ++s) {
-    if (s + 1 < nstep) RG_GLOAD(s + 1);
-    const char *b = lds + (s & 1) * STAGE;
+    rg_wait(min(kRgStages - 2, nstep - 1 - s));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's reads of step s - 1 are done
+    __builtin_amdgcn_s_barrier();
+    if (s + kRgStages - 1 < nstep) RG_ISSUE(s + kRgStages - 1);
+    const char *b = lds + (s % kRgStages) * kRgStage + rd;
     u32x4 av[4][2], bv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) av[i][q] = lds16(b + (q * 128 + we * 64 + 16 * i + r16) * kRgRow + kq * 16);
+      for (int q = 0; q < 2; ++q) av[i][q] = lds16(b + (q * 128 + we * 64 + 16 * i) * 64);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = lds16(b + (256 + wt * 64 + 16 * j + r16) * kRgRow + kq * 16);
+    for (int j = 0; j < 4; ++j) bv[j] = lds16(b + (256 + wt * 64 + 16 * j) * 64);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -439,11 +454,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i][q]),
                                                               __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
-    if (s + 1 < nstep) RG_LSTORE((s + 1) & 1);
-    __syncthreads();
   }
-#undef RG_GLOAD
-#undef RG_LSTORE
+#undef RG_ISSUE
   // lane: token t0 + 64 wt + 16 j + r16, rows e0 + 64 we + 16 i + 4 kq .. + 3
   float *out = part + (size_t)sk * T * E;
 #pragma unroll
@@ -750,9 +762,12 @@ static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
     // input slices so that about 256 workgroups run (at least 4 K steps each)
     int SK = 1;
     while (SK < kRgMaxSK && ntile * SK < 256 && H / 32 / (2 * SK) >= 4) SK *= 2;
-    const size_t lds = (size_t)2 * 384 * kRgRow;
+    const size_t lds = (size_t)kRgStages * kRgStage;
     const dim3 grid((unsigned)(ntile * SK));
     float *part = rw.part;
+    int rc = SK == 1 ? allow_lds<router_gemm_kernel<1>>(lds)
+                     : SK == 2 ? allow_lds<router_gemm_kernel<2>>(lds) : allow_lds<router_gemm_kernel<4>>(lds);
+    if (rc) return rc;
     switch (SK) {
       case 1: TMOE_LAUNCH(TMOE_KERNEL_ROUTER_LOGITS, router_gemm_kernel<1>, grid, dim3(256), lds, st, X, T, rw.parts,
                           (int)E, H, (int)cdiv(E, 128), part); break;
