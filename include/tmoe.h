@@ -155,6 +155,22 @@ size_t tmoe_linear_workspace_bytes(int64_t T, int64_t K);
 int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t N, int64_t K, const uint16_t *X,
                         int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws, size_t ws_bytes);
 
+/* The same product from canonical packed bytes: P uint8 [N][ldp], ldp >=
+ * ceil(K/5), row-major, 5 trits per byte as tmoe_pack_host writes them
+ * (ai.thesatyajit.com, "The 5.31 GB claim reconciles": five base-3 digits per
+ * byte). The call first writes the tiled image of P into the workspace
+ * (tmoe_repack_tiled), then runs tmoe_ternary_linear on it, both on `stream`;
+ * Y is the same as tmoe_ternary_linear's on that image. ws: at least
+ * tmoe_linear_packed_workspace_bytes(N, K, T) bytes, 16-byte aligned, owned
+ * by the caller and free for reuse when the stream has passed the call. A
+ * caller that multiplies the same weights many times repacks once and calls
+ * tmoe_ternary_linear. Errors: as tmoe_repack_tiled and tmoe_ternary_linear;
+ * TMOE_E_WORKSPACE when ws is short. */
+size_t tmoe_linear_packed_workspace_bytes(int64_t N, int64_t K, int64_t T);
+int tmoe_ternary_linear_packed(void *stream, const uint8_t *P, int64_t ldp, const float *s, int64_t N, int64_t K,
+                               const uint16_t *X, int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws,
+                               size_t ws_bytes);
+
 /* ------------------------------------------------------------------ router
  * Full-precision router (ai.thesatyajit.com, "The claim, verified from the
  * bytes": routers stay sharp; 8 of 256 chosen by logit margins).

@@ -176,6 +176,18 @@ def ternary_linear(Pt, s, N: int, K: int, X, Y, ws, stream=None) -> None:
                                    _ptr(ws), ws.numel() * ws.element_size()), "ternary_linear")
 
 
+def linear_packed_workspace_bytes(N: int, K: int, T: int) -> int:
+    return _load().tmoe_linear_packed_workspace_bytes(N, K, T)
+
+
+def ternary_linear_packed(P, s, K: int, X, Y, ws, stream=None) -> None:
+    """The same product from canonical packed bytes P uint8 [N][ldp] (repacked into ws first)."""
+    N, ldp = P.shape
+    T, ldx = X.shape
+    _check(_load().tmoe_ternary_linear_packed(_stream(stream), _ptr(P), ldp, _ptr(s), N, K, _ptr(X), ldx, T, _ptr(Y),
+                                          Y.shape[1], _ptr(ws), ws.numel() * ws.element_size()), "ternary_linear_packed")
+
+
 # -------------------------------------------------------------------- router
 def router_workspace_bytes(T: int, E: int) -> int:
     return _load().tmoe_router_workspace_bytes(T, E)

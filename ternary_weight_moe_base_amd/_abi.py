@@ -71,6 +71,9 @@ SIGNATURES = {
     "tmoe_linear_workspace_bytes": (c_size_t, [c_int64, c_int64]),
     "tmoe_ternary_linear": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64,
                                     c_void_p, c_int64, c_void_p, c_size_t]),
+    "tmoe_linear_packed_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
+    "tmoe_ternary_linear_packed": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_int64,
+                                           c_int64, c_void_p, c_int64, c_void_p, c_size_t]),
     "tmoe_router_workspace_bytes": (c_size_t, [c_int64, c_int64]),
     "tmoe_router_topk": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_size_t]),

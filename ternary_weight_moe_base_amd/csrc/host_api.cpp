@@ -235,6 +235,30 @@ int tmoe_ternary_linear(void *stream, const uint8_t *Pt, const float *s, int64_t
   return launch_linear((hipStream_t)stream, Pt, s, N, K, X, ldx, T, Y, ldy, ws);
 }
 
+size_t tmoe_linear_packed_workspace_bytes(int64_t N, int64_t K, int64_t T) {
+  if (N <= 0 || K <= 0) return 0;
+  return align_up((size_t)tmoe_tiled_bytes(N, K), 256) + tmoe_linear_workspace_bytes(T, K);
+}
+
+int tmoe_ternary_linear_packed(void *stream, const uint8_t *P, int64_t ldp, const float *s, int64_t N, int64_t K,
+                               const uint16_t *X, int64_t ldx, int64_t T, float *Y, int64_t ldy, void *ws,
+                               size_t ws_bytes) {
+  clear_error();
+  REQUIRE(N >= 0 && K >= 0 && T >= 0, TMOE_E_ARG, "negative size");
+  if (N == 0 || T == 0) return TMOE_OK;
+  REQUIRE(K > 0, TMOE_E_SHAPE, "K must be positive");
+  REQUIRE(ldp >= (K + 4) / 5, TMOE_E_SHAPE, "ldp < ceil(K/5)");
+  REQUIRE(ldx >= K && ldy >= N, TMOE_E_SHAPE, "ldx < K or ldy < N");
+  REQUIRE(P && s && X && Y, TMOE_E_ARG, "null pointer");
+  const size_t need = tmoe_linear_packed_workspace_bytes(N, K, T);
+  REQUIRE(ws && ws_bytes >= need && aligned16(ws), TMOE_E_WORKSPACE, "workspace needs %zu bytes (16-aligned)", need);
+  uint8_t *Pt = static_cast<uint8_t *>(ws);
+  const size_t tiled = align_up((size_t)tmoe_tiled_bytes(N, K), 256);
+  int rc = tmoe_repack_tiled(stream, P, N, K, ldp, Pt);
+  if (rc) return rc;
+  return tmoe_ternary_linear(stream, Pt, s, N, K, X, ldx, T, Y, ldy, static_cast<char *>(ws) + tiled, ws_bytes - tiled);
+}
+
 // -------------------------------------------------------------------- router
 size_t tmoe_router_workspace_bytes(int64_t T, int64_t E) {
   if (T < 0 || E <= 0) return 0;

@@ -133,6 +133,18 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
     assert lib.tmoe_combine(None, 16, 16, 16, 1, 8, 2048, 16, None, 16) == E.TMOE_E_ARG  # resid_out w/o resid_in
     assert lib.tmoe_synth_ih12(None, 1, 0, 1, 0, -1, 1.0, 16) == E.TMOE_E_ARG
     assert lib.tmoe_repack_tiled(None, 16, 4, 23, 4, 16) == E.TMOE_E_SHAPE  # ldp < ceil(23/5)
+    # the canonical-byte linear: the tiled image (256-byte aligned) plus the linear's own scratch
+    for N, K, T in [(512, 2048, 4), (17, 23, 3), (300, 1000, 37)]:
+        need = lib.tmoe_linear_packed_workspace_bytes(N, K, T)
+        assert need == math.ceil(tm.tiled_bytes(N, K) / 256) * 256 + lib.tmoe_linear_workspace_bytes(T, K)
+    assert lib.tmoe_linear_packed_workspace_bytes(0, 8, 4) == 0
+    f = lib.tmoe_ternary_linear_packed
+    assert f(None, 16, 1, 16, 4, 8, 16, 8, 2, 16, 4, 16, 1 << 20) == E.TMOE_E_SHAPE  # ldp < ceil(8/5)
+    assert f(None, 16, 2, 16, 4, 8, 16, 4, 2, 16, 4, 16, 1 << 20) == E.TMOE_E_SHAPE  # ldx < K
+    assert f(None, None, 2, None, 4, 8, None, 8, 2, None, 4, 16, 1 << 20) == E.TMOE_E_ARG
+    assert f(None, 16, 2, 16, 4, 8, 16, 8, 2, 16, 4, 16, 16) == E.TMOE_E_WORKSPACE
+    assert f(None, 16, 2, 16, 4, 8, 16, 8, 2, 16, 4, 17, 1 << 20) == E.TMOE_E_WORKSPACE  # misaligned ws
+    assert f(None, None, 2, None, 0, 8, None, 8, 2, None, 0, None, 0) == E.TMOE_OK  # N = 0
 
 
 def test_lm_head_rejects_bad_arguments_without_gpu():

@@ -200,6 +200,33 @@ def test_ternary_linear_config1(tm, T):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("N,K,T,ldp", [(512, 2048, 4, 410), (300, 1000, 37, 208), (17, 2048, 1, 416)])
+def test_ternary_linear_packed(tm, N, K, T, ldp):
+    """The canonical-byte entry point: the host-packed bytes of oracle trits
+    (row stride ldp, ragged row tiles, K not a multiple of 5 or of the step)
+    give the oracle's product, and the same Y bit for bit as repacking once
+    and calling the tiled entry point."""
+    say(f"linear packed N={N} K={K} T={T} ldp={ldp}")
+    g = np.random.default_rng(N * 7 + K + T)
+    t, s = O.ternarize_absmean(g.standard_normal((N, K)).astype(np.float32))
+    Ph = O.pack_trits(t, ldp)
+    xb = ti.activations(3, T, K)
+    x = O.bf16_to_f64(xb)
+    P = torch.from_numpy(Ph).cuda()
+    sd = dev(s.astype(np.float32))
+    Xd = bf16_dev(xb)
+    Y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    tm.ternary_linear_packed(P, sd, K, Xd, Y, ws_bytes(tm.linear_packed_workspace_bytes(N, K, T)))
+    Pt = torch.empty(tm.tiled_bytes(N, K), dtype=torch.uint8, device="cuda")
+    tm.repack_tiled(P, K, Pt)
+    Y2 = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    tm.ternary_linear(Pt, sd, N, K, Xd, Y2, ws_bytes(tm.linear_workspace_bytes(T, K)))
+    assert np.array_equal(host(Y), host(Y2))
+    err = O.max_normalized_error(host(Y), O.ternary_linear(t, s.astype(np.float32), x))
+    say(f"  max normalized error {err:.2e}")
+    assert err <= TOL
+
+
 def test_ternary_linear_streamed(tm):
     """The streamed variant of the 2048 -> 512 linear: 2048 distinct matrices
     stacked into one 1,048,576 x 2048 operand (436 MB packed), 4 tokens, in the
@@ -964,3 +991,26 @@ def test_native_driver_runs(args):
     r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr
     assert ("us/step" in r.stdout) or ("GB/s" in r.stdout), r.stdout
+
+
+def test_native_driver_issue_costs():
+    """The issue-cost calibration of the native driver: every instruction kind
+    gets a positive cost per wavefront instruction, a product costs more than any
+    vector instruction, and the clock line is printed."""
+    import re
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.dirname(__file__)), "ternary_weight_moe_base_amd", "tmoe_run")
+    say("tmoe_run issue")
+    r = subprocess.run([exe, "issue"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    rows = dict()
+    for line in r.stdout.splitlines():
+        m = re.match(r"\s+(v_\w+)\s+([0-9.]+)\s+([0-9.]+)\s*$", line)
+        if m:
+            rows[m.group(1)] = (float(m.group(2)), float(m.group(3)))
+    assert len(rows) == 10, r.stdout
+    assert all(a > 0 and b > 0 for a, b in rows.values())
+    mfma = rows["v_mfma_f32_16x16x32_bf16"][1]
+    assert all(mfma > b for k, (a, b) in rows.items() if not k.startswith("v_mfma"))
+    assert "core clock" in r.stdout
