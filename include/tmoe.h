@@ -427,8 +427,9 @@ int tmoe_lm_head_topk(void *stream, const uint16_t *X, int64_t T, int64_t H, con
  * tmoe_profile_end, which waits for them and writes the per-launch durations
  * in milliseconds to ms[0..*count). The events carry no system-scope fence
  * (hipEventDisableSystemFence), so they add no cache write-back to the timed
- * dispatch. Global state: not thread-safe; one
- * profiling window at a time (TMOE_E_ARG otherwise). */
+ * dispatch. The window belongs to the calling thread: only launches that
+ * thread issues are timed, calls from other threads are untouched, and a
+ * thread holds one window at a time (TMOE_E_ARG otherwise). */
 enum {
   TMOE_KERNEL_ROUTER_LOGITS = 1, /* fp64 logits (VALU for T <= 64, matrix cores above) */
   TMOE_KERNEL_ROUTER_TOPK = 2,   /* certified top-k (with its rare double-double recompute) */

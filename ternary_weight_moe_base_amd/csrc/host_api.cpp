@@ -27,10 +27,13 @@ int hip_fail(hipError_t e, const char *what) {
 }
 
 // ------------------------------------------------------------ kernel timing
-static struct {
+// The measurement window of the calling thread (launches from other threads
+// never see it).
+struct ProfWindow {
   int kernel = 0, cap = 0, n = 0;
   hipEvent_t *start = nullptr, *stop = nullptr;
-} g_prof;
+};
+static thread_local ProfWindow g_prof;
 
 bool prof_events(int kid, hipEvent_t *start, hipEvent_t *stop) {
   if (g_prof.kernel != kid || g_prof.n >= g_prof.cap) return false;
