@@ -776,20 +776,7 @@ __global__ __launch_bounds__(64 * NW) void gateup_kernel(GateUpArgs a) {
   }
 }
 
-// ------------------------------------------- gate / up, token-blocked
-// Many pairs per expert (prefill): a workgroup takes a block of up to 64 pairs
-// of one expert and 256 intermediate rows (eight wavefronts, two row tiles
-// each). Each wavefront decodes the weights of a K step once for its two row
-// tiles and applies them to all four token tiles, and each activation slice it
-// reads from LDS feeds both row tiles, so a product costs 1/2 of an LDS read
-// and 1/4 of a decode. Activations stream through LDS one K step at a time by
-// direct global-to-LDS loads, kTbDepth steps in flight; a step's buffer is
-// [token tile][slice m][quarter g][column n] x 16 B, so the 16 columns of an
-// operand read are consecutive (no bank conflicts). Inputs past K are read
-// from a valid address (their trits are zero). Weights stream kTbWDepth steps
-// ahead of their use. The epilogue also writes, per pair, the largest |h| of
-// the workgroup's rows (hmax[pair][row group]), which the down projection
-// uses to pick the pair's scale.
+// ------------------------------------------- token-blocked work items
 // Work item of a token-blocked kernel: a 64-pair block and a row group. The
 // grid is 1-D, 8 * groups * ceil(max blocks / 8) workgroups; the dispatcher
 // hands consecutive workgroups to the eight XCDs in turn, so XCD x runs
@@ -815,6 +802,20 @@ static inline unsigned tb_grid(int64_t max_blocks, int groups) {
   return (unsigned)(8 * groups * ((max_blocks + 7) / 8));
 }
 
+// ------------------------------------------- gate / up, token-blocked
+// Many pairs per expert (prefill): a workgroup takes a block of up to 64 pairs
+// of one expert and 256 intermediate rows (eight wavefronts, two row tiles
+// each). Each wavefront decodes the weights of a K step once for its two row
+// tiles and applies them to all four token tiles, and each activation slice it
+// reads from LDS feeds both row tiles, so a product costs 1/2 of an LDS read
+// and 1/4 of a decode. Activations stream through LDS one K step at a time by
+// direct global-to-LDS loads, kTbDepth - 1 steps ahead; a step's buffer is
+// [token tile][slice m][quarter g][column n] x 16 B, so the 16 columns of an
+// operand read are consecutive (no bank conflicts). Inputs past K are read
+// from a valid address (their trits are zero). Weights stream kTbWDepth steps
+// ahead of their use. The epilogue also writes, per pair, the largest |h| of
+// the workgroup's rows (hmax[pair][row group]), which the down projection
+// uses to pick the pair's scale.
 constexpr int kTbWaves = 8, kTbR = 2, kTbDepth = 4, kTbWDepth = 3, kTbStepBytes = 4 * 5 * 64 * 16;
 constexpr int kTbRows = 16 * kTbWaves * kTbR;  // intermediate rows per workgroup
 constexpr int kTbMaxGroups = kTbMaxGroupsH;   // row groups per pair kept in hmax
