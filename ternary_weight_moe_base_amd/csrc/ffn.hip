@@ -306,10 +306,11 @@ __device__ inline void stage_h_parts(const float *h, int cnt, int I, int q5, cha
 // The same operand staging when each row's largest |h| is already known (the
 // token-blocked gate/up writes it per row group, hmax[row][q] for q <
 // ngroups): every thread takes whole 16-byte chunks of any rows, all of its
-// loads in flight at once, with no reduction across lanes.
-template <int NT, int M>
+// loads in flight at once, with no reduction across lanes. after_loads() runs
+// once the h loads are issued (its own loads then queue behind them).
+template <int NT, int M, class AfterLoads>
 __device__ inline void stage_h_known(const float *h, const uint32_t *hmax, int ngroups, int cnt, int I, int q5,
-                                     char *pl0, char *pl1, int rs, int *sig) {
+                                     char *pl0, char *pl1, int rs, int *sig, AfterLoads after_loads) {
   constexpr int NCH = 4 * M;                    // 16-byte chunks per staged row
   constexpr int PER = (64 * NCH + NT - 1) / NT;  // chunks per thread (at most 64 rows)
   for (int r = threadIdx.x; r < cnt; r += NT) {
@@ -336,6 +337,7 @@ __device__ inline void stage_h_known(const float *h, const uint32_t *hmax, int n
       v[u][e + 1] = f.y;
     }
   }
+  after_loads();
   __syncthreads();  // sig[] written
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -1195,9 +1197,10 @@ __device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int 
   const int rt0 = grp * (a.H / 16 / kDtbGroups) + wave * per_wave;
 
   DtbWeights<F, RT> cur;
-  dtb_load<F, RT>(a, e, rt0, lane, cur);
+  // h first (it is needed first), then the first row tiles' weights behind it
   stage_h_known<64 * kDtbWaves, M>(a.hf + (int64_t)start * a.I, a.hmax + (int64_t)start * kTbMaxGroups, a.hgroups, nb,
-                                   a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig);
+                                   a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig,
+                                   [&]() { dtb_load<F, RT>(a, e, rt0, lane, cur); });
   __syncthreads();
 
   const char *bq[NT];
