@@ -313,7 +313,12 @@ __device__ inline void stage_h_known(const float *h, const uint32_t *hmax, int n
                                      char *pl0, char *pl1, int rs, int *sig, AfterLoads after_loads) {
   constexpr int NCH = 4 * M;                    // 16-byte chunks per staged row
   constexpr int PER = (64 * NCH + NT - 1) / NT;  // chunks per thread (at most 64 rows)
-  for (int r = threadIdx.x; r < cnt; r += NT) {
+  // the thread index through an empty asm: a caller that stages inside a loop
+  // must not have the chunk offsets derived from it hoisted out of the loop
+  // and held in registers across its products
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  for (int r = tid; r < cnt; r += NT) {
     uint32_t mx = 0u;
     for (int q = 0; q < ngroups; ++q) mx = max(mx, hmax[(int64_t)r * kTbMaxGroupsH + q]);
     int sg = 0;
@@ -327,7 +332,7 @@ __device__ inline void stage_h_known(const float *h, const uint32_t *hmax, int n
   float v[PER][8];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int i = threadIdx.x + NT * u, row = i / NCH, c = i - row * NCH;
+    const int i = tid + NT * u, row = i / NCH, c = i - row * NCH;
     const int quarter = c / M, j0 = 8 * (c - quarter * M), k0 = q5 * quarter + j0;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -341,7 +346,7 @@ __device__ inline void stage_h_known(const float *h, const uint32_t *hmax, int n
   __syncthreads();  // sig[] written
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int i = threadIdx.x + NT * u, row = i / NCH, c = i - row * NCH;
+    const int i = tid + NT * u, row = i / NCH, c = i - row * NCH;
     if (row >= cnt) continue;
     const int sg = sig[row];
     uint32_t w[2][4];
@@ -1139,13 +1144,25 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs a) {
 // products. Columns past the block read its last pair and are not stored. The next row tiles' weights are in
 // flight while the current ones are multiplied (the first ones while h is
 // staged).
-constexpr int kDtbWaves = 8, kDtbR = 4, kDtbGroups = 2;
+constexpr int kDtbWaves = 8, kDtbR = 4, kDtbGroups = 4;
+// workgroups of the persistent token-blocked down: one per CU (its 138 KB of
+// LDS leave room for one), a multiple of 8
+static unsigned dtb_grid() {
+  static unsigned n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    n = (unsigned)((cus + 7) / 8 * 8);
+  }
+  return n;
+}
 
 template <int F, int RT>
 struct DtbWeights {
   uint2 d[kDtbR][F];
   uint32_t dw[kDtbR], sh[kDtbR];
-  float4 sd[kDtbR];
 };
 
 template <int F, int RT>
@@ -1158,7 +1175,6 @@ __device__ __forceinline__ void dtb_load(const DownArgs &a, int e, int rt, int l
     for (int s = 0; s < F; ++s) w.d[r][s] = *reinterpret_cast<const uint2 *>(dt + (int64_t)s * 512 + lane * 8);
     w.dw[r] = w.sh[r] = 0;
     if constexpr (RT > 0) load_tail<RT>(dt, F, lane, w.dw[r], w.sh[r]);
-    w.sd[r] = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + (rt + r) * 16 + 4 * (lane >> 4));
   }
 }
 
@@ -1167,13 +1183,13 @@ __device__ __forceinline__ void dtb_load(const DownArgs &a, int e, int rt, int l
 // accumulator). All four token tiles run (straight-line code schedules the
 // LDS reads ahead of the products); columns past the block read its last pair.
 template <int NT, int NW>
-__device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, const char *const bq[NT], int plane,
-                                          int off, f32x4 (*acc)[NT]) {
+__device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, const char *base, const int bq[NT],
+                                          int plane, int off, f32x4 (*acc)[NT]) {
   u32x4 b[2][NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    b[0][t] = lds16(bq[t] + off);
-    b[1][t] = lds16(bq[t] + plane + off);
+    b[0][t] = lds16(base + bq[t] + off);
+    b[1][t] = lds16(base + bq[t] + plane + off);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q)
@@ -1183,49 +1199,80 @@ __device__ __forceinline__ void dtb_slice(const uint32_t (*pw)[NW], int w0, cons
       for (int r = 0; r < kDtbR; ++r) acc[r][t] = mfma_f16(pw[r] + w0, b[q][t], acc[r][t]);
 }
 
-// NT: token tiles multiplied (those past the block's pairs read its last pair
-// and are not stored).
-template <int F, int RT, int NT>
-__device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int *sig, int e, int start, int nb,
-                                             int grp) {
+// Persistent walk: gridDim.x workgroups (a multiple of 8, one per CU) take
+// contiguous runs of the (block, row group) items, kDtbGroups items per block
+// in order, the runs of XCD x (workgroups x, x + 8, ...) next to each other.
+// A workgroup stages a block's h once for all of that block's items it runs
+// (a block change waits for every wavefront, then restages), and issues the
+// next item's weights during the current item's last K step. All four token
+// tiles are multiplied (a form per live-tile count would need more than the
+// 256 registers two wavefronts per SIMD leave each); columns past the block's
+// pairs read its last pair and are not stored.
+template <int F, int RT>
+__global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
+  extern __shared__ __align__(16) char smem[];  // [2][64][rs]: the hi and lo planes
+  __shared__ int sig[64];
+  constexpr int NT = 4, G = kDtbGroups;
+  constexpr int M = 5 * F + tail_mfmas(RT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  constexpr int M = 5 * F + tail_mfmas(RT);
   const int rs = lds_row_bytes(a.slots);
   const int plane = 64 * rs;
-  const int per_wave = a.H / 16 / kDtbGroups / kDtbWaves;  // row tiles of this wavefront
-  const int rt0 = grp * (a.H / 16 / kDtbGroups) + wave * per_wave;
+  const int nitems = *a.ntiles * G;  // here: the 64-pair blocks
+  const int nwg = (int)gridDim.x;
+  const int run = (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3);
+  const int per = (nitems + nwg - 1) / nwg;
+  const int i0 = min(run * per, nitems), i1 = min(i0 + per, nitems);
+  if (i0 >= i1) return;
+  const int rows_g = a.H / 16 / G;  // row tiles of an item: kDtbR per wavefront
+  const int4 *tiles = reinterpret_cast<const int4 *>(a.tiles);
 
+  int blk = -1, e = 0, start = 0, nb = 1;
   DtbWeights<F, RT> cur;
-  // h first (it is needed first), then the first row tiles' weights behind it
-  stage_h_known<64 * kDtbWaves, M>(a.hf + (int64_t)start * a.I, a.hmax + (int64_t)start * kTbMaxGroups, a.hgroups, nb,
-                                   a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig,
-                                   [&]() { dtb_load<F, RT>(a, e, rt0, lane, cur); });
-  __syncthreads();
-
-  const char *bq[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) bq[t] = smem + min(16 * t + n, nb - 1) * rs + g * M * 16;
 #pragma unroll 1
-  for (int it = 0; it < per_wave; it += kDtbR) {
+  for (int item = i0; item < i1; ++item) {
+    if (item / G != blk) {
+      // a new block: every wavefront has finished reading the last one's h and
+      // sig; its h is staged (the run's first item: its weights behind h; the
+      // later items' weights are already in flight)
+      if (blk >= 0) __syncthreads();
+      blk = item / G;
+      const int4 td = tiles[blk];
+      e = td.x;
+      start = td.y;
+      nb = td.z;  // 1..64 pairs
+      stage_h_known<64 * kDtbWaves, M>(a.hf + (int64_t)start * a.I, a.hmax + (int64_t)start * kTbMaxGroups,
+                                       a.hgroups, nb, a.I, 5 * a.gd.Q, smem, smem + plane, rs, sig, [&]() {
+                                         if (item == i0) dtb_load<F, RT>(a, e, (i0 % G) * rows_g + wave * kDtbR, lane, cur);
+                                       });
+      __syncthreads();
+    }
+    const int rt0 = (item % G) * rows_g + wave * kDtbR;  // this wavefront's kDtbR row tiles
+    // the next item of the run (the last one again after the last): its block's tiles
+    const int nxt = min(item + 1, i1 - 1);
+    const int4 ntd = tiles[nxt / G];
+    int bq[NT];  // LDS offsets of the four token tiles' operand rows
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bq[t] = min(16 * t + n, nb - 1) * rs + g * M * 16;
     f32x4 acc[kDtbR][NT];
 #pragma unroll
     for (int r = 0; r < kDtbR; ++r)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the row scales, needed only by the epilogue
     float4 sd[kDtbR];
 #pragma unroll
-    for (int r = 0; r < kDtbR; ++r) sd[r] = cur.sd[r];
-    // the tail slices first, then the full steps: after the last step is
-    // decoded the weight registers are free for the next row tiles' loads,
-    // which land while that step's products run
+    for (int r = 0; r < kDtbR; ++r)
+      sd[r] = *reinterpret_cast<const float4 *>(a.down_s + (int64_t)e * a.H + (rt0 + r) * 16 + 4 * g);
+    // after the last step is decoded the weight registers are free for the
+    // next item's row tiles, which land while that step's products run
     if constexpr (RT > 0) {
       uint32_t pw[kDtbR][16];
 #pragma unroll
       for (int r = 0; r < kDtbR; ++r) unpack_tail<RT>(cur.dw[r], cur.sh[r], pw[r]);
 #pragma unroll
       for (int m = 0; m < tail_mfmas(RT); ++m) {
-        dtb_slice<NT>(pw, 4 * m, bq, plane, (5 * F + m) * 16, acc);
+        dtb_slice<NT>(pw, 4 * m, smem, bq, plane, (5 * F + m) * 16, acc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1234,10 +1281,10 @@ __device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int 
       uint32_t pw[kDtbR][20];
 #pragma unroll
       for (int r = 0; r < kDtbR; ++r) unpack8(cur.d[r][s], pw[r]);
-      if (s == F - 1 && it + kDtbR < per_wave) dtb_load<F, RT>(a, e, rt0 + it + kDtbR, lane, cur);
+      if (s == F - 1) dtb_load<F, RT>(a, ntd.x, (nxt % G) * rows_g + wave * kDtbR, lane, cur);
 #pragma unroll
       for (int m = 0; m < 5; ++m) {
-        dtb_slice<NT>(pw, 4 * m, bq, plane, (5 * s + m) * 16, acc);
+        dtb_slice<NT>(pw, 4 * m, smem, bq, plane, (5 * s + m) * 16, acc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1249,7 +1296,7 @@ __device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int 
       float *op = a.O + (int64_t)(start + col) * a.H;
 #pragma unroll
       for (int r = 0; r < kDtbR; ++r) {
-        const int row0 = (rt0 + it + r) * 16 + 4 * g;
+        const int row0 = (rt0 + r) * 16 + 4 * g;
         float4 o;
         o.x = ldexpf(acc[r][t][0], us) * sd[r].x;
         o.y = ldexpf(acc[r][t][1], us) * sd[r].y;
@@ -1259,20 +1306,6 @@ __device__ __forceinline__ void down_tb_body(const DownArgs &a, char *smem, int 
       }
     }
   }
-}
-
-template <int F, int RT>
-__global__ __launch_bounds__(64 * kDtbWaves) void down_tb_kernel(DownArgs a) {
-  extern __shared__ __align__(16) char smem[];  // [2][64][rs]: the hi and lo planes
-  __shared__ int sig[64];
-  const int nblk = *a.ntiles;  // here: the 64-pair blocks
-  const TbItem it = tb_item(nblk, kDtbGroups);
-  if (it.blk >= nblk) return;
-  const int4 td = reinterpret_cast<const int4 *>(a.tiles)[it.blk];
-  const int e = td.x, start = td.y, nb = td.z;  // nb: 1..64 pairs
-  // all four token tiles (a form per live-tile count would need more than
-  // the 256 registers two wavefronts per SIMD leave each one)
-  down_tb_body<F, RT, 4>(a, smem, sig, e, start, nb, it.grp);
 }
 
 // ------------------------------------------------- down + combine (decode)
@@ -2030,8 +2063,7 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
     const size_t lds = (size_t)2 * 64 * lds_row_bytes(gi.slots);
     rc = allow_lds<down_tb_kernel<3, 2>>(lds);
     if (rc) return rc;
-    TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_tb_kernel<3, 2>), dim3(tb_grid(ffn_max_blocks(P, E), kDtbGroups)),
-                dim3(64 * kDtbWaves), lds, st, da);
+    TMOE_LAUNCH(TMOE_KERNEL_DOWN, (down_tb_kernel<3, 2>), dim3(dtb_grid()), dim3(64 * kDtbWaves), lds, st, da);
     TMOE_LAUNCHED("down_tb");
     return TMOE_OK;
   }
@@ -2039,8 +2071,7 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
 }
 
 bool ffn_blocked(int64_t P, int64_t E, int64_t H, int64_t I) {
-  return P >= 32 * E && I % kTbRows == 0 && I / kTbRows <= kTbMaxGroups && H % (16 * kDtbGroups * kDtbWaves) == 0 &&
-         (H / 16 / kDtbGroups / kDtbWaves) % kDtbR == 0;
+  return P >= 32 * E && I % kTbRows == 0 && I / kTbRows <= kTbMaxGroups && H == 16 * kDtbGroups * kDtbWaves * kDtbR;
 }
 
 size_t linear_ws_bytes(int64_t T, int64_t K) {
