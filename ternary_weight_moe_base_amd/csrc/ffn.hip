@@ -1148,14 +1148,15 @@ constexpr int kDtbWaves = 8, kDtbR = 4, kDtbGroups = 4;
 // workgroups of the persistent token-blocked down: one per CU (its 138 KB of
 // LDS leave room for one), a multiple of 8
 static unsigned dtb_grid() {
-  static unsigned n = 0;
-  if (n == 0) {
+  // read once (thread-safe static initialization); any multiple of 8 is
+  // correct, the CU count only balances the runs
+  static const unsigned n = []() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    n = (unsigned)((cus + 7) / 8 * 8);
-  }
+    return (unsigned)((cus + 7) / 8 * 8);
+  }();
   return n;
 }
 
