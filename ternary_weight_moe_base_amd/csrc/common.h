@@ -1,6 +1,8 @@
 // Internal declarations shared by the host and device sources of libtmoe.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -133,15 +135,17 @@ bool prof_events(int kid, hipEvent_t *start, hipEvent_t *stop);
     }                                                                                  \
   } while (0)
 
-// Kernels using more than 64 KiB of LDS opt in once per kernel (gfx950 has 160 KiB).
+// Kernels using more than 64 KiB of LDS opt in once per kernel (gfx950 has 160 KiB;
+// each such kernel always asks for the same size). Concurrent first calls may
+// both set the attribute, which is idempotent.
 template <auto Kern>
 inline int allow_lds(size_t bytes) {
-  static bool done = false;  // one flag per kernel instantiation
-  if (done || bytes <= 65536) return TMOE_OK;
+  static std::atomic<bool> done{false};  // one flag per kernel instantiation
+  if (bytes <= 65536 || done.load(std::memory_order_acquire)) return TMOE_OK;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)bytes);
   if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
-  done = true;
+  done.store(true, std::memory_order_release);
   return TMOE_OK;
 }
 
