@@ -231,6 +231,62 @@ __global__ __launch_bounds__(kBlockTok) void group_scatter_kernel(const int32_t 
   }
 }
 
+// Scatter with the scan folded in, for a batch of a few token blocks (at most
+// kScanInMaxBlocks): each workgroup reads the block counts of every expert
+// (group_count_kernel's output), forms the expert totals, the pairs in blocks
+// before its own and the expert offsets (one workgroup scan), then scatters
+// its block as group_scatter_kernel does from the same bases. Workgroup 0 also
+// writes counts, offsets and the work tiles. Same outputs as scan + scatter,
+// one launch fewer.
+static constexpr int kScanInMaxBlocks = 64;
+
+template <int KM>
+__global__ __launch_bounds__(kBlockTok) void group_scatter_scan_kernel(const int32_t *idx, int64_t T, int k, int E,
+                                                                       const int32_t *bcount, int nb, int32_t *counts,
+                                                                       int32_t *offsets, int32_t *sorted_token,
+                                                                       int32_t *sorted_slot, int32_t *pos,
+                                                                       int32_t *tiles, int32_t *ntiles, int tile) {
+  constexpr int B = 16;
+  __shared__ uint32_t bits[1024 * 8];
+  __shared__ int off[1024], base[1024], c0[1024], tc[1024];
+  __shared__ int tmp[kBlockTok];
+  const int64_t t0 = (int64_t)blockIdx.x * kBlockTok;
+  // this workgroup's own choices first, in flight with the counts
+  int ch[KM > 0 ? KM : 1];
+  if constexpr (KM > 0) load_choices<KM>(idx, T, k, t0, ch);
+  for (int e = threadIdx.x; e < E; e += kBlockTok) {
+    int tot = 0, before = 0;
+    for (int b0 = 0; b0 < nb; b0 += B) {
+      int c[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) c[u] = bcount[(int64_t)min(b0 + u, nb - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        tot += b0 + u < nb ? c[u] : 0;
+        before += b0 + u < (int)blockIdx.x ? c[u] : 0;
+      }
+    }
+    off[e] = tot;
+    c0[e] = tot;
+    base[e] = before;
+    if (blockIdx.x == 0) counts[e] = tot;
+  }
+  const int total = block_exclusive_scan<kBlockTok>(off, E, tmp);  // off: expert offsets
+  for (int e = threadIdx.x; e < E; e += kBlockTok) {
+    base[e] += off[e];
+    if (blockIdx.x == 0) offsets[e] = off[e];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = total;
+  if constexpr (KM > 0) {
+    build_bitmask_r<KM>(bits, ch, E);  // its first barrier also orders the base writes above
+    scatter_block_r<KM>(bits, base, ch, T, k, E, t0, sorted_token, sorted_slot, pos);
+  } else {
+    build_bitmask(bits, idx, T, k, E, t0);
+    scatter_block(bits, base, idx, T, k, E, t0, sorted_token, sorted_slot, pos);
+  }
+  if (blockIdx.x == 0 && tiles) write_tiles(c0, off, E, tc, tmp, tiles, ntiles, tile);
+}
+
 template <int KM>
 static int launch_group_k(hipStream_t st, const int32_t *idx, int64_t T, int k, int64_t E, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_token, int32_t *sorted_slot, int32_t *pos,
@@ -246,6 +302,12 @@ static int launch_group_k(hipStream_t st, const int32_t *idx, int64_t T, int k, 
   TMOE_LAUNCH(TMOE_KERNEL_GROUP, group_count_kernel<KM>, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E,
               gw.bcount);
   TMOE_LAUNCHED("group_count");
+  if (nb <= kScanInMaxBlocks) {
+    hipLaunchKernelGGL(group_scatter_scan_kernel<KM>, dim3((unsigned)nb), dim3(kBlockTok), 0, st, idx, T, k, (int)E,
+                       gw.bcount, (int)nb, counts, offsets, sorted_token, sorted_slot, pos, tiles, ntiles, tile);
+    TMOE_LAUNCHED("group_scatter_scan");
+    return TMOE_OK;
+  }
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kBlockTok), 0, st, gw.bcount, (int)nb, (int)E, gw.bbase, counts,
                      offsets, tiles, ntiles, tile);
   TMOE_LAUNCHED("group_scan");
