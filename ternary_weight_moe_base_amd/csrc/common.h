@@ -230,10 +230,19 @@ int launch_ffn(hipStream_t st, const tmoe_moe_weights *W, const uint16_t *X, int
 // kDcMaxPairs pairs, down with the weighted combine (+ residual) fused, else
 // down into O and the combine. The per-token bound slots are cleared for the
 // next call.
+// 1.01 gamma_d (gamma_d = d u / (1 - d u), u = 2^-53): the factor of the fp64
+// logits' error bound for summation depth d, formed once on the host (the
+// same IEEE operations in the same order as a device-side evaluation).
+inline double topk_bound_scale(int d) {
+  const double u = 0x1p-53;
+  return 1.01 * ((double)d * u / (1.0 - (double)d * u));
+}
+
 struct DecodeRoute {
   const double *lg;
   const uint64_t *bnd;
   int depth, nb;  // error-bound depth; bound slots per token
+  double bscale;  // topk_bound_scale(depth)
   const float *Wr, *bias;
   int32_t *idx, *n_fixup, *sorted_token, *sorted_slot, *pos;
   float *w;

@@ -451,7 +451,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
     // one token: wavefront 0 selects its k experts; their ranks among the k
     // (all distinct) are the grouped positions and the tile indices
     if (wave == 0) {
-      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(slot_max(bs[0])));
+      const double B = r.bscale * bitsd(wave_max_u64(slot_max(bs[0])));
 #pragma unroll
       for (int j = 0; j < NPL; ++j) lv[0][j] = lane * NPL + j < E ? lv[0][j] : 0.0;
       int nfix = 0;
@@ -492,7 +492,7 @@ __device__ inline void route_prologue(const GateUpArgs &a, RouteLds &s, char *sm
   for (int q = 0; q < kDecodeMaxT / 4; ++q) {
     const int t = wave + 4 * q;
     if (t < T) {
-      const double B = 1.01 * gamma_d(r.depth) * bitsd(wave_max_u64(slot_max(bs[q])));
+      const double B = r.bscale * bitsd(wave_max_u64(slot_max(bs[q])));
 #pragma unroll
       for (int j = 0; j < NPL; ++j) lv[q][j] = lane * NPL + j < E ? lv[q][j] : 0.0;
       if (!topk_certified_v<NPL, true>(lv[q], r.lg + (int64_t)t * E, E, k, B, s.sidx + t * k, s.sw + t * k)) {

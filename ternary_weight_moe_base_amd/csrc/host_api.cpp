@@ -566,8 +566,8 @@ int moe_forward_impl(void *stream, const tmoe_moe_weights *W, const uint16_t *X,
     int depth = 0, nb = 0;
     rc = launch_router_logits(st, X, T, H, W->router_w, W->router_bias, E, rw, &depth, &nb);
     if (rc) return rc;
-    const DecodeRoute r{rw.lg, rw.bnd, depth, nb, W->router_w, W->router_bias, idx, o.n_fixup, st_tok, st_slot, pos,
-                        wt, nullptr, nullptr, nullptr};
+    const DecodeRoute r{rw.lg, rw.bnd, depth, nb, topk_bound_scale(depth), W->router_w, W->router_bias, idx,
+                        o.n_fixup, st_tok, st_slot, pos, wt, nullptr, nullptr, nullptr};
     return launch_decode_tail(st, W, X, T, o.clamp, r, fw, O, Y, o.resid_out ? X : nullptr, o.resid_out);
   }
   rc = launch_router(st, X, T, H, W->router_w, W->router_bias, E, k, idx, wt, nullptr, o.n_fixup, rw);

@@ -66,34 +66,40 @@ RouterWs router_ws_carve(void *ws, int64_t T, int64_t E, int64_t H) {
 // ------------------------------------------------------------ fp64 logits
 // One token's chains over this lane's inputs (exact bf16 x fp32 products in
 // fp64): the logit sum and the sum of |x w| for the bound.
+// Two chains of 2 NC products each (inputs of even and odd c), then their sum:
+// no element passes more than 2 NC + 1 roundings here, within the 4 NC that
+// the bound's depth counts for this part.
 template <int NC>
 __device__ __forceinline__ void logit_chains(const uint2 *xr, const double (&w)[4 * NC], int lane, double &acc,
                                              double &aab) {
-  acc = 0.0;
-  aab = 0.0;
+  double a2[2] = {0.0, 0.0}, b2[2] = {0.0, 0.0};
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     uint2 xv = xr[c * 64 + lane];
     const double x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xFFFF0000u);
     const double x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xFFFF0000u);
-    acc = fma(w[4 * c], x0, acc);
-    acc = fma(w[4 * c + 1], x1, acc);
-    acc = fma(w[4 * c + 2], x2, acc);
-    acc = fma(w[4 * c + 3], x3, acc);
-    aab = fma(fabs(w[4 * c]), fabs(x0), aab);
-    aab = fma(fabs(w[4 * c + 1]), fabs(x1), aab);
-    aab = fma(fabs(w[4 * c + 2]), fabs(x2), aab);
-    aab = fma(fabs(w[4 * c + 3]), fabs(x3), aab);
+    double &a = a2[c & 1], &b = b2[c & 1];
+    a = fma(w[4 * c], x0, a);
+    a = fma(w[4 * c + 1], x1, a);
+    a = fma(w[4 * c + 2], x2, a);
+    a = fma(w[4 * c + 3], x3, a);
+    b = fma(fabs(w[4 * c]), fabs(x0), b);
+    b = fma(fabs(w[4 * c + 1]), fabs(x1), b);
+    b = fma(fabs(w[4 * c + 2]), fabs(x2), b);
+    b = fma(fabs(w[4 * c + 3]), fabs(x3), b);
   }
+  acc = a2[0] + a2[1];
+  aab = b2[0] + b2[1];
 }
 
 // Each lane keeps 4*NC router weights (elements c*256 + 4*lane + 0..3, loaded
-// by the caller as wv[c]) as fp64 and runs one FMA chain of 4*NC exact
-// products per logit, then a 6-level butterfly: depth 4*NC + 6, plus 1 for the
-// bias (bv: the caller's bias value, used when bias is not null). The same
-// chain accumulates A = sum |x w| for the bound. Four tokens go together
-// (eight independent chains) when the chunk holds them. Results for token n go
-// to lgs[n*4 + wave] and abs_s[n*4 + wave] (LDS).
+// by the caller as wv[c]) as fp64 and sums its 4*NC exact products per logit
+// in two FMA chains (logit_chains), then a 6-level DPP butterfly: depth at most
+// 4*NC + 6, plus 1 for the bias (bv: the caller's bias value, used when bias
+// is not null); the bound counts 4*NC + 8. The same chains accumulate
+// A = sum |x w| for the bound. Four tokens go together (sixteen independent
+// chains) when the chunk holds them. Results for token n go to lgs[n*4 + wave]
+// and abs_s[n*4 + wave] (LDS).
 template <int NC>
 __device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv)[NC], const float *bias, float bv,
                                    int64_t e, int E, double *lgs, double *abs_s) {
@@ -126,8 +132,8 @@ __device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv
       logit_chains<NC>(reinterpret_cast<const uint2 *>(xs + (size_t)(n + u) * H), w, lane, acc[u], aab[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc[u] = wave_sum_d(acc[u]);
-      aab[u] = wave_sum_d(aab[u]);
+      acc[u] = wave_sum_dpp(acc[u]);
+      aab[u] = wave_sum_dpp(aab[u]);
     }
     if (lane == 0) {
 #pragma unroll
@@ -140,8 +146,8 @@ __device__ inline void logits_rows(const uint16_t *xs, int nt, const float4 (&wv
   for (; n < nt; ++n) {
     double acc, aab;
     logit_chains<NC>(reinterpret_cast<const uint2 *>(xs + (size_t)n * H), w, lane, acc, aab);
-    acc = wave_sum_d(acc);
-    aab = wave_sum_d(aab);
+    acc = wave_sum_dpp(acc);
+    aab = wave_sum_dpp(aab);
     if (lane == 0) {
       lgs[n * 4 + wave] = acc + b;
       abs_s[n * 4 + wave] = aab + fabs(b);
@@ -709,12 +715,12 @@ static void router_bf16_bound(int H, int SK, double *gfac, double *babs) {
 template <int NPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(int64_t T, const uint16_t *X, int H, const float *Wr,
                                                           const float *bias, const double *lg, const uint64_t *bnd,
-                                                          int nb, int E, int k, int depth, int32_t *idx, float *wout,
-                                                          int32_t *n_fixup) {
+                                                          int nb, int E, int k, double bscale, int32_t *idx,
+                                                          float *wout, int32_t *n_fixup) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const double B = 1.01 * gamma_d(depth) * bound_of_slots(bnd + t * nb, nb);
+  const double B = bscale * bound_of_slots(bnd + t * nb, nb);  // bscale = topk_bound_scale(depth)
   if (!topk_certified<NPL>(lg + t * E, E, k, B, idx + t * k, wout + t * k)) {
     if (lane == 0 && n_fixup) atomicAdd(n_fixup, 1);
     topk_dd<NPL>(X + t * H, H, Wr, bias, E, k, idx + t * k, wout + t * k, nullptr);
@@ -796,7 +802,7 @@ static int launch_router_nc(hipStream_t st, const uint16_t *X, int64_t T, const 
   }
   TMOE_LAUNCHED("router_logits");
   TMOE_LAUNCH(TMOE_KERNEL_ROUTER_TOPK, (router_topk_kernel<NPL>), dim3((unsigned)cdiv(T, 4)), dim3(256), 0, st, T, X,
-              H, Wr, bias, rw.lg, rw.bnd, nb, (int)E, k, depth, idx, w, n_fixup);
+              H, Wr, bias, rw.lg, rw.bnd, nb, (int)E, k, topk_bound_scale(depth), idx, w, n_fixup);
   TMOE_LAUNCHED("router_topk");
   return TMOE_OK;
 }
