@@ -13,8 +13,9 @@
  *  - The router stays full precision and picks 8 of 256 experts per token
  *    (ai.thesatyajit.com, "The claim, verified from the bytes";
  *    codeinsider.com.br, "256 experts, 8 ativos").
- *  - One expert is linear(act(clamp(x Wg^T, max=7)) * clamp(x Wu^T, -7, 7), Wd)
- *    (ai.thesatyajit.com, "The shipped code does no quantization"); act is SiLU.
+ *  - One expert maps a token x to o = Wd h, where h = SiLU(min(g, 7)) times
+ *    the clip of u to [-7, 7], g = Wg x and u = Wu x (ai.thesatyajit.com,
+ *    "The shipped code does no quantization").
  *  - Shapes: hidden 2048, 256 experts, top 8, moe_intermediate_size 512
  *    (jj-blog Maple-Preview news, architecture list).
  *

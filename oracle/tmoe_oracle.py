@@ -16,8 +16,8 @@ what the layer is defined to compute. Sources (the pages are the authority):
     (3**5 = 243 <= 256); log2(3) bits per trit is the floor.
   - "The claim, verified from the bytes" (router paragraph): the MoE router
     stays full precision and chooses 8 of 256 experts from its logits.
-  - "The shipped code does no quantization": the expert forward is
-    ``linear(act(clamp(x Wg^T, max=7)) * clamp(x Wu^T, -7, 7), Wd)``.
+  - "The shipped code does no quantization": an expert maps x to
+    o = Wd h with h = SiLU(min(g, 7)) * clip(u, -7, 7), g = Wg x, u = Wu x.
 * codeinsider.com.br, "Pesos ternarios": a ternary weight skips (0), adds
   (+1) or subtracts (-1) the activation; "256 experts, 8 ativos": 8 of 256
   experts are active per token.

@@ -3,7 +3,8 @@
 //
 // Arithmetic (codeinsider.com.br, "Pesos ternarios": a ternary weight adds,
 // subtracts or skips its input; ai.thesatyajit.com, "The shipped code does no
-// quantization": out = linear(act(clamp(x Wg^T, max=7)) * clamp(x Wu^T, -7, 7), Wd)):
+// quantization": an expert computes o = Wd h with h = SiLU(min(g, 7)) times
+// clip(u, -7, 7), g = Wg x, u = Wu x):
 //  - A trit t enters the matrix core as the 16-bit value 2t, whose bit pattern
 //    ((d - 1) mod 4) << 14 (d = t + 1 the base-3 digit) is the same in bf16
 //    and fp16: 0xC000 = -2, 0 = 0, 0x4000 = +2. Products with bf16 or fp16

@@ -359,9 +359,9 @@ def test_grouping_matches_stable_argsort():
 
 
 # ---------------------------------------------------------------- expert FFN / combine (O7, O8, O9)
-def test_expert_ffn_matches_printed_forward():
-    # ai.thesatyajit.com, "The shipped code does no quantization": the printed
-    # MapleMLP.forward written with torch's own linear/clamp/silu in float64
+def test_expert_ffn_matches_torch_forward():
+    # ai.thesatyajit.com, "The shipped code does no quantization": the expert
+    # forward evaluated step by step with torch's float64 matmul, clamp and silu
     torch = pytest.importorskip("torch")
     F = torch.nn.functional
     g = np.random.default_rng(8)
@@ -371,8 +371,10 @@ def test_expert_ffn_matches_printed_forward():
     x = g.standard_normal((6, H)) * 2
     gg, uu, hh, oo = O.expert_ffn(x, Wg, Wu, Wd, 7.0)
     tx = torch.from_numpy(x)
-    ref = F.linear(F.silu(torch.clamp(F.linear(tx, torch.from_numpy(Wg)), max=7.0))
-                   * torch.clamp(F.linear(tx, torch.from_numpy(Wu)), min=-7.0, max=7.0), torch.from_numpy(Wd))
+    tg = tx @ torch.from_numpy(Wg).T
+    tu = tx @ torch.from_numpy(Wu).T
+    th = F.silu(torch.clamp(tg, max=7.0)) * torch.clamp(tu, min=-7.0, max=7.0)
+    ref = th @ torch.from_numpy(Wd).T
     assert np.allclose(oo, ref.numpy(), rtol=1e-12, atol=1e-12)
     assert np.any(gg > 7) and np.any(np.abs(uu) > 7)  # the clamps were exercised
     # g >= 7 saturates to the constant silu(7)
@@ -438,8 +440,8 @@ def test_moe_layer_distinct_experts_dense_form():
         for e in chosen:
             deq = [torch.from_numpy(O.dequantize(*O.ternarize_absmean(m))) for m in experts[e]]
             tx = torch.from_numpy(x[t:t + 1])
-            o = F.linear(F.silu(torch.clamp(F.linear(tx, deq[0]), max=7.0))
-                         * torch.clamp(F.linear(tx, deq[1]), min=-7.0, max=7.0), deq[2])
+            th = F.silu(torch.clamp(tx @ deq[0].T, max=7.0)) * torch.clamp(tx @ deq[1].T, min=-7.0, max=7.0)
+            o = th @ deq[2].T
             outs.append(o.numpy()[0])
         Y[t] = sum(wj * oj for wj, oj in zip(w, outs))
         Y_swapped[t] = w[1] * outs[0] + w[0] * outs[1] + sum(wj * oj for wj, oj in zip(w[2:], outs[2:]))
