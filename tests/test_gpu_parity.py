@@ -374,7 +374,8 @@ def _group(tm, idx, E):
 @pytest.mark.parametrize("T,k,E,mode", [(1, 8, 256, "rand"), (7, 8, 256, "rand"), (64, 8, 256, "zipf"),
                                         (256, 8, 256, "rand"), (257, 8, 256, "rand"), (1000, 1, 64, "rand"),
                                         (4096, 8, 256, "rand"), (300, 16, 1000, "rand"), (600, 8, 256, "one"),
-                                        (50, 40, 128, "rand"), (700, 12, 64, "rand"), (16640, 8, 256, "rand")])
+                                        (50, 40, 128, "rand"), (700, 12, 64, "rand"), (300, 20, 256, "rand"),
+                                        (16640, 8, 256, "rand")])
 def test_grouping_parity(tm, T, k, E, mode):
     """One workgroup (T <= 256), count + scatter with the scan folded in (up to
     64 blocks of 256 tokens) and count + scan + scatter (T = 16640: 65 blocks)
@@ -596,6 +597,31 @@ def test_layer_prefill_every_row(tm, layers):
         say(f"  clamp={clamp}: h error {eh:.2e}, expert outputs error {eo:.2e} over all {T * k} pairs")
         assert eh <= TOL and eo <= TOL
         del O_, Hh
+
+
+@pytest.mark.parametrize("T", [1023, 1024])
+def test_layer_at_the_prefill_switch(tm, layers, T):
+    """Both sides of the 1024-token switch, where the router moves from the
+    fp64 matrix-core logits (+ the top-k kernel) to the bf16 candidates refined
+    in fp64, and the expert kernels from 16-pair tiles to the token-blocked
+    form (T k >= 32 E): idx, pos and Y on every row against the oracle."""
+    cfg, k, E = 4, 8, 256
+    W = layers(cfg, 0, "uniform")
+    xb = ti.activations(cfg, T)
+    Wr, b = ti.router_matrix(cfg, 0), ti.router_bias(cfg, "uniform")
+    ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, k)
+    counts, offsets, st, ss, pos = O.group_by_expert(ridx, E)
+    say(f"layer T={T}: {T * k} pairs, expert counts min {counts.min()} max {counts.max()}")
+    _prefetch_experts(cfg, 0, range(E))
+    Href, Oref = _grouped_ffn_reference(cfg, 0, O.bf16_to_f64(xb), st, offsets, (7.0,))[7.0]
+    got = _run_layer(tm, W, xb, 7.0)
+    say(f"  tokens recomputed in double-double: {got['nfix']}")
+    assert np.array_equal(got["idx"], ridx)
+    assert np.array_equal(got["pos"], pos)
+    assert O.max_normalized_error(got["w"], rw) <= TOL
+    err = O.max_normalized_error(got["Y"], O.combine(Oref, rw, pos))
+    say(f"  Y max normalized error over all {T} rows {err:.2e}")
+    assert err <= TOL
 
 
 def test_layer_is_deterministic(tm, layers):
