@@ -1773,27 +1773,36 @@ __global__ __launch_bounds__(256) void linear3_kernel(Linear3Args a) {
 }
 
 // ------------------------------------------------------------------ combine
-// grid (T, H / 512), 128 threads x one float4 each; fixed slot order j = 0..k-1
-// (slots with pos < 0 are skipped). The slots go 8 at a time with all 8 output
-// rows in flight before the first product: no load sits under a branch (an
-// invalid slot reads row 0 and is dropped by a select, so nothing it holds can
-// reach the sum), which would make each product wait for its own load.
-// NT: the expert outputs are far larger than the caches and read once, non-temporally.
-template <bool NT>
+// grid (T, H / (512 C)), 128 threads x C float4 columns each (128 apart, so
+// every load instruction of the workgroup is contiguous); fixed slot order
+// j = 0..k-1 (slots with pos < 0 are skipped). The slots go 8 at a time with
+// all 8 C output rows in flight before the first product: no load sits under a
+// branch (an invalid slot reads row 0 and is dropped by a select, so nothing it
+// holds can reach the sum), which would make each product wait for its own
+// load. NT: the expert outputs are far larger than the caches and read once,
+// non-temporally. C = 2 for large batches (twice the loads in flight per
+// thread); C = 1 keeps enough workgroups for a few tokens.
+template <bool NT, int C>
 __global__ __launch_bounds__(128) void combine_kernel(const float *O, const float *w, const int32_t *pos, int k,
                                                        int H, float *Y, const uint16_t *resid_in,
                                                        uint16_t *resid_out) {
   constexpr int B = 8;
   const int64_t t = blockIdx.x;
-  const int c = blockIdx.y * 128 + threadIdx.x;  // float4 column
-  if (c * 4 >= H) return;
-  uint2 xi = make_uint2(0u, 0u);  // the residual input, fetched with the first slots
-  if (resid_out) xi = reinterpret_cast<const uint2 *>(resid_in + t * H)[c];
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int cb = blockIdx.y * 128 * C + threadIdx.x;  // float4 column of q = 0
+  uint2 xi[C];  // the residual input, fetched with the first slots
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const int c = cb + 128 * q;
+    xi[q] = make_uint2(0u, 0u);
+    if (resid_out && c * 4 < H) xi[q] = reinterpret_cast<const uint2 *>(resid_in + t * H)[c];
+  }
+  float4 acc[C];
+#pragma unroll
+  for (int q = 0; q < C; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += B) {
     int pj[B];
     float wj[B];
-    f32x4 o[B];
+    f32x4 o[B][C];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const int j = min(j0 + u, k - 1);
@@ -1801,28 +1810,40 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *O, const floa
       wj[u] = w[t * k + j];
     }
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const f32x4 *src = reinterpret_cast<const f32x4 *>(O + (int64_t)max(pj[u], 0) * H) + c;
-      if constexpr (NT) o[u] = __builtin_nontemporal_load(src);
-      else o[u] = *src;
-    }
+    for (int u = 0; u < B; ++u)
+#pragma unroll
+      for (int q = 0; q < C; ++q) {
+        // columns past H read the row's last column (dropped below)
+        const int c = min(cb + 128 * q, H / 4 - 1);
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(O + (int64_t)max(pj[u], 0) * H) + c;
+        if constexpr (NT) o[u][q] = __builtin_nontemporal_load(src);
+        else o[u][q] = *src;
+      }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const bool use = j0 + u < k && pj[u] >= 0;
-      acc.x = use ? fmaf(wj[u], o[u][0], acc.x) : acc.x;
-      acc.y = use ? fmaf(wj[u], o[u][1], acc.y) : acc.y;
-      acc.z = use ? fmaf(wj[u], o[u][2], acc.z) : acc.z;
-      acc.w = use ? fmaf(wj[u], o[u][3], acc.w) : acc.w;
+#pragma unroll
+      for (int q = 0; q < C; ++q) {
+        acc[q].x = use ? fmaf(wj[u], o[u][q][0], acc[q].x) : acc[q].x;
+        acc[q].y = use ? fmaf(wj[u], o[u][q][1], acc[q].y) : acc[q].y;
+        acc[q].z = use ? fmaf(wj[u], o[u][q][2], acc[q].z) : acc[q].z;
+        acc[q].w = use ? fmaf(wj[u], o[u][q][3], acc[q].w) : acc[q].w;
+      }
     }
   }
-  if (Y) reinterpret_cast<float4 *>(Y + t * H)[c] = acc;
-  if (resid_out) {
-    const float x0 = __uint_as_float(xi.x << 16), x1 = __uint_as_float(xi.x & 0xFFFF0000u);
-    const float x2 = __uint_as_float(xi.y << 16), x3 = __uint_as_float(xi.y & 0xFFFF0000u);
-    uint2 r;
-    r.x = (uint32_t)f32_to_bf16_rne(x0 + acc.x) | ((uint32_t)f32_to_bf16_rne(x1 + acc.y) << 16);
-    r.y = (uint32_t)f32_to_bf16_rne(x2 + acc.z) | ((uint32_t)f32_to_bf16_rne(x3 + acc.w) << 16);
-    reinterpret_cast<uint2 *>(resid_out + t * H)[c] = r;
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const int c = cb + 128 * q;
+    if (c * 4 >= H) continue;
+    if (Y) reinterpret_cast<float4 *>(Y + t * H)[c] = acc[q];
+    if (resid_out) {
+      const float x0 = __uint_as_float(xi[q].x << 16), x1 = __uint_as_float(xi[q].x & 0xFFFF0000u);
+      const float x2 = __uint_as_float(xi[q].y << 16), x3 = __uint_as_float(xi[q].y & 0xFFFF0000u);
+      uint2 r;
+      r.x = (uint32_t)f32_to_bf16_rne(x0 + acc[q].x) | ((uint32_t)f32_to_bf16_rne(x1 + acc[q].y) << 16);
+      r.y = (uint32_t)f32_to_bf16_rne(x2 + acc[q].z) | ((uint32_t)f32_to_bf16_rne(x3 + acc[q].w) << 16);
+      reinterpret_cast<uint2 *>(resid_out + t * H)[c] = r;
+    }
   }
 }
 
@@ -2168,13 +2189,22 @@ int launch_linear3(hipStream_t st, const uint8_t *Pt, const float *s, int64_t N,
 int launch_combine(hipStream_t st, const float *O, const float *w, const int32_t *pos, int64_t T, int k, int64_t H,
                    float *Y, const uint16_t *resid_in, uint16_t *resid_out) {
   if (T > 0x7FFFFFFF) return fail(TMOE_E_UNSUPPORTED, "T too large");
-  const dim3 grid((unsigned)T, (unsigned)cdiv(H, 512));
-  if ((double)T * k * H * 4 > 64.0 * (1 << 20))  // expert outputs beyond 64 MB: stream them
-    TMOE_LAUNCH(TMOE_KERNEL_COMBINE, combine_kernel<true>, grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y, resid_in,
-                resid_out);
-  else
-    TMOE_LAUNCH(TMOE_KERNEL_COMBINE, combine_kernel<false>, grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y, resid_in,
-                resid_out);
+  const bool wide = T >= 1024;  // two columns per thread: 4096 tokens 50 -> 48.5 us
+  const dim3 grid((unsigned)T, (unsigned)cdiv(H, wide ? 1024 : 512));
+  if ((double)T * k * H * 4 > 64.0 * (1 << 20)) {  // expert outputs beyond 64 MB: stream them
+    if (wide)
+      TMOE_LAUNCH(TMOE_KERNEL_COMBINE, (combine_kernel<true, 2>), grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y,
+                  resid_in, resid_out);
+    else
+      TMOE_LAUNCH(TMOE_KERNEL_COMBINE, (combine_kernel<true, 1>), grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y,
+                  resid_in, resid_out);
+  } else if (wide) {
+    TMOE_LAUNCH(TMOE_KERNEL_COMBINE, (combine_kernel<false, 2>), grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y,
+                resid_in, resid_out);
+  } else {
+    TMOE_LAUNCH(TMOE_KERNEL_COMBINE, (combine_kernel<false, 1>), grid, dim3(128), 0, st, O, w, pos, k, (int)H, Y,
+                resid_in, resid_out);
+  }
   TMOE_LAUNCHED("combine");
   return TMOE_OK;
 }
