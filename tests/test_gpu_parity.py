@@ -375,11 +375,11 @@ def _group(tm, idx, E):
                                         (256, 8, 256, "rand"), (257, 8, 256, "rand"), (1000, 1, 64, "rand"),
                                         (4096, 8, 256, "rand"), (300, 16, 1000, "rand"), (600, 8, 256, "one"),
                                         (50, 40, 128, "rand"), (700, 12, 64, "rand"), (300, 20, 256, "rand"),
-                                        (16640, 8, 256, "rand")])
+                                        (16384, 8, 256, "rand"), (16640, 8, 256, "rand")])
 def test_grouping_parity(tm, T, k, E, mode):
     """One workgroup (T <= 256), count + scatter with the scan folded in (up to
-    64 blocks of 256 tokens) and count + scan + scatter (T = 16640: 65 blocks)
-    against the oracle's grouping."""
+    64 blocks of 256 tokens; T = 16384: exactly 64) and count + scan + scatter
+    (T = 16640: 65 blocks) against the oracle's grouping."""
     say(f"group T={T} k={k} E={E} {mode}")
     g = np.random.default_rng(T * 31 + k + E)
     if mode == "zipf":
@@ -431,11 +431,12 @@ def layers():
     cache = {}
 
     def get(cfg, layer, bias):
-        if (cfg, layer) not in cache:
-            say(f"building layer cfg={cfg} layer={layer} on the device")
-            cache[(cfg, layer)] = synthetic.build_layer(cfg, layer, bias)
+        key = (cfg, layer, bias)  # the routing bias is part of the device layer
+        if key not in cache:
+            say(f"building layer cfg={cfg} layer={layer} bias={bias} on the device")
+            cache[key] = synthetic.build_layer(cfg, layer, bias)
             torch.cuda.synchronize()
-        return cache[(cfg, layer)]
+        return cache[key]
     return get
 
 
@@ -599,16 +600,18 @@ def test_layer_prefill_every_row(tm, layers):
         del O_, Hh
 
 
-@pytest.mark.parametrize("T", [1023, 1024])
-def test_layer_at_the_prefill_switch(tm, layers, T):
+@pytest.mark.parametrize("T,bias_kind", [(1023, "uniform"), (1024, "uniform"), (2048, "zipf")])
+def test_layer_at_the_prefill_switch(tm, layers, T, bias_kind):
     """Both sides of the 1024-token switch, where the router moves from the
     fp64 matrix-core logits (+ the top-k kernel) to the bf16 candidates refined
     in fp64, and the expert kernels from 16-pair tiles to the token-blocked
-    form (T k >= 32 E): idx, pos and Y on every row against the oracle."""
+    form (T k >= 32 E): idx, pos and Y on every row against the oracle. The
+    Zipf-routed case gives the token-blocked kernels one expert with dozens of
+    full blocks next to experts with a single partial block or none."""
     cfg, k, E = 4, 8, 256
-    W = layers(cfg, 0, "uniform")
+    W = layers(cfg, 0, bias_kind)
     xb = ti.activations(cfg, T)
-    Wr, b = ti.router_matrix(cfg, 0), ti.router_bias(cfg, "uniform")
+    Wr, b = ti.router_matrix(cfg, 0), ti.router_bias(cfg, bias_kind)
     ridx, rw, _, _ = O.router_topk(O.bf16_to_f64(xb), Wr, b, k)
     counts, offsets, st, ss, pos = O.group_by_expert(ridx, E)
     say(f"layer T={T}: {T * k} pairs, expert counts min {counts.min()} max {counts.max()}")
